@@ -1,0 +1,160 @@
+/*
+ * moeroute.h -- C ABI of the MI355X (gfx950) MoE token-routing library.
+ *
+ * The library turns router inputs into expert-grouped token slots:
+ *
+ *   route:  x [M, H] bf16, gate_w [E, H] bf16 (+ shared_w [H] bf16)
+ *           -> topk_ids [M, S] int32, topk_weights [M, S] fp32, S = k + shared
+ *   align:  topk_ids [M, S] -> sorted_token_ids, expert_ids, npp
+ *
+ * and mr_route_align does both in ONE kernel launch.
+ *
+ * Passages the operations follow (web pages, cited by title and section):
+ *   [R] "[AMD] One-launch small-M MoE router ... on gfx950" (sglang PR),
+ *       Modifications: the gate rows (routed and shared) are dot products
+ *       over the hidden size with fp32 accumulation, read in place from the
+ *       [out, in] gate weights; the routed logits are rounded to bf16; top-k
+ *       with the lower id winning ties; softmax and renormalisation; slot k
+ *       holds (E, sigmoid(shared logit) * scale); the launch is graph-safe
+ *       through a self-resetting ticket counter; the outputs are ids [M, k+1]
+ *       int32 and weights [M, k+1] fp32.
+ *   [A] "W4A16 MoE prefill: M-aware moe_align block size" (ROCm vLLM),
+ *       Purpose: moe_align_block_size groups the routed rows by expert and
+ *       pads each touched expert to the alignment A, so that
+ *       num_tokens_post_padded = sum over touched experts of ceil(c_e/A)*A;
+ *       the alignment is 64 below one full block of routed rows per expert
+ *       (tokens * top-k / E < 128) and 128 at or above it.
+ *   [N] "Netra Kernel: Open-Source ROCm Kernels for AMD MI350X", Compile
+ *       exact contracts: before capture the caller allocates persistent
+ *       workspace; a launch then does no allocation, symbol lookup or host
+ *       synchronisation.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - Pointers named x, gate_w, shared_w, topk_*, sorted_token_ids,
+ *   expert_ids, npp, ws are DEVICE pointers owned by the caller.  The
+ *   library never allocates, frees, synchronises, or reads device memory
+ *   on the host.  `stream` is a hipStream_t (NULL = the default stream);
+ *   every kernel is enqueued on it, so calls are capturable into HIP graphs.
+ * - Layouts are row-major and dense: x [M, H] (stride H), gate_w [E, H]
+ *   (stride H, one row per routed expert), shared_w [H], topk_ids and
+ *   topk_weights [M, S].  bf16 tensors are passed as raw 16-bit patterns.
+ *   x, gate_w and shared_w must be 16-byte aligned and H a multiple of 8.
+ * - S = k + (shared_w != NULL).  The shared expert, when present, has id E,
+ *   so the align step sees num_experts = E' = E + 1 ids.
+ * - Return value: MR_OK (0) or a negative MR_E* code.  On refusal nothing is
+ *   launched and mr_last_error() lists every failed check (thread-local
+ *   string, valid until the next call on the same thread).
+ * - Device-side preconditions that are documented, not checked: inputs are
+ *   finite; align's ids are in [0, num_experts) -- ids outside that range
+ *   are skipped (never written out of bounds).
+ * - Workspace `ws` (ws_bytes >= mr_workspace_bytes(...)) must be zeroed ONCE
+ *   by the caller before first use (e.g. torch.zeros).  Every launch leaves
+ *   its counters at zero again, so the same workspace can be reused and
+ *   replayed from a graph.  Launches that may overlap in time (different
+ *   streams) need different workspaces.  If a launch was aborted,
+ *   mr_workspace_reset() re-zeroes the counters.
+ * - sorted_token_ids: entries [0, npp) are defined: for each touched expert
+ *   e in ascending order, its pairs' flat indices i = m*S + slot in
+ *   ascending order, then the sentinel M*S up to the next multiple of A.
+ *   expert_ids[b] for b < npp/A is the expert of block b.  Entries at or
+ *   past npp (and past npp/A) are unspecified.
+ */
+#ifndef MOEROUTE_H
+#define MOEROUTE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MR_ABI_VERSION 1
+
+#define MR_OK 0
+#define MR_EINVAL (-1)        /* null pointer, negative size, k < 1, k > E  */
+#define MR_EUNSUPPORTED (-2)  /* outside the supported contract (H % 8,
+                                 alignment, E or num_experts too large,
+                                 k > MR_MAX_TOPK, A)                        */
+#define MR_ECAPACITY (-3)     /* an output or the workspace is too small   */
+#define MR_ELAUNCH (-4)       /* the HIP runtime reported a launch error   */
+
+/* Largest supported sizes. */
+#define MR_MAX_ROUTED_EXPERTS 1024  /* E for the route entry points          */
+#define MR_MAX_ALIGN_EXPERTS 4096   /* num_experts for mr_align              */
+#define MR_MAX_TOPK 32              /* routed k                              */
+#define MR_MAX_TOKENS (1 << 20)
+
+/* ABI version of the loaded library (MR_ABI_VERSION). */
+int mr_abi_version(void);
+
+/* Every failed check of the last refused call on this thread, or "". */
+const char *mr_last_error(void);
+
+/* Alignment tier [A], Purpose: 128 when M*k >= 128*E, else 64 (routed k and
+ * E, computed in 64-bit).  Returns MR_EINVAL for M < 0, k < 1 or E < 1. */
+int32_t mr_select_alignment(int32_t M, int32_t k, int32_t E);
+
+/* Entries sorted_token_ids needs so that any routing of M*S pairs over
+ * num_experts ids fits: M*S + min(num_experts, M*S) * (A - 1).  (Passing the
+ * looser M*S + num_experts*(A-1) is also fine.)  Negative on bad input. */
+int64_t mr_align_capacity(int32_t M, int32_t S, int32_t num_experts, int32_t A);
+
+/* Entries expert_ids needs: mr_align_capacity(...) / A. */
+int64_t mr_expert_ids_capacity(int32_t M, int32_t S, int32_t num_experts, int32_t A);
+
+/* Workspace bytes for any call with M <= M_max tokens, E routed experts,
+ * routed top-k, a shared expert or not.  Covers mr_route, mr_route_align,
+ * mr_align (with S = k + has_shared, num_experts = E + has_shared) and
+ * mr_debug_gate_logits. */
+size_t mr_workspace_bytes(int32_t M_max, int32_t E, int32_t k, int32_t has_shared);
+
+/* Re-zero the workspace's counters on `stream` (a small fill kernel, safe to
+ * capture).  Needed only after an aborted launch. */
+int mr_workspace_reset(void *ws, size_t ws_bytes, void *stream);
+
+/* Route [R], Modifications: gate contraction in fp32, bf16 rounding of the
+ * routed logits, top-k (lower id wins ties), softmax + renormalise, shared
+ * slot k = (E, sigmoid(s) * scale).  Writes topk_ids / topk_weights [M, S].
+ * shared_w may be NULL (then S = k and there is no shared slot).
+ * 0 <= M <= MR_MAX_TOKENS; 1 <= k <= min(E, MR_MAX_TOPK); H % 8 == 0. */
+int mr_route(const void *x, const void *gate_w, const void *shared_w,
+             int32_t M, int32_t H, int32_t E, int32_t k, float scale,
+             int32_t *topk_ids, float *topk_weights,
+             void *ws, size_t ws_bytes, void *stream);
+
+/* moe_align_block_size [A], Purpose, on caller-given ids [M, S] over
+ * num_experts ids with alignment A (a power of two in [16, 256]).
+ * sorted_cap and expert_cap are the lengths of sorted_token_ids and
+ * expert_ids; they must be at least mr_align_capacity() and
+ * mr_expert_ids_capacity().  *npp (device int32) receives
+ * num_tokens_post_padded.  Works for any ids, repeated or not. */
+int mr_align(const int32_t *topk_ids, int32_t M, int32_t S, int32_t num_experts,
+             int32_t A, int32_t *sorted_token_ids, int64_t sorted_cap,
+             int32_t *expert_ids, int64_t expert_cap, int32_t *npp,
+             void *ws, size_t ws_bytes, void *stream);
+
+/* Route followed by align, in ONE launch: the arguments of mr_route plus
+ * the alignment A (pass mr_select_alignment(M, k, E) for the M-aware tier)
+ * and the align outputs.  num_experts is E + (shared_w != NULL). */
+int mr_route_align(const void *x, const void *gate_w, const void *shared_w,
+                   int32_t M, int32_t H, int32_t E, int32_t k, float scale,
+                   int32_t A, int32_t *topk_ids, float *topk_weights,
+                   int32_t *sorted_token_ids, int64_t sorted_cap,
+                   int32_t *expert_ids, int64_t expert_cap, int32_t *npp,
+                   void *ws, size_t ws_bytes, void *stream);
+
+/* Test hook, not part of the routing API: writes the fp32 gate logits the
+ * route kernels compute for these inputs -- logits [M, E + has_shared]
+ * (the shared logit in the last column) -- using the same kernel code and
+ * summation order as mr_route for the same M. */
+int mr_debug_gate_logits(const void *x, const void *gate_w, const void *shared_w,
+                         int32_t M, int32_t H, int32_t E, float *logits,
+                         void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOEROUTE_H */

@@ -1,0 +1,233 @@
+"""ctypes binding of libmoeroute.so (include/moeroute.h): argument marshalling
+only.  Torch tensors provide device memory and streams; every step of the
+route and align runs in the library's HIP kernels.  There is no fallback: if
+the library is missing or refuses a call, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libmoeroute.so")
+_lib = None
+
+MR_OK = 0
+MR_EINVAL = -1
+MR_EUNSUPPORTED = -2
+MR_ECAPACITY = -3
+MR_ELAUNCH = -4
+
+# Every symbol include/moeroute.h declares, with (restype, argtypes).
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+_F32 = ctypes.c_float
+SIGNATURES = {
+    "mr_abi_version": (ctypes.c_int, []),
+    "mr_last_error": (ctypes.c_char_p, []),
+    "mr_select_alignment": (_I32, [_I32, _I32, _I32]),
+    "mr_align_capacity": (_I64, [_I32, _I32, _I32, _I32]),
+    "mr_expert_ids_capacity": (_I64, [_I32, _I32, _I32, _I32]),
+    "mr_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
+    "mr_workspace_reset": (ctypes.c_int, [_P, _SZ, _P]),
+    "mr_route": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _F32, _P, _P, _P, _SZ, _P]),
+    "mr_align": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _P, _I64, _P, _I64, _P, _P, _SZ, _P]),
+    "mr_route_align": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _F32, _I32, _P, _P, _P, _I64,
+                                      _P, _I64, _P, _P, _SZ, _P]),
+    "mr_debug_gate_logits": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _P, _P, _SZ, _P]),
+}
+
+
+class MoeRouteError(RuntimeError):
+    """A refused or failed library call (code is the MR_E* value)."""
+
+    def __init__(self, code: int, message: str):
+        super().__init__(f"[{code}] {message}")
+        self.code = code
+        self.message = message
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise MoeRouteError(MR_ELAUNCH, f"{_LIB_PATH} is missing: build it with "
+                                "`python -m moe_token_routing_amd.build` (hipcc, gfx950)")
+        L = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(rc: int) -> None:
+    if rc != MR_OK:
+        raise MoeRouteError(rc, lib().mr_last_error().decode())
+
+
+def _stream(stream, device):
+    import torch
+
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _bf16_2d(t, name):
+    import torch
+
+    if t.dtype != torch.bfloat16 or t.dim() != 2 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous 2-D bfloat16 tensor")
+    return t
+
+
+# --------------------------------------------------------------- host-only --
+
+def mr_abi_version() -> int:
+    return int(lib().mr_abi_version())
+
+
+def mr_last_error() -> str:
+    return lib().mr_last_error().decode()
+
+
+def mr_select_alignment(M: int, k: int, E: int) -> int:
+    return int(lib().mr_select_alignment(M, k, E))
+
+
+def mr_align_capacity(M: int, S: int, num_experts: int, A: int) -> int:
+    return int(lib().mr_align_capacity(M, S, num_experts, A))
+
+
+def mr_expert_ids_capacity(M: int, S: int, num_experts: int, A: int) -> int:
+    return int(lib().mr_expert_ids_capacity(M, S, num_experts, A))
+
+
+def mr_workspace_bytes(M_max: int, E: int, k: int, has_shared: bool) -> int:
+    return int(lib().mr_workspace_bytes(M_max, E, k, int(bool(has_shared))))
+
+
+# ----------------------------------------------------------------- device --
+
+def new_workspace(M_max: int, E: int, k: int, has_shared: bool, device="cuda"):
+    """A zeroed workspace tensor (uint8) big enough for M <= M_max."""
+    import torch
+
+    nbytes = mr_workspace_bytes(M_max, E, k, has_shared)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+
+def mr_workspace_reset(workspace, stream=None) -> None:
+    _check(lib().mr_workspace_reset(_ptr(workspace), workspace.numel(), _stream(stream, workspace.device)))
+
+
+def mr_route(x, gate_w, shared_w, k: int, scale: float = 1.0, *, workspace,
+             topk_ids=None, topk_weights=None, stream=None):
+    """Returns (topk_ids [M, S] int32, topk_weights [M, S] float32)."""
+    import torch
+
+    _bf16_2d(x, "x")
+    _bf16_2d(gate_w, "gate_w")
+    M, H = x.shape
+    E = gate_w.shape[0]
+    S = k + (shared_w is not None)
+    if topk_ids is None:
+        topk_ids = torch.empty((M, S), dtype=torch.int32, device=x.device)
+    if topk_weights is None:
+        topk_weights = torch.empty((M, S), dtype=torch.float32, device=x.device)
+    _check(lib().mr_route(_ptr(x), _ptr(gate_w), _ptr(shared_w), M, H, E, k, float(scale),
+                          _ptr(topk_ids), _ptr(topk_weights), _ptr(workspace), workspace.numel(),
+                          _stream(stream, x.device)))
+    return topk_ids, topk_weights
+
+
+def _align_outputs(M, S, num_experts, A, device, sorted_token_ids, expert_ids, npp):
+    import torch
+
+    cap = mr_align_capacity(M, S, num_experts, A)
+    if sorted_token_ids is None:
+        sorted_token_ids = torch.empty(max(cap, 1), dtype=torch.int32, device=device)
+    if expert_ids is None:
+        expert_ids = torch.empty(max(cap // A, 1), dtype=torch.int32, device=device)
+    if npp is None:
+        npp = torch.empty(1, dtype=torch.int32, device=device)
+    return sorted_token_ids, expert_ids, npp
+
+
+def mr_align(topk_ids, num_experts: int, A: int, *, workspace, sorted_token_ids=None,
+             expert_ids=None, npp=None, stream=None):
+    """Returns (sorted_token_ids, expert_ids, npp) as device tensors; entries
+    at or past npp are unspecified."""
+    import torch
+
+    if topk_ids.dtype != torch.int32 or not topk_ids.is_contiguous():
+        raise ValueError("topk_ids must be a contiguous int32 tensor")
+    ids2 = topk_ids.view(topk_ids.shape[0], -1) if topk_ids.dim() >= 1 and topk_ids.numel() else topk_ids
+    M = topk_ids.shape[0] if topk_ids.dim() else 0
+    S = ids2.shape[1] if ids2.dim() == 2 else 1
+    sorted_token_ids, expert_ids, npp = _align_outputs(M, S, num_experts, A, topk_ids.device,
+                                                       sorted_token_ids, expert_ids, npp)
+    _check(lib().mr_align(_ptr(topk_ids), M, S, num_experts, A, _ptr(sorted_token_ids),
+                          sorted_token_ids.numel(), _ptr(expert_ids), expert_ids.numel(), _ptr(npp),
+                          _ptr(workspace), workspace.numel(), _stream(stream, topk_ids.device)))
+    return sorted_token_ids, expert_ids, npp
+
+
+def mr_route_align(x, gate_w, shared_w, k: int, scale: float = 1.0, A: int | None = None, *,
+                   workspace, topk_ids=None, topk_weights=None, sorted_token_ids=None,
+                   expert_ids=None, npp=None, stream=None):
+    """Route + align in one launch.  A defaults to the M-aware tier.
+    Returns dict(topk_ids, topk_weights, sorted_token_ids, expert_ids, npp, A)."""
+    import torch
+
+    _bf16_2d(x, "x")
+    _bf16_2d(gate_w, "gate_w")
+    M, H = x.shape
+    E = gate_w.shape[0]
+    sh = shared_w is not None
+    S = k + sh
+    if A is None:
+        A = mr_select_alignment(M, k, E)
+    if topk_ids is None:
+        topk_ids = torch.empty((M, S), dtype=torch.int32, device=x.device)
+    if topk_weights is None:
+        topk_weights = torch.empty((M, S), dtype=torch.float32, device=x.device)
+    sorted_token_ids, expert_ids, npp = _align_outputs(M, S, E + sh, A, x.device, sorted_token_ids,
+                                                       expert_ids, npp)
+    _check(lib().mr_route_align(_ptr(x), _ptr(gate_w), _ptr(shared_w), M, H, E, k, float(scale), A,
+                                _ptr(topk_ids), _ptr(topk_weights), _ptr(sorted_token_ids),
+                                sorted_token_ids.numel(), _ptr(expert_ids), expert_ids.numel(), _ptr(npp),
+                                _ptr(workspace), workspace.numel(), _stream(stream, x.device)))
+    return {"topk_ids": topk_ids, "topk_weights": topk_weights, "sorted_token_ids": sorted_token_ids,
+            "expert_ids": expert_ids, "npp": npp, "A": A}
+
+
+def mr_debug_gate_logits(x, gate_w, shared_w, *, workspace, logits=None, stream=None):
+    """Test hook: the fp32 logits [M, E + shared] the route kernels compute."""
+    import torch
+
+    _bf16_2d(x, "x")
+    _bf16_2d(gate_w, "gate_w")
+    M, H = x.shape
+    E = gate_w.shape[0]
+    Ep = E + (shared_w is not None)
+    if logits is None:
+        logits = torch.empty((M, Ep), dtype=torch.float32, device=x.device)
+    _check(lib().mr_debug_gate_logits(_ptr(x), _ptr(gate_w), _ptr(shared_w), M, H, E, _ptr(logits),
+                                      _ptr(workspace), workspace.numel(), _stream(stream, x.device)))
+    return logits

@@ -1,0 +1,172 @@
+// align.hip -- moe_align_block_size for arbitrary ids, one launch.
+//
+// Computes what "W4A16 MoE prefill: M-aware moe_align block size" (ROCm
+// vLLM), Purpose, describes: the n = M*S (token, slot) pairs grouped by
+// expert, each touched expert padded to a multiple of A, so that
+// num_tokens_post_padded = sum over touched experts of ceil(c_e / A) * A.
+// Inside an expert, pairs keep ascending flat index; padding holds M*S.
+//
+// Launch shape: one block of 256 threads per chunk of 64*W pairs.
+//   Phase one (every block): per-expert bitmaps of the chunk's pairs in LDS
+//   (W 64-bit words per expert, set with LDS atomic OR -- order free), then a
+//   per-expert prefix of the word popcounts gives the chunk's count of each
+//   expert and every pair's stable rank inside the chunk.  Counts and ranks
+//   go to the workspace; the block pre-fills a slice of sorted_token_ids with
+//   the sentinel and takes a ticket.
+//   The last block: per-expert totals over chunks, padded sizes, a block scan
+//   for the expert offsets, expert_ids and npp, and for every chunk the base
+//   offset of each expert; then it publishes.
+//   Scatter: the winner and every block that can safely wait (all blocks have
+//   begun) take chunks from a queue and write sorted[base + rank] = i.
+//   The last block to exit re-zeroes the counters.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace mr {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void align_kernel(AlignParams p) {
+  extern __shared__ uint64_t smem[];
+  __shared__ uint32_t flag, slot;
+  __shared__ uint32_t scan_tmp[kThreads / kWave + 1];
+  const int tid = threadIdx.x;
+  const int W = p.W, Ep = p.Ep, A = p.A;
+  const int64_t CH = 64 * (int64_t)W;
+  uint32_t *ctr = p.ctr;
+  if (tid == 0) __hip_atomic_fetch_add(&ctr[kCtrStarted], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // ---- phase one: this block's chunk ------------------------------------
+  {
+    uint64_t *bm = smem;                                         // [Ep * W]
+    uint16_t *pre = reinterpret_cast<uint16_t *>(smem + (size_t)Ep * W);  // [Ep * W]
+    const int c = blockIdx.x;
+    const int64_t lo = c * CH;
+    const int64_t hi = min(p.n, lo + CH);
+    for (int j = tid; j < Ep * W; j += kThreads) bm[j] = 0ull;
+    __syncthreads();
+    for (int64_t i = lo + tid; i < hi; i += kThreads) {
+      const int32_t e = p.ids[i];
+      if (e >= 0 && e < Ep) {
+        const int li = (int)(i - lo);
+        atomicOr(reinterpret_cast<unsigned long long *>(&bm[(size_t)e * W + (li >> 6)]), 1ull << (li & 63));
+      }
+    }
+    __syncthreads();
+    for (int e = tid; e < Ep; e += kThreads) {
+      uint32_t run = 0;
+      for (int w = 0; w < W; ++w) {
+        pre[(size_t)e * W + w] = (uint16_t)run;
+        run += __popcll(bm[(size_t)e * W + w]);
+      }
+      p.counts[(size_t)c * Ep + e] = (int32_t)run;
+    }
+    __syncthreads();
+    for (int64_t i = lo + tid; i < hi; i += kThreads) {
+      const int32_t e = p.ids[i];
+      if (e >= 0 && e < Ep) {
+        const int li = (int)(i - lo);
+        const size_t j = (size_t)e * W + (li >> 6);
+        p.ranks[i] = (int32_t)(pre[j] + __popcll(bm[j] & ((1ull << (li & 63)) - 1ull)));
+      }
+    }
+    const int32_t sentinel = (int32_t)p.n;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + tid; i < p.fill_count; i += (int64_t)gridDim.x * kThreads)
+      p.sorted[i] = sentinel;
+  }
+
+  // ---- the last chunk block computes offsets and bases -----------------
+  const bool winner = last_block_ticket(&ctr[kCtrDone], gridDim.x, &flag);
+  bool help = winner;
+  if (winner) {
+    const int nch = p.nchunks;
+    const int per = (Ep + kThreads - 1) / kThreads;
+    const int e0 = tid * per;
+    uint32_t local = 0;
+    for (int e = e0; e < e0 + per && e < Ep; ++e) {
+      uint32_t tot = 0;
+      for (int c = 0; c < nch; ++c) tot += (uint32_t)p.counts[(size_t)c * Ep + e];
+      local += (tot + A - 1) / A * A;
+    }
+    uint32_t total;
+    uint32_t base = block_excl_scan_u32<kThreads>(local, scan_tmp, &total);
+    for (int e = e0; e < e0 + per && e < Ep; ++e) {
+      uint32_t run = base;
+      for (int c = 0; c < nch; ++c) {
+        const uint32_t t = (uint32_t)p.counts[(size_t)c * Ep + e];
+        p.counts[(size_t)c * Ep + e] = (int32_t)run;
+        run += t;
+      }
+      const uint32_t P = (run - base + A - 1) / A * A;
+      for (uint32_t b = base / A; b < (base + P) / A; ++b)
+        if (b < (uint64_t)p.expert_cap) p.expert_ids[b] = e;
+      base += P;
+    }
+    if (tid == 0) *p.npp = (int32_t)total;
+    publish(&ctr[kCtrPublished]);
+  } else {
+    help = join_after_publish(&ctr[kCtrStarted], gridDim.x, &ctr[kCtrPublished], &flag);
+  }
+
+  // ---- scatter: chunks from the queue -----------------------------------
+  if (help) {
+    for (;;) {
+      const uint32_t c = next_work_item(&ctr[kCtrWork], &slot);
+      if (c >= (uint32_t)p.nchunks) break;
+      const int64_t lo = c * CH;
+      const int64_t hi = min(p.n, lo + CH);
+      for (int64_t i = lo + tid; i < hi; i += kThreads) {
+        const int32_t e = p.ids[i];
+        if (e < 0 || e >= Ep) continue;
+        const int64_t pos = (int64_t)p.counts[(size_t)c * Ep + e] + p.ranks[i];
+        if (pos < p.sorted_cap) p.sorted[pos] = (int32_t)i;
+      }
+    }
+  }
+
+  if (last_to_exit(&ctr[kCtrExited], gridDim.x, &flag) && tid == 0) {
+    reset_counter(&ctr[kCtrStarted]);
+    reset_counter(&ctr[kCtrDone]);
+    reset_counter(&ctr[kCtrPublished]);
+    reset_counter(&ctr[kCtrWork]);
+    reset_counter(&ctr[kCtrExited]);
+  }
+}
+
+__global__ void zero_words_kernel(uint32_t *p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+__global__ void store_zero_kernel(int32_t *p) { *p = 0; }
+
+}  // namespace
+
+int align_words_per_expert(int Ep) {
+  // Largest power of two <= 16 with the bitmaps within 48 KiB of LDS.
+  int W = 16;
+  while (W > 1 && (size_t)Ep * W * 8 > 48 * 1024) W >>= 1;
+  return W;
+}
+
+hipError_t launch_align(const AlignParams &p, hipStream_t stream) {
+  const size_t lds = (size_t)p.Ep * p.W * (8 + 2);
+  align_kernel<<<p.nchunks, kThreads, lds, stream>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_words(uint32_t *p, size_t n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int grid = (int)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
+  zero_words_kernel<<<grid, 256, 0, stream>>>(p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_store_zero(int32_t *p, hipStream_t stream) {
+  store_zero_kernel<<<1, 1, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace mr

@@ -1,0 +1,300 @@
+// api.cpp -- the C ABI declared in include/moeroute.h: argument checks,
+// workspace layout, path choice and launches on the caller's stream.
+//
+// Nothing here allocates device memory, synchronises, or reads device
+// memory; every refusal is decided from the arguments alone and lists every
+// failed check (the default-deny discipline of "Netra Kernel: Open-Source
+// ROCm Kernels for AMD MI350X", Compile exact contracts).
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "kernels.h"
+#include "moeroute.h"
+
+static_assert(MR_MAX_ROUTED_EXPERTS == mr::kMaxRouteExperts, "route expert limit");
+static_assert(MR_MAX_ALIGN_EXPERTS == mr::kMaxAlignExperts, "align expert limit");
+static_assert(MR_MAX_TOPK == mr::kMaxTopK, "top-k limit");
+
+namespace {
+
+thread_local std::string g_last_error;
+
+struct Checks {
+  std::string msg;
+  bool inval = false, unsupported = false, capacity = false;
+  void fail(int c, const char *fmt, ...) {
+    char buf[256];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    if (!msg.empty()) msg += "; ";
+    msg += buf;
+    inval |= c == MR_EINVAL;
+    unsupported |= c == MR_EUNSUPPORTED;
+    capacity |= c == MR_ECAPACITY;
+  }
+  // MR_EINVAL before MR_EUNSUPPORTED before MR_ECAPACITY
+  int code() const {
+    return inval ? MR_EINVAL : unsupported ? MR_EUNSUPPORTED : capacity ? MR_ECAPACITY : MR_OK;
+  }
+  int finish(const char *fn) {
+    const int c = code();
+    if (c != MR_OK) g_last_error = std::string(fn) + ": " + msg;
+    else g_last_error.clear();
+    return c;
+  }
+};
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int64_t tight_capacity(int64_t n, int64_t Ep, int64_t A) {
+  const int64_t touched = Ep < n ? Ep : n;
+  return n + touched * (A - 1);
+}
+
+// Workspace regions for one call.
+struct Layout {
+  size_t counters = 0, logits = 0, counts = 0, ranks = 0, total = 0;
+};
+
+Layout layout_for(int64_t M, int64_t E, int64_t k, int64_t sh) {
+  Layout L;
+  const int64_t S = k + sh, Ep = E + sh, n = M * S;
+  size_t o = mr::kCounterBytes;
+  L.logits = o;
+  o = align_up(o + (size_t)mr::kSmallMaxTokens * (size_t)(Ep > 0 ? Ep : 1) * 4, 256);
+  const int W = mr::align_words_per_expert((int)(Ep > 0 ? Ep : 1));
+  const int64_t nch = (n + 64 * W - 1) / (64 * W);
+  L.counts = o;
+  o = align_up(o + (size_t)(nch > 0 ? nch : 1) * (size_t)(Ep > 0 ? Ep : 1) * 4, 256);
+  L.ranks = o;
+  o = align_up(o + (size_t)(n > 0 ? n : 1) * 4, 256);
+  L.total = o;
+  return L;
+}
+
+int launch_result(hipError_t e, const char *fn) {
+  if (e == hipSuccess) {
+    g_last_error.clear();
+    return MR_OK;
+  }
+  g_last_error = std::string(fn) + ": launch failed: " + hipGetErrorString(e);
+  return MR_ELAUNCH;
+}
+
+void check_route_args(Checks &ck, const void *x, const void *gate_w, const void *shared_w, int32_t M,
+                      int32_t H, int32_t E, int32_t k) {
+  if (!x && M > 0) ck.fail(MR_EINVAL, "x is NULL");
+  if (!gate_w) ck.fail(MR_EINVAL, "gate_w is NULL");
+  if (M < 0) ck.fail(MR_EINVAL, "M=%d < 0", M);
+  if (M > MR_MAX_TOKENS) ck.fail(MR_EUNSUPPORTED, "M=%d > %d", M, MR_MAX_TOKENS);
+  if (H < 8) ck.fail(MR_EINVAL, "H=%d < 8", H);
+  else if (H % 8) ck.fail(MR_EUNSUPPORTED, "H=%d is not a multiple of 8", H);
+  if (E < 1) ck.fail(MR_EINVAL, "E=%d < 1", E);
+  if (E > mr::kMaxRouteExperts) ck.fail(MR_EUNSUPPORTED, "E=%d > %d", E, mr::kMaxRouteExperts);
+  if (k < 1) ck.fail(MR_EINVAL, "k=%d < 1", k);
+  if (k > E && E >= 1) ck.fail(MR_EINVAL, "k=%d > E=%d", k, E);
+  if (k > mr::kMaxTopK) ck.fail(MR_EUNSUPPORTED, "k=%d > %d", k, mr::kMaxTopK);
+  if (x && !aligned16(x)) ck.fail(MR_EUNSUPPORTED, "x is not 16-byte aligned");
+  if (gate_w && !aligned16(gate_w)) ck.fail(MR_EUNSUPPORTED, "gate_w is not 16-byte aligned");
+  if (shared_w && !aligned16(shared_w)) ck.fail(MR_EUNSUPPORTED, "shared_w is not 16-byte aligned");
+}
+
+void check_align_outputs(Checks &ck, int64_t n, int64_t Ep, int32_t A, const int32_t *sorted,
+                         int64_t sorted_cap, const int32_t *expert_ids, int64_t expert_cap, const int32_t *npp) {
+  if (!sorted) ck.fail(MR_EINVAL, "sorted_token_ids is NULL");
+  if (!expert_ids) ck.fail(MR_EINVAL, "expert_ids is NULL");
+  if (!npp) ck.fail(MR_EINVAL, "npp is NULL");
+  if (!pow2(A) || A < 16 || A > 256)
+    ck.fail(MR_EUNSUPPORTED, "A=%d is not a power of two in [16, 256]", A);
+  else {
+    const int64_t need = tight_capacity(n, Ep, A);
+    if (sorted_cap < need)
+      ck.fail(MR_ECAPACITY, "sorted_cap=%lld < %lld", (long long)sorted_cap, (long long)need);
+    if (expert_cap < need / A)
+      ck.fail(MR_ECAPACITY, "expert_cap=%lld < %lld", (long long)expert_cap, (long long)(need / A));
+  }
+}
+
+void check_workspace(Checks &ck, const void *ws, size_t ws_bytes, size_t need) {
+  if (!ws) ck.fail(MR_EINVAL, "ws is NULL");
+  else if (!aligned16(ws)) ck.fail(MR_EUNSUPPORTED, "ws is not 16-byte aligned");
+  if (ws_bytes < need) ck.fail(MR_ECAPACITY, "ws_bytes=%zu < %zu", ws_bytes, need);
+}
+
+// Shared implementation of mr_route / mr_route_align / mr_debug_gate_logits.
+int route_impl(const char *fn, const void *x, const void *gate_w, const void *shared_w, int32_t M,
+               int32_t H, int32_t E, int32_t k, float scale, int32_t A, int32_t *ids, float *wts,
+               int32_t *sorted, int64_t sorted_cap, int32_t *expert_ids, int64_t expert_cap, int32_t *npp,
+               float *logits_out, void *ws, size_t ws_bytes, void *stream, bool do_align) {
+  Checks ck;
+  const bool logits_only = logits_out != nullptr;
+  check_route_args(ck, x, gate_w, shared_w, M, H, E, logits_only ? 1 : k);
+  const int32_t sh = shared_w ? 1 : 0;
+  const int64_t S = (int64_t)k + sh, Ep = (int64_t)E + sh, n = (int64_t)M * S;
+  if (!logits_only) {
+    if (!ids && M > 0) ck.fail(MR_EINVAL, "topk_ids is NULL");
+    if (!wts && M > 0) ck.fail(MR_EINVAL, "topk_weights is NULL");
+  }
+  if (do_align) check_align_outputs(ck, n, Ep, A, sorted, sorted_cap, expert_ids, expert_cap, npp);
+  const Layout L = layout_for(M, E > 0 ? E : 1, k > 0 ? k : 1, sh);
+  check_workspace(ck, ws, ws_bytes, L.total);
+  if (M > mr::kSmallMaxTokens)
+    ck.fail(MR_EUNSUPPORTED, "M=%d > %d is not supported by this build yet", M, mr::kSmallMaxTokens);
+  if (ck.code() != MR_OK) return ck.finish(fn);
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (M == 0) {
+    if (do_align) return launch_result(mr::launch_store_zero(npp, s), fn);
+    g_last_error.clear();
+    return MR_OK;
+  }
+  char *wsb = static_cast<char *>(ws);
+  uint32_t *ctr = reinterpret_cast<uint32_t *>(wsb + L.counters);
+
+  mr::SmallParams p{};
+  p.x = static_cast<const uint16_t *>(x);
+  p.w = static_cast<const uint16_t *>(gate_w);
+  p.ws_row = static_cast<const uint16_t *>(shared_w);
+  p.M = M;
+  p.H = H;
+  p.E = E;
+  p.k = k;
+  p.S = (int)S;
+  p.Ep = (int)Ep;
+  p.has_shared = sh;
+  p.scale = scale;
+  p.ids = ids;
+  p.wts = wts;
+  p.logits = logits_only ? logits_out : reinterpret_cast<float *>(wsb + L.logits);
+  p.ticket = &ctr[mr::kCtrTicket];
+  p.logits_only = logits_only ? 1 : 0;
+  p.do_align = do_align ? 1 : 0;
+  p.A = do_align ? A : 64;
+  p.sorted = sorted;
+  p.sorted_cap = sorted_cap;
+  p.expert_ids = expert_ids;
+  p.expert_cap = expert_cap;
+  p.npp = npp;
+  if (do_align) {
+    const int64_t fill = tight_capacity(n, Ep, A);
+    p.fill_count = fill < sorted_cap ? fill : sorted_cap;
+  }
+  return launch_result(mr::launch_route_small(p, s), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+int mr_abi_version(void) { return MR_ABI_VERSION; }
+
+const char *mr_last_error(void) { return g_last_error.c_str(); }
+
+int32_t mr_select_alignment(int32_t M, int32_t k, int32_t E) {
+  if (M < 0 || k < 1 || E < 1) return MR_EINVAL;
+  return ((int64_t)M * k >= (int64_t)128 * E) ? 128 : 64;
+}
+
+int64_t mr_align_capacity(int32_t M, int32_t S, int32_t num_experts, int32_t A) {
+  if (M < 0 || S < 1 || num_experts < 1 || A < 1) return MR_EINVAL;
+  return tight_capacity((int64_t)M * S, num_experts, A);
+}
+
+int64_t mr_expert_ids_capacity(int32_t M, int32_t S, int32_t num_experts, int32_t A) {
+  const int64_t c = mr_align_capacity(M, S, num_experts, A);
+  return c < 0 ? c : c / A;
+}
+
+size_t mr_workspace_bytes(int32_t M_max, int32_t E, int32_t k, int32_t has_shared) {
+  if (M_max < 0 || E < 1 || k < 1) return 0;
+  return layout_for(M_max, E, k, has_shared ? 1 : 0).total;
+}
+
+int mr_workspace_reset(void *ws, size_t ws_bytes, void *stream) {
+  Checks ck;
+  if (!ws) ck.fail(MR_EINVAL, "ws is NULL");
+  if (ws_bytes < mr::kCounterBytes) ck.fail(MR_ECAPACITY, "ws_bytes=%zu < %zu", ws_bytes, mr::kCounterBytes);
+  if (ck.code() != MR_OK) return ck.finish("mr_workspace_reset");
+  return launch_result(mr::launch_zero_words(static_cast<uint32_t *>(ws), mr::kCounterBytes / 4,
+                                             reinterpret_cast<hipStream_t>(stream)),
+                       "mr_workspace_reset");
+}
+
+int mr_route(const void *x, const void *gate_w, const void *shared_w, int32_t M, int32_t H, int32_t E,
+             int32_t k, float scale, int32_t *topk_ids, float *topk_weights, void *ws, size_t ws_bytes,
+             void *stream) {
+  return route_impl("mr_route", x, gate_w, shared_w, M, H, E, k, scale, 64, topk_ids, topk_weights, nullptr, 0,
+                    nullptr, 0, nullptr, nullptr, ws, ws_bytes, stream, false);
+}
+
+int mr_route_align(const void *x, const void *gate_w, const void *shared_w, int32_t M, int32_t H, int32_t E,
+                   int32_t k, float scale, int32_t A, int32_t *topk_ids, float *topk_weights,
+                   int32_t *sorted_token_ids, int64_t sorted_cap, int32_t *expert_ids, int64_t expert_cap,
+                   int32_t *npp, void *ws, size_t ws_bytes, void *stream) {
+  return route_impl("mr_route_align", x, gate_w, shared_w, M, H, E, k, scale, A, topk_ids, topk_weights,
+                    sorted_token_ids, sorted_cap, expert_ids, expert_cap, npp, nullptr, ws, ws_bytes, stream, true);
+}
+
+int mr_debug_gate_logits(const void *x, const void *gate_w, const void *shared_w, int32_t M, int32_t H,
+                         int32_t E, float *logits, void *ws, size_t ws_bytes, void *stream) {
+  if (!logits) {
+    g_last_error = "mr_debug_gate_logits: logits is NULL";
+    return MR_EINVAL;
+  }
+  return route_impl("mr_debug_gate_logits", x, gate_w, shared_w, M, H, E, 1, 1.0f, 64, nullptr, nullptr,
+                    nullptr, 0, nullptr, 0, nullptr, logits, ws, ws_bytes, stream, false);
+}
+
+int mr_align(const int32_t *topk_ids, int32_t M, int32_t S, int32_t num_experts, int32_t A,
+             int32_t *sorted_token_ids, int64_t sorted_cap, int32_t *expert_ids, int64_t expert_cap, int32_t *npp,
+             void *ws, size_t ws_bytes, void *stream) {
+  Checks ck;
+  if (!topk_ids && M > 0) ck.fail(MR_EINVAL, "topk_ids is NULL");
+  if (M < 0) ck.fail(MR_EINVAL, "M=%d < 0", M);
+  if (M > MR_MAX_TOKENS) ck.fail(MR_EUNSUPPORTED, "M=%d > %d", M, MR_MAX_TOKENS);
+  if (S < 1) ck.fail(MR_EINVAL, "S=%d < 1", S);
+  if (S > mr::kMaxTopK + 1) ck.fail(MR_EUNSUPPORTED, "S=%d > %d", S, mr::kMaxTopK + 1);
+  if (num_experts < 1) ck.fail(MR_EINVAL, "num_experts=%d < 1", num_experts);
+  if (num_experts > mr::kMaxAlignExperts)
+    ck.fail(MR_EUNSUPPORTED, "num_experts=%d > %d", num_experts, mr::kMaxAlignExperts);
+  const int64_t n = (int64_t)(M > 0 ? M : 0) * (S > 0 ? S : 0);
+  const int Ep = num_experts > 0 ? num_experts : 1;
+  check_align_outputs(ck, n, Ep, A, sorted_token_ids, sorted_cap, expert_ids, expert_cap, npp);
+  // the align regions of a route workspace with E = Ep and k = S
+  const Layout L = layout_for(M > 0 ? M : 0, Ep, S > 0 ? S : 1, 0);
+  check_workspace(ck, ws, ws_bytes, L.total);
+  if (ck.code() != MR_OK) return ck.finish("mr_align");
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (n == 0) return launch_result(mr::launch_store_zero(npp, s), "mr_align");
+  char *wsb = static_cast<char *>(ws);
+  mr::AlignParams p{};
+  p.ids = topk_ids;
+  p.n = n;
+  p.S = S;
+  p.Ep = Ep;
+  p.A = A;
+  p.sorted = sorted_token_ids;
+  p.sorted_cap = sorted_cap;
+  p.expert_ids = expert_ids;
+  p.expert_cap = expert_cap;
+  p.npp = npp;
+  const int64_t fill = tight_capacity(n, Ep, A);
+  p.fill_count = fill < sorted_cap ? fill : sorted_cap;
+  p.W = mr::align_words_per_expert(Ep);
+  p.nchunks = (int)((n + 64 * p.W - 1) / (64 * p.W));
+  p.ctr = reinterpret_cast<uint32_t *>(wsb + L.counters);
+  p.counts = reinterpret_cast<int32_t *>(wsb + L.counts);
+  p.ranks = reinterpret_cast<int32_t *>(wsb + L.ranks);
+  return launch_result(mr::launch_align(p, s), "mr_align");
+}
+
+}  // extern "C"

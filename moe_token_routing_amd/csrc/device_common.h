@@ -1,0 +1,272 @@
+// device_common.h -- small gfx950 device helpers shared by the route and
+// align kernels: bf16 rounding and ordered keys, wave64 reductions and scans
+// on DPP lane moves, and the release/acquire ticket hand-off.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mr {
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------- bf16 keys --
+
+// fp32 -> bf16 bits, round to nearest, ties to even (finite inputs; an
+// overflow carries into the exponent and becomes infinity).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+// Monotone 16-bit code of a bf16 value: a larger value gets a larger code,
+// and -0 gets the code of +0 so the two compare equal.
+__device__ __forceinline__ uint32_t bf16_order(uint32_t b) {
+  b = (b == 0x8000u) ? 0u : b;
+  return (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
+}
+
+__device__ __forceinline__ uint32_t bf16_from_order(uint32_t o) {
+  return (o & 0x8000u) ? (o & 0x7FFFu) : (~o & 0xFFFFu);
+}
+
+// 32-bit selection key of expert e with fp32 logit z: the order code of
+// bf16(z) in the high half and 0xFFFF - e in the low half.  Unsigned max
+// picks the larger rounded logit and, among equal ones, the lower id (the
+// tie rule of the one-launch router page, Modifications).  Every real key
+// is >= 0x007F0000, so 0 marks an empty slot.
+__device__ __forceinline__ uint32_t make_key(float z, uint32_t e) {
+  return (bf16_order(f32_to_bf16_rne(z)) << 16) | (0xFFFFu - e);
+}
+
+__device__ __forceinline__ uint32_t key_id(uint32_t key) { return 0xFFFFu - (key & 0xFFFFu); }
+
+__device__ __forceinline__ float key_value(uint32_t key) {
+  return bf16_to_f32(bf16_from_order(key >> 16));
+}
+
+// ------------------------------------------------------ wave64 collectives --
+
+__device__ __forceinline__ float readlane_f32(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  // Lanes whose source is outside the row read 0 (the `old` operand).
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// DPP controls (GFX9 encoding).
+constexpr int kQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141; // lane i <- lane 7-i within 8
+constexpr int kRowMirror = 0x140;     // lane i <- lane 15-i within 16
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+
+// Max over the 64 lanes; every lane must be active.  Returns a wave-uniform
+// value.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<kQuadXor1>(v));
+  v = max(v, dpp_u32<kQuadXor2>(v));
+  v = max(v, dpp_u32<kRowHalfMirror>(v));
+  v = max(v, dpp_u32<kRowMirror>(v));
+  uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return max(max(a, b), max(c, d));
+}
+
+// Sum over the 64 lanes (fixed butterfly order, so deterministic); every
+// lane must be active.  Returns a wave-uniform value.
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v += dpp_f32<kQuadXor1>(v);
+  v += dpp_f32<kQuadXor2>(v);
+  v += dpp_f32<kRowHalfMirror>(v);
+  v += dpp_f32<kRowMirror>(v);
+  float a = readlane_f32(v, 0), b = readlane_f32(v, 16);
+  float c = readlane_f32(v, 32), d = readlane_f32(v, 48);
+  return (a + b) + (c + d);
+}
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  v += dpp_u32<kQuadXor1>(v);
+  v += dpp_u32<kQuadXor2>(v);
+  v += dpp_u32<kRowHalfMirror>(v);
+  v += dpp_u32<kRowMirror>(v);
+  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+         __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
+}
+
+// Inclusive prefix sum over the 64 lanes; every lane must be active.
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v, int lane) {
+  v += dpp_u32<kRowShr1>(v);
+  v += dpp_u32<kRowShr2>(v);
+  v += dpp_u32<kRowShr4>(v);
+  v += dpp_u32<kRowShr8>(v);
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 15);
+  const uint32_t r1 = __builtin_amdgcn_readlane(v, 31);
+  const uint32_t r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = lane >> 4;
+  v += (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+  return v;
+}
+
+// Exclusive prefix sum over a block of NT threads (NT/64 waves); `tmp` is
+// LDS scratch of NT/64 + 1 words.  Returns the exclusive prefix for this
+// thread and writes the block total to *total.  Contains barriers: every
+// thread of the block must call it.
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t *tmp, uint32_t *total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t incl = wave_incl_scan_u32(v, lane);
+  if (lane == 63) tmp[wave] = incl;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const uint32_t t = tmp[w];
+    base += (w < wave) ? t : 0u;
+    tot += t;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + incl - v;
+}
+
+// ------------------------------------------------------- grid hand-off ---
+
+// Every thread of a block calls this after its global writes.  Makes the
+// block's writes visible at device (agent) scope, then thread 0 takes a
+// ticket.  Returns true in every thread of the block that took the last of
+// `count` tickets; that block then sees all other blocks' writes (acquire).
+// Contains barriers: every thread of the block must call it.
+__device__ __forceinline__ bool last_block_ticket(uint32_t *ticket, uint32_t count, uint32_t *lds_flag) {
+  __threadfence();  // release this thread's writes at agent scope
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t t = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    *lds_flag = (t == count - 1) ? 1u : 0u;
+  }
+  __syncthreads();
+  const bool last = *lds_flag != 0u;
+  if (last) __threadfence();  // acquire: other blocks' writes are visible
+  return last;
+}
+
+__device__ __forceinline__ void reset_counter(uint32_t *c) {
+  __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Loads of data another block wrote during this launch (after an acquire):
+// always a vector load at agent scope, never a scalar-cache load.
+__device__ __forceinline__ uint32_t ld_agent_u32(const uint32_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent_f32(const float *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Bounded waits: iterations of s_sleep(2) (about 128 cycles each).
+constexpr int kStartSpin = 8192;        // ~0.5 ms
+constexpr int kPublishSpin = 1 << 22;   // ~0.2 s
+
+// Lets a block that has finished its own part help with the work the
+// winning block publishes.  It may wait only once every one of the `nblocks`
+// blocks of the grid has begun: the blocks it waits for are then all
+// resident and never wait themselves, so the wait ends.  If not every block
+// has begun within kStartSpin polls, or the publication does not come
+// within kPublishSpin polls, the block does not help (the winner does all
+// the work).  Returns true, with acquire semantics for every thread, if the
+// block may help.  Contains barriers: every thread must call it.
+__device__ __forceinline__ bool join_after_publish(const uint32_t *started, uint32_t nblocks,
+                                                   const uint32_t *published, uint32_t *lds_flag) {
+  if (threadIdx.x == 0) {
+    uint32_t ok = 0;
+    for (int it = 0; it < kStartSpin; ++it) {
+      if (__hip_atomic_load(started, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= nblocks) {
+        ok = 1;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    if (ok) {
+      ok = 0;
+      for (int it = 0; it < kPublishSpin; ++it) {
+        if (__hip_atomic_load(published, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+          ok = 1;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    *lds_flag = ok;
+  }
+  __syncthreads();
+  const bool ok = *lds_flag != 0u;
+  if (ok) __threadfence();
+  return ok;
+}
+
+// Winner side of join_after_publish: release everything written so far,
+// then raise the flag.  Every thread of the block must call it.
+__device__ __forceinline__ void publish(uint32_t *published) {
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_store(published, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Next item of a shared work queue (block-uniform).  Contains barriers.
+__device__ __forceinline__ uint32_t next_work_item(uint32_t *queue, uint32_t *lds_slot) {
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *lds_slot = __hip_atomic_fetch_add(queue, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  return *lds_slot;
+}
+
+// Counts block exits; the last block to leave returns true (and then owns
+// every counter of the launch, which nobody else touches any more).
+__device__ __forceinline__ bool last_to_exit(uint32_t *exited, uint32_t nblocks, uint32_t *lds_flag) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t t = __hip_atomic_fetch_add(exited, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    *lds_flag = (t == nblocks - 1) ? 1u : 0u;
+  }
+  __syncthreads();
+  return *lds_flag != 0u;
+}
+
+// ---------------------------------------------------------- bf16 dot ----
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+
+// 16-byte streaming load (non-temporal hint: data read once per launch).
+__device__ __forceinline__ uint4 ld_stream_16(const uint4 *p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2_t, u); }
+
+// acc + sum_{j<8} a_j * b_j for two 16-byte vectors of 8 bf16 each (fp32
+// accumulation through v_dot2_f32_bf16; bf16 x bf16 products are exact).
+__device__ __forceinline__ float dot8_bf16(uint4 a, uint4 b, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a.x), as_bf16x2(b.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a.y), as_bf16x2(b.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a.z), as_bf16x2(b.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a.w), as_bf16x2(b.w), acc, false);
+  return acc;
+}
+
+}  // namespace mr

@@ -1,0 +1,78 @@
+// kernels.h -- launch parameters shared by the host entry points (api.cpp)
+// and the kernels.  Internal to the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mr {
+
+constexpr int kMaxTopK = 32;            // routed k
+constexpr int kMaxRouteExperts = 1024;  // routed E for the route kernels
+constexpr int kMaxAlignExperts = 4096;  // E' for align
+constexpr int kSmallMaxTokens = 16;     // route_small handles M <= 16
+
+// Counter words at the start of the workspace (all zero between launches).
+enum CounterIndex : int {
+  kCtrTicket = 0,     // last-block election
+  kCtrStarted = 1,    // blocks that have begun
+  kCtrDone = 2,       // phase-one completions
+  kCtrPublished = 3,  // winner's publication flag
+  kCtrWork = 4,       // work-queue head
+  kCtrExited = 5,     // block exits
+  kCtrTileBase = 16,  // per-row-tile tickets follow
+};
+constexpr size_t kCounterBytes = 256;
+
+// Small-M fused route (+ align).
+struct SmallParams {
+  const uint16_t *x;       // [M, H] bf16
+  const uint16_t *w;       // [E, H] bf16
+  const uint16_t *ws_row;  // [H] bf16 or null
+  int M, H, E, k, S, Ep, has_shared;
+  float scale;
+  int32_t *ids;   // [M, S]
+  float *wts;     // [M, S]
+  float *logits;  // [M, Ep] fp32 (workspace, or the caller's buffer when logits_only)
+  uint32_t *ticket;
+  int logits_only;
+  // align
+  int do_align, A;
+  int32_t *sorted;
+  int64_t sorted_cap;
+  int32_t *expert_ids;
+  int64_t expert_cap;
+  int32_t *npp;
+  int64_t fill_count;  // sentinel pre-fill length
+};
+
+// Standalone align.
+struct AlignParams {
+  const int32_t *ids;  // [n]
+  int64_t n;
+  int S, Ep, A;
+  int32_t *sorted;
+  int64_t sorted_cap;
+  int32_t *expert_ids;
+  int64_t expert_cap;
+  int32_t *npp;
+  int64_t fill_count;
+  int W;        // bitmap words per expert; a chunk is 64 * W pairs
+  int nchunks;
+  uint32_t *ctr;    // counter words
+  int32_t *counts;  // [nchunks, Ep]: per-chunk counts, then per-chunk bases
+  int32_t *ranks;   // [n] rank of each pair inside its chunk
+};
+
+int small_rows_per_block(int Ep);
+hipError_t launch_route_small(const SmallParams &p, hipStream_t stream);
+
+int align_words_per_expert(int Ep);
+hipError_t launch_align(const AlignParams &p, hipStream_t stream);
+
+// Fill n words with zero / write *npp = 0 (small kernels, graph-safe).
+hipError_t launch_zero_words(uint32_t *p, size_t n, hipStream_t stream);
+hipError_t launch_store_zero(int32_t *p, hipStream_t stream);
+
+}  // namespace mr
