@@ -110,8 +110,8 @@ int64_t mr_expert_ids_capacity(int32_t M, int32_t S, int32_t num_experts, int32_
  * mr_debug_gate_logits. */
 size_t mr_workspace_bytes(int32_t M_max, int32_t E, int32_t k, int32_t has_shared);
 
-/* Re-zero the workspace's counters on `stream` (a small fill kernel, safe to
- * capture).  Needed only after an aborted launch. */
+/* Re-zero the whole workspace (ws_bytes bytes) on `stream` with a small fill
+ * kernel (safe to capture).  Needed only after an aborted launch. */
 int mr_workspace_reset(void *ws, size_t ws_bytes, void *stream);
 
 /* Route [R], Modifications: gate contraction in fp32, bf16 rounding of the

@@ -61,7 +61,7 @@ __global__ __launch_bounds__(kThreads) void align_kernel(AlignParams p) {
         pre[(size_t)e * W + w] = (uint16_t)run;
         run += __popcll(bm[(size_t)e * W + w]);
       }
-      p.counts[(size_t)c * Ep + e] = (int32_t)run;
+      st_agent(p.counts + (size_t)c * Ep + e, (int32_t)run);
     }
     __syncthreads();
     for (int64_t i = lo + tid; i < hi; i += kThreads) {
@@ -69,12 +69,12 @@ __global__ __launch_bounds__(kThreads) void align_kernel(AlignParams p) {
       if (e >= 0 && e < Ep) {
         const int li = (int)(i - lo);
         const size_t j = (size_t)e * W + (li >> 6);
-        p.ranks[i] = (int32_t)(pre[j] + __popcll(bm[j] & ((1ull << (li & 63)) - 1ull)));
+        st_agent(p.ranks + i, (int32_t)(pre[j] + __popcll(bm[j] & ((1ull << (li & 63)) - 1ull))));
       }
     }
     const int32_t sentinel = (int32_t)p.n;
     for (int64_t i = (int64_t)blockIdx.x * kThreads + tid; i < p.fill_count; i += (int64_t)gridDim.x * kThreads)
-      p.sorted[i] = sentinel;
+      st_agent(p.sorted + i, sentinel);
   }
 
   // ---- the last chunk block computes offsets and bases -----------------
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(kThreads) void align_kernel(AlignParams p) {
     uint32_t local = 0;
     for (int e = e0; e < e0 + per && e < Ep; ++e) {
       uint32_t tot = 0;
-      for (int c = 0; c < nch; ++c) tot += (uint32_t)p.counts[(size_t)c * Ep + e];
+      for (int c = 0; c < nch; ++c) tot += (uint32_t)ld_agent(p.counts + (size_t)c * Ep + e);
       local += (tot + A - 1) / A * A;
     }
     uint32_t total;
@@ -95,8 +95,8 @@ __global__ __launch_bounds__(kThreads) void align_kernel(AlignParams p) {
     for (int e = e0; e < e0 + per && e < Ep; ++e) {
       uint32_t run = base;
       for (int c = 0; c < nch; ++c) {
-        const uint32_t t = (uint32_t)p.counts[(size_t)c * Ep + e];
-        p.counts[(size_t)c * Ep + e] = (int32_t)run;
+        const uint32_t t = (uint32_t)ld_agent(p.counts + (size_t)c * Ep + e);
+        st_agent(p.counts + (size_t)c * Ep + e, (int32_t)run);
         run += t;
       }
       const uint32_t P = (run - base + A - 1) / A * A;
@@ -120,7 +120,7 @@ __global__ __launch_bounds__(kThreads) void align_kernel(AlignParams p) {
       for (int64_t i = lo + tid; i < hi; i += kThreads) {
         const int32_t e = p.ids[i];
         if (e < 0 || e >= Ep) continue;
-        const int64_t pos = (int64_t)p.counts[(size_t)c * Ep + e] + p.ranks[i];
+        const int64_t pos = (int64_t)ld_agent(p.counts + (size_t)c * Ep + e) + ld_agent(p.ranks + i);
         if (pos < p.sorted_cap) p.sorted[pos] = (int32_t)i;
       }
     }

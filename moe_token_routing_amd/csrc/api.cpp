@@ -61,15 +61,17 @@ int64_t tight_capacity(int64_t n, int64_t Ep, int64_t A) {
 
 // Workspace regions for one call.
 struct Layout {
-  size_t counters = 0, logits = 0, counts = 0, ranks = 0, total = 0;
+  size_t counters = 0, keys = 0, shared = 0, counts = 0, ranks = 0, total = 0;
 };
 
 Layout layout_for(int64_t M, int64_t E, int64_t k, int64_t sh) {
   Layout L;
   const int64_t S = k + sh, Ep = E + sh, n = M * S;
   size_t o = mr::kCounterBytes;
-  L.logits = o;
-  o = align_up(o + (size_t)mr::kSmallMaxTokens * (size_t)(Ep > 0 ? Ep : 1) * 4, 256);
+  L.keys = o;  // small-M selection keys [16, E]
+  o = align_up(o + (size_t)mr::kSmallMaxTokens * (size_t)(E > 0 ? E : 1) * 4, 256);
+  L.shared = o;  // small-M shared logits [16] (64-bit words)
+  o = align_up(o + (size_t)mr::kSmallMaxTokens * 8, 256);
   const int W = mr::align_words_per_expert((int)(Ep > 0 ? Ep : 1));
   const int64_t nch = (n + 64 * W - 1) / (64 * W);
   L.counts = o;
@@ -173,11 +175,16 @@ int route_impl(const char *fn, const void *x, const void *gate_w, const void *sh
   p.scale = scale;
   p.ids = ids;
   p.wts = wts;
-  p.logits = logits_only ? logits_out : reinterpret_cast<float *>(wsb + L.logits);
-  p.ticket = &ctr[mr::kCtrTicket];
+  p.keys = reinterpret_cast<uint32_t *>(wsb + L.keys);
+  p.shared_logit = reinterpret_cast<unsigned long long *>(wsb + L.shared);
+  p.logits_out = logits_out;
+  p.ctr = ctr;
   p.logits_only = logits_only ? 1 : 0;
   p.do_align = do_align ? 1 : 0;
   p.A = do_align ? A : 64;
+  p.log2A = 0;
+  while ((1 << p.log2A) < p.A) ++p.log2A;
+  p.S_magic = (uint32_t)((((uint64_t)1 << 32) + (uint64_t)S - 1) / (uint64_t)S);
   p.sorted = sorted;
   p.sorted_cap = sorted_cap;
   p.expert_ids = expert_ids;
@@ -221,9 +228,10 @@ size_t mr_workspace_bytes(int32_t M_max, int32_t E, int32_t k, int32_t has_share
 int mr_workspace_reset(void *ws, size_t ws_bytes, void *stream) {
   Checks ck;
   if (!ws) ck.fail(MR_EINVAL, "ws is NULL");
+  else if (!aligned16(ws)) ck.fail(MR_EUNSUPPORTED, "ws is not 16-byte aligned");
   if (ws_bytes < mr::kCounterBytes) ck.fail(MR_ECAPACITY, "ws_bytes=%zu < %zu", ws_bytes, mr::kCounterBytes);
   if (ck.code() != MR_OK) return ck.finish("mr_workspace_reset");
-  return launch_result(mr::launch_zero_words(static_cast<uint32_t *>(ws), mr::kCounterBytes / 4,
+  return launch_result(mr::launch_zero_words(static_cast<uint32_t *>(ws), ws_bytes / 4,
                                              reinterpret_cast<hipStream_t>(stream)),
                        "mr_workspace_reset");
 }

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace mr {
 
 constexpr int kWave = 64;
@@ -86,6 +88,20 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return max(max(a, b), max(c, d));
 }
 
+// Max over the 64 lanes, left in every lane (no scalar round trip): DPP
+// within rows of 16, then gfx950's permlane16/permlane32 swaps pair each lane
+// with lane^16 and lane^32.  Every lane must be active.
+__device__ __forceinline__ uint32_t wave_max_all_u32(uint32_t v) {
+  v = max(v, dpp_u32<kQuadXor1>(v));
+  v = max(v, dpp_u32<kQuadXor2>(v));
+  v = max(v, dpp_u32<kRowHalfMirror>(v));
+  v = max(v, dpp_u32<kRowMirror>(v));
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max(a[0], a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max(b[0], b[1]);
+}
+
 // Sum over the 64 lanes (fixed butterfly order, so deterministic); every
 // lane must be active.  Returns a wave-uniform value.
 __device__ __forceinline__ float wave_sum_f32(float v) {
@@ -121,6 +137,25 @@ __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v, int lane) {
   return v;
 }
 
+// Inclusive prefix maximum over the 64 lanes (signed); every lane active.
+__device__ __forceinline__ int32_t wave_incl_max_i32(int32_t v, int lane) {
+  auto shr = [](int32_t x, auto ctrl) {
+    return __builtin_amdgcn_update_dpp((int)0x80000000, x, decltype(ctrl)::value, 0xF, 0xF, false);
+  };
+  v = max(v, shr(v, std::integral_constant<int, kRowShr1>{}));
+  v = max(v, shr(v, std::integral_constant<int, kRowShr2>{}));
+  v = max(v, shr(v, std::integral_constant<int, kRowShr4>{}));
+  v = max(v, shr(v, std::integral_constant<int, kRowShr8>{}));
+  const int32_t r0 = __builtin_amdgcn_readlane(v, 15);
+  const int32_t r1 = __builtin_amdgcn_readlane(v, 31);
+  const int32_t r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = lane >> 4;
+  if (row >= 1) v = max(v, r0);
+  if (row >= 2) v = max(v, r1);
+  if (row >= 3) v = max(v, r2);
+  return v;
+}
+
 // Exclusive prefix sum over a block of NT threads (NT/64 waves); `tmp` is
 // LDS scratch of NT/64 + 1 words.  Returns the exclusive prefix for this
 // thread and writes the block total to *total.  Contains barriers: every
@@ -143,37 +178,102 @@ __device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t *tm
   return base + incl - v;
 }
 
-// ------------------------------------------------------- grid hand-off ---
+// Makes LDS writes by other lanes of this wave visible to this lane's later
+// LDS reads.  The hardware already executes a wave's LDS operations in order;
+// the fence stops the compiler from reusing a value this lane itself stored
+// or loaded earlier (lanes exchanging data through LDS without it is a data
+// race the compiler may optimise away).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+}
 
-// Every thread of a block calls this after its global writes.  Makes the
-// block's writes visible at device (agent) scope, then thread 0 takes a
-// ticket.  Returns true in every thread of the block that took the last of
-// `count` tickets; that block then sees all other blocks' writes (acquire).
-// Contains barriers: every thread of the block must call it.
+// ------------------------------------------------------- grid hand-off ---
+//
+// Blocks of one launch exchange data through agent-coherent accesses: a
+// relaxed agent-scope atomic store is a write-through store (sc1) that is
+// complete once the issuing wave's store counter drains, and a relaxed
+// agent-scope atomic load (sc1) reads the coherent copy, never a stale line
+// in another XCD's L2.  Every hand-off therefore goes: data stores (st_agent)
+// -> each wave waits for its own stores -> barrier -> one relaxed atomic per
+// block -> the receiving block's loads (ld_agent).  No L2 write-back or
+// invalidate is needed, so hundreds of blocks can take tickets without
+// serialising on cache maintenance.
+
+__device__ __forceinline__ void st_agent(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(uint32_t *p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(int32_t *p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(unsigned long long *p, unsigned long long v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long ld_agent(const unsigned long long *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_agent(const uint32_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t ld_agent(const int32_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Waits until every global store and atomic this wave issued has completed
+// (s_waitcnt with all counters at zero).
+__device__ __forceinline__ void wait_own_stores() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Every thread of a block calls this after its st_agent writes.  Returns true
+// in every thread of the block that took the last of `count` tickets; that
+// block may then ld_agent everything the other blocks wrote before their
+// tickets.  Contains barriers: every thread of the block must call it.
 __device__ __forceinline__ bool last_block_ticket(uint32_t *ticket, uint32_t count, uint32_t *lds_flag) {
-  __threadfence();  // release this thread's writes at agent scope
+  wait_own_stores();
   __syncthreads();
   if (threadIdx.x == 0) {
-    const uint32_t t = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t t = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *lds_flag = (t == count - 1) ? 1u : 0u;
   }
   __syncthreads();
-  const bool last = *lds_flag != 0u;
-  if (last) __threadfence();  // acquire: other blocks' writes are visible
-  return last;
+  return *lds_flag != 0u;
+}
+
+// Two-level version of last_block_ticket for large grids: block b first
+// takes a ticket on first-level counter b % kLanes (each in its own 256-byte
+// slot, `stride` words apart); the block that completes a first-level
+// counter then takes a ticket on `top`.  Same contract and return value as
+// last_block_ticket.  The winner must later reset all counters it used
+// (reset_two_level_tickets).
+template <int kLanes>
+__device__ __forceinline__ bool last_block_ticket2(uint32_t *lanes, int stride, uint32_t *top, uint32_t count,
+                                                   uint32_t *lds_flag) {
+  wait_own_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t nl = count < (uint32_t)kLanes ? count : (uint32_t)kLanes;
+    const uint32_t r = blockIdx.x % nl;
+    const uint32_t in_lane = (count - 1 - r) / nl + 1;  // blocks sharing this counter
+    uint32_t last = 0;
+    const uint32_t t = __hip_atomic_fetch_add(lanes + (size_t)r * stride, 1u, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    if (t == in_lane - 1) {
+      const uint32_t u = __hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last = (u == nl - 1) ? 1u : 0u;
+    }
+    *lds_flag = last;
+  }
+  __syncthreads();
+  return *lds_flag != 0u;
 }
 
 __device__ __forceinline__ void reset_counter(uint32_t *c) {
   __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Loads of data another block wrote during this launch (after an acquire):
-// always a vector load at agent scope, never a scalar-cache load.
-__device__ __forceinline__ uint32_t ld_agent_u32(const uint32_t *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_agent_f32(const float *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Bounded waits: iterations of s_sleep(2) (about 128 cycles each).
@@ -202,7 +302,7 @@ __device__ __forceinline__ bool join_after_publish(const uint32_t *started, uint
     if (ok) {
       ok = 0;
       for (int it = 0; it < kPublishSpin; ++it) {
-        if (__hip_atomic_load(published, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+        if (__hip_atomic_load(published, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
           ok = 1;
           break;
         }
@@ -212,17 +312,16 @@ __device__ __forceinline__ bool join_after_publish(const uint32_t *started, uint
     *lds_flag = ok;
   }
   __syncthreads();
-  const bool ok = *lds_flag != 0u;
-  if (ok) __threadfence();
-  return ok;
+  return *lds_flag != 0u;
 }
 
-// Winner side of join_after_publish: release everything written so far,
-// then raise the flag.  Every thread of the block must call it.
+// Winner side of join_after_publish: after its st_agent writes, every wave
+// waits for its stores, then thread 0 raises the flag.  Every thread of the
+// block must call it.
 __device__ __forceinline__ void publish(uint32_t *published) {
-  __threadfence();
+  wait_own_stores();
   __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_store(published, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) __hip_atomic_store(published, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Next item of a shared work queue (block-uniform).  Contains barriers.
@@ -235,11 +334,16 @@ __device__ __forceinline__ uint32_t next_work_item(uint32_t *queue, uint32_t *ld
 }
 
 // Counts block exits; the last block to leave returns true (and then owns
-// every counter of the launch, which nobody else touches any more).
+// every counter of the launch, which nobody else touches any more).  The
+// counters are only ever accessed with agent-scope atomics; each wave waits
+// for its own outstanding atomics before the exit ticket, so every earlier
+// counter update of every block has been performed when the last block sees
+// its ticket.
 __device__ __forceinline__ bool last_to_exit(uint32_t *exited, uint32_t nblocks, uint32_t *lds_flag) {
+  wait_own_stores();
   __syncthreads();
   if (threadIdx.x == 0) {
-    const uint32_t t = __hip_atomic_fetch_add(exited, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t t = __hip_atomic_fetch_add(exited, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *lds_flag = (t == nblocks - 1) ? 1u : 0u;
   }
   __syncthreads();

@@ -14,16 +14,21 @@ constexpr int kMaxAlignExperts = 4096;  // E' for align
 constexpr int kSmallMaxTokens = 16;     // route_small handles M <= 16
 
 // Counter words at the start of the workspace (all zero between launches).
+// The first 256 bytes hold single counters; then kTicketLanes first-level
+// ticket counters follow, each alone in its own 256-byte slot so that blocks
+// taking tickets spread their atomics over several addresses.
 enum CounterIndex : int {
-  kCtrTicket = 0,     // last-block election
+  kCtrTicket = 0,     // last-block election (second level)
   kCtrStarted = 1,    // blocks that have begun
   kCtrDone = 2,       // phase-one completions
   kCtrPublished = 3,  // winner's publication flag
   kCtrWork = 4,       // work-queue head
   kCtrExited = 5,     // block exits
-  kCtrTileBase = 16,  // per-row-tile tickets follow
+  kCtrError = 6,      // set to 1 if a bounded wait gave up (never expected)
 };
-constexpr size_t kCounterBytes = 256;
+constexpr int kTicketLanes = 16;
+constexpr int kTicketLaneStride = 64;  // words (256 bytes)
+constexpr size_t kCounterBytes = 256 + (size_t)kTicketLanes * kTicketLaneStride * 4;
 
 // Small-M fused route (+ align).
 struct SmallParams {
@@ -34,11 +39,16 @@ struct SmallParams {
   float scale;
   int32_t *ids;   // [M, S]
   float *wts;     // [M, S]
-  float *logits;  // [M, Ep] fp32 (workspace, or the caller's buffer when logits_only)
-  uint32_t *ticket;
+  // Workspace, all zero between launches: selection keys [M, E] (0 = not yet
+  // written) and the shared logits [M] as (1 << 32 | fp32 bits).
+  uint32_t *keys;
+  unsigned long long *shared_logit;
+  float *logits_out;  // logits_only: the caller's [M, Ep] fp32 buffer
+  uint32_t *ctr;      // counter words (kCounterBytes)
   int logits_only;
   // align
-  int do_align, A;
+  int do_align, A, log2A;
+  uint32_t S_magic;  // ceil(2^32 / S): i / S == umulhi(i, S_magic) for i < 2^32 / S
   int32_t *sorted;
   int64_t sorted_cap;
   int32_t *expert_ids;
@@ -65,7 +75,7 @@ struct AlignParams {
   int32_t *ranks;   // [n] rank of each pair inside its chunk
 };
 
-int small_rows_per_block(int Ep);
+int small_rows_per_block(int Ep, int M);
 hipError_t launch_route_small(const SmallParams &p, hipStream_t stream);
 
 int align_words_per_expert(int Ep);

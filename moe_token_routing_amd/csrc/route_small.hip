@@ -15,17 +15,28 @@
 //   grid = ceil(E' / RPB) blocks of 256 threads; block b owns gate rows
 //   [b*RPB, b*RPB + RPB) of the E' = E + shared rows (the shared row is
 //   row E).  Each row is split over 4/RPB waves; a thread streams 16-byte
-//   chunks of its row (coalesced 128-bit loads) and of the M token rows,
-//   accumulating with v_dot2_f32_bf16.  Partial sums are reduced with DPP
-//   butterflies and across waves through LDS; the block writes fp32 logits
-//   to the workspace, every block pre-fills its slice of sorted_token_ids
-//   with the sentinel, releases its writes and takes a ticket.
-//   The block that takes the last ticket (acquire) runs the tail: one wave
-//   per token row does the top-k as k rounds of a wave-wide max over packed
-//   32-bit keys (value code << 16 | 0xFFFF - id) with DPP, then the softmax,
-//   shared slot and stores; then the align: per-expert 32-bit row bitmaps in
-//   LDS give counts and stable ranks, a block scan gives padded offsets, and
-//   each pair is scattered to offset + rank.  The tail resets the ticket.
+//   chunks of its row (coalesced 128-bit non-temporal loads) and of the M
+//   token rows, all issued before any arithmetic, accumulating with
+//   v_dot2_f32_bf16.  Partial sums are reduced with DPP butterflies and across
+//   waves through LDS.
+//
+// Hand-off (no ticket): every block writes, with write-through agent-scope
+//   stores, the 32-bit selection key of each routed logit -- the bf16 order
+//   code in the high half and 0xFFFF - e in the low half, never 0 -- and the
+//   shared logit as (1 << 32 | fp32 bits).  Block 0, after its own gate rows,
+//   polls the key buffer with coherent loads until its rows are complete (a
+//   zero marks a slot not yet written); the poll IS the load of the tail's
+//   input.  It then re-zeroes the buffer for the next launch.  Only block 0
+//   ever waits, on blocks that never wait, and the wait is bounded.  The
+//   sentinel pre-fill of sorted_token_ids is issued first in every block and
+//   completed before that block's keys are written, so block 0 never races it.
+//
+// Tail (block 0): one wave per token row selects the top-k as k rounds of a
+//   wave-wide maximum over the packed keys (DPP within rows of 16, then
+//   gfx950's permlane16/32 swaps), then the softmax, shared slot and stores;
+//   then one wave aligns: LDS row bitmaps per expert give counts and stable
+//   ranks, one wave scan gives the padded offsets, each pair is scattered to
+//   offset + rank.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -34,27 +45,59 @@ namespace mr {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kPollSpin = 1 << 21;  // bound on block 0's polls (each is one memory round trip)
+// Most blocks an align of M <= 16 rows can produce: every pair alone in its
+// expert's block, at the smallest alignment (16).
+constexpr int kMaxSmallBlocks = kSmallMaxTokens * (kMaxTopK + 1);
 
-// Tail of the launch: top-k, softmax, shared slot for rows m = wave, wave+4, ...
-// NK = keys per lane (E <= 64 * NK).
+// Max of N keys held in registers (a balanced tree, depth log2 N).
+template <int N>
+__device__ __forceinline__ uint32_t max_of(const uint32_t (&a)[N]) {
+  uint32_t t[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) t[i] = a[i];
+#pragma unroll
+  for (int w = N / 2; w > 0; w >>= 1)
+#pragma unroll
+    for (int i = 0; i < w; ++i) t[i] = max(t[i], t[i + w]);
+  return t[0];
+}
+
+// Tail, part 1: rows m = wave, wave+4, ...  Each lane holds NK keys (experts
+// lane, lane+64, ...); a selection round is the lane maximum, a wave-wide
+// maximum, and clearing the one key equal to it (keys are unique).
 template <int NK>
 __device__ void route_tail_rows(const SmallParams &p, int32_t *lds_ids) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int E = p.E, k = p.k, S = p.S, Ep = p.Ep;
+  const int E = p.E, k = p.k, S = p.S;
   for (int m = wave; m < p.M; m += kThreads / kWave) {
-    const float *zr = p.logits + (size_t)m * Ep;
+    uint32_t *kr = p.keys + (size_t)m * E;
     uint32_t keys[NK];
+    unsigned long long sv = 0;
+    // poll until every key of this row (and its shared logit) has arrived
+    for (int it = 0;; ++it) {
+#pragma unroll
+      for (int i = 0; i < NK; ++i) keys[i] = ld_agent(kr + min(lane + kWave * i, E - 1));
+      if (p.has_shared) sv = ld_agent(p.shared_logit + m);
+      bool missing = p.has_shared && (sv >> 32) == 0;
+#pragma unroll
+      for (int i = 0; i < NK; ++i) missing |= (lane + kWave * i < E) && keys[i] == 0u;
+      if (__builtin_amdgcn_ballot_w64(missing) == 0) break;
+      if (it == kPollSpin) {
+        if (lane == 0) st_agent(p.ctr + kCtrError, 1u);
+        break;
+      }
+    }
+    // consume: mask lanes past E, re-zero the slots for the next launch
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
-      const int e = lane + kWave * i;
-      keys[i] = (e < E) ? make_key(zr[e], (uint32_t)e) : 0u;
+      if (lane + kWave * i < E) st_agent(kr + lane + kWave * i, 0u);
+      else keys[i] = 0u;
     }
+    if (p.has_shared && lane == 0) st_agent(p.shared_logit + m, 0ull);
     uint32_t mine = 0u;  // lane j < k keeps the j-th chosen key
     for (int j = 0; j < k; ++j) {
-      uint32_t lm = keys[0];
-#pragma unroll
-      for (int i = 1; i < NK; ++i) lm = max(lm, keys[i]);
-      const uint32_t top = wave_max_u32(lm);
+      const uint32_t top = wave_max_all_u32(max_of(keys));
       mine = (lane == j) ? top : mine;
 #pragma unroll
       for (int i = 0; i < NK; ++i) keys[i] = (keys[i] == top) ? 0u : keys[i];
@@ -66,7 +109,7 @@ __device__ void route_tail_rows(const SmallParams &p, int32_t *lds_ids) {
     int32_t id = (int32_t)key_id(mine);
     float w = ex / den;
     if (p.has_shared && lane == k) {
-      const float s = zr[E];
+      const float s = __uint_as_float((uint32_t)sv);
       id = E;
       w = p.scale / (1.0f + expf(-s));
     }
@@ -78,88 +121,133 @@ __device__ void route_tail_rows(const SmallParams &p, int32_t *lds_ids) {
   }
 }
 
-// Align over the n = M*S pairs whose ids are in lds_ids.  Every id in a row
-// is distinct (top-k ids plus the shared id E), so a 32-bit bitmap of rows
-// per expert gives both the count and the stable rank of each pair.
-__device__ void align_tail_small(const SmallParams &p, const int32_t *lds_ids, uint32_t *bm,
-                                 uint32_t *off, uint32_t *scan_tmp) {
-  const int tid = threadIdx.x;
-  const int S = p.S, Ep = p.Ep, A = p.A;
-  const int n = p.M * S;
-  for (int e = tid; e < Ep; e += kThreads) bm[e] = 0u;
-  __syncthreads();
-  for (int i = tid; i < n; i += kThreads) {
+// Tail, part 2: align over the n = M*S pairs whose ids are in lds_ids, by
+// ONE wave (no block barriers; a wave's LDS operations complete in order, and
+// wave_lds_sync orders them for the compiler).  Every id in a row is distinct
+// (top-k ids plus the shared id E), so a 32-bit bitmap of rows per routed
+// expert gives both its count and each pair's stable rank.  Lane l owns the
+// NK consecutive routed experts [NK*l, NK*l + NK): a local prefix over them
+// plus one wave scan gives every padded offset in expert order.  The shared
+// expert (id E, the largest) holds every row once: its segment is rows
+// 0..M-1 in order, after all routed experts.
+template <int NK>
+__device__ void align_wave(const SmallParams &p, const int32_t *lds_ids, uint32_t *bm, uint32_t *offl,
+                           int32_t *mark) {
+  const int lane = threadIdx.x & 63;
+  const int E = p.E, S = p.S, M = p.M, sh = p.log2A;
+  const uint32_t amask = (1u << sh) - 1u;
+  const int n = M * S;
+  const int e0 = NK * lane;
+#pragma unroll
+  for (int j = 0; j < NK; ++j) bm[e0 + j] = 0u;
+  wave_lds_sync();
+  for (int i = lane; i < n; i += kWave) {
     const int e = lds_ids[i];
-    if (e >= 0 && e < Ep) atomicOr(&bm[e], 1u << (i / S));
+    if (e >= 0 && e < E) atomicOr(&bm[e], 1u << __umulhi((uint32_t)i, p.S_magic));
   }
-  __syncthreads();
-  // padded sizes, exclusive scan over experts: thread t owns a contiguous
-  // run of experts [t*per, t*per + per)
-  const int per = (Ep + kThreads - 1) / kThreads;
-  const int e0 = tid * per;
-  uint32_t local = 0;
-  for (int e = e0; e < e0 + per && e < Ep; ++e) {
-    const uint32_t c = __builtin_popcount(bm[e]);
-    local += (c + A - 1) / A * A;
+  wave_lds_sync();
+  uint32_t P[NK], pre[NK], lane_total = 0;
+#pragma unroll
+  for (int j = 0; j < NK; ++j) {
+    P[j] = (__builtin_popcount(bm[e0 + j]) + amask) & ~amask;
+    pre[j] = lane_total;
+    lane_total += P[j];
   }
-  uint32_t total;
-  uint32_t base = block_excl_scan_u32<kThreads>(local, scan_tmp, &total);
-  for (int e = e0; e < e0 + per && e < Ep; ++e) {
-    const uint32_t c = __builtin_popcount(bm[e]);
-    const uint32_t P = (c + A - 1) / A * A;
-    off[e] = base;
-    for (uint32_t b = base / A; b < (base + P) / A; ++b)
-      if (b < (uint64_t)p.expert_cap) p.expert_ids[b] = e;
-    base += P;
+  const uint32_t incl = wave_incl_scan_u32(lane_total, lane);
+  const uint32_t base = incl - lane_total;
+  const uint32_t routed = __builtin_amdgcn_readlane(incl, 63);
+  const uint32_t P_sh = p.has_shared ? (((uint32_t)M + amask) & ~amask) : 0u;
+  const uint32_t total = routed + P_sh;
+  const uint32_t nblocks = min((uint64_t)(total >> sh), (uint64_t)p.expert_cap);
+  // expert_ids: expert ids grow with the block index, so block b's expert is
+  // the running maximum of the segment-start marks at or before b
+  for (uint32_t b = lane; b < nblocks; b += kWave) mark[b] = -1;
+  wave_lds_sync();
+#pragma unroll
+  for (int j = 0; j < NK; ++j) {
+    const uint32_t off = base + pre[j];
+    offl[e0 + j] = off;
+    if (P[j] != 0u) mark[off >> sh] = e0 + j;
   }
-  __syncthreads();
-  for (int i = tid; i < n; i += kThreads) {
+  if (p.has_shared && lane == 0 && P_sh != 0u) mark[routed >> sh] = E;
+  wave_lds_sync();
+  int32_t carry = -1;
+  for (uint32_t b0 = 0; b0 < nblocks; b0 += kWave) {
+    const uint32_t b = b0 + lane;
+    const int32_t v = wave_incl_max_i32(max(carry, b < nblocks ? mark[b] : -1), lane);
+    if (b < nblocks) p.expert_ids[b] = v;
+    carry = __builtin_amdgcn_readlane(v, 63);
+  }
+  wave_lds_sync();
+  for (int i = lane; i < n; i += kWave) {
     const int e = lds_ids[i];
-    if (e < 0 || e >= Ep) continue;
-    const int m = i / S;
-    const uint32_t rank = __builtin_popcount(bm[e] & ((1u << m) - 1u));
-    const uint32_t pos = off[e] + rank;
+    const uint32_t m = __umulhi((uint32_t)i, p.S_magic);
+    uint32_t pos;
+    if (e >= 0 && e < E) pos = offl[e] + __builtin_popcount(bm[e] & ((1u << m) - 1u));
+    else if (p.has_shared && e == E) pos = routed + m;
+    else continue;
     if (pos < (uint64_t)p.sorted_cap) p.sorted[pos] = i;
   }
-  if (tid == 0) *p.npp = (int32_t)total;
+  if (lane == 0) *p.npp = (int32_t)total;
 }
 
 template <int RPB, int MAXM, int NK>
 __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
   constexpr int WPR = (kThreads / kWave) / RPB;  // waves per gate row
   __shared__ float red[kThreads / kWave][MAXM];
-  __shared__ uint32_t flag;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rloc = wave / WPR, sub = wave % WPR;
   const int row = blockIdx.x * RPB + rloc;
   const int H = p.H, M = p.M;
   const int nch = H >> 3;  // 16-byte chunks per row
 
+  // ---- sentinel pre-fill of this block's slice of sorted_token_ids ------
+  if (p.do_align) {
+    const int32_t sentinel = M * p.S;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + tid; i < p.fill_count; i += (int64_t)gridDim.x * kThreads)
+      st_agent(p.sorted + i, sentinel);
+  }
+
   // ---- gate: stream this wave's share of one gate row -----------------
+  // Each iteration first issues every load it needs -- the gate-row chunks
+  // (non-temporal: read once) and the same chunks of every token row -- and
+  // only then accumulates, so a thread has all its loads in flight at once.
   float acc[MAXM];
 #pragma unroll
   for (int m = 0; m < MAXM; ++m) acc[m] = 0.0f;
   if (row < p.Ep) {
     const uint4 *wrow = reinterpret_cast<const uint4 *>(row < p.E ? p.w + (size_t)row * H : p.ws_row);
     const uint4 *xb = reinterpret_cast<const uint4 *>(p.x);
-    constexpr int kU = 4;  // chunks in flight per thread
-    for (int c0 = sub * kWave + lane; c0 < nch; c0 += kU * WPR * kWave) {
-      uint4 wv[kU];
+    constexpr int kChunks = 2 * RPB;             // chunks per thread per iteration (H = 4096: one iteration)
+    constexpr int kStride = WPR * kWave;         // threads sharing the row
+    constexpr int kRowsPerGroup = 16 / kChunks;  // token rows whose chunks are loaded together
+    int c0 = sub * kWave + lane;
+    for (; c0 + (kChunks - 1) * kStride < nch; c0 += kChunks * kStride) {
+      uint4 wv[kChunks];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int c = c0 + u * WPR * kWave;
-        wv[u] = (c < nch) ? ld_stream_16(wrow + c) : make_uint4(0, 0, 0, 0);
-      }
+      for (int u = 0; u < kChunks; ++u) wv[u] = ld_stream_16(wrow + c0 + u * kStride);
 #pragma unroll
-      for (int m = 0; m < MAXM; ++m) {
-        if (m < M) {
+      for (int g = 0; g < MAXM; g += kRowsPerGroup) {
+        if (g < M) {
+          uint4 xv[kRowsPerGroup][kChunks];
 #pragma unroll
-          for (int u = 0; u < kU; ++u) {
-            const int c = c0 + u * WPR * kWave;
-            if (c < nch) acc[m] = dot8_bf16(wv[u], xb[(size_t)m * nch + c], acc[m]);
+          for (int r = 0; r < kRowsPerGroup; ++r) {
+            const int m = min(g + r, M - 1);  // rows past M reload row M-1; their sums are dropped
+#pragma unroll
+            for (int u = 0; u < kChunks; ++u) xv[r][u] = xb[(size_t)m * nch + c0 + u * kStride];
           }
+#pragma unroll
+          for (int r = 0; r < kRowsPerGroup; ++r)
+#pragma unroll
+            for (int u = 0; u < kChunks; ++u) acc[g + r] = dot8_bf16(wv[u], xv[r][u], acc[g + r]);
         }
       }
+    }
+    for (; c0 < nch; c0 += kStride) {  // ragged tail: one chunk at a time
+      const uint4 wv = ld_stream_16(wrow + c0);
+#pragma unroll
+      for (int m = 0; m < MAXM; ++m)
+        if (m < M) acc[m] = dot8_bf16(wv, xb[(size_t)m * nch + c0], acc[m]);
     }
   }
 #pragma unroll
@@ -169,13 +257,7 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
       if (lane == 0) red[wave][m] = v;
     }
   }
-
-  // ---- sentinel pre-fill of this block's slice of sorted_token_ids ------
-  if (p.do_align) {
-    const int32_t sentinel = M * p.S;
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + tid; i < p.fill_count; i += (int64_t)gridDim.x * kThreads)
-      p.sorted[i] = sentinel;
-  }
+  wait_own_stores();  // the pre-fill is complete before any key is published
   __syncthreads();
   if (tid < RPB * M) {
     const int rl = tid / M, m = tid % M;
@@ -183,23 +265,26 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
     float z = 0.0f;
 #pragma unroll
     for (int s = 0; s < WPR; ++s) z += red[rl * WPR + s][m];
-    if (e < p.Ep) p.logits[(size_t)m * p.Ep + e] = z;
+    if (p.logits_only) {
+      if (e < p.Ep) p.logits_out[(size_t)m * p.Ep + e] = z;
+    } else if (e < p.E) {
+      st_agent(p.keys + (size_t)m * p.E + e, make_key(z, (uint32_t)e));
+    } else if (e == p.E) {
+      st_agent(p.shared_logit + m, (1ull << 32) | __float_as_uint(z));
+    }
   }
-  if (p.logits_only) return;
+  if (p.logits_only || blockIdx.x != 0) return;
 
-  // ---- hand-off: the last block runs the tail ---------------------------
-  if (!last_block_ticket(p.ticket, gridDim.x, &flag)) return;
-
+  // ---- block 0: the tail ---------------------------------------------------
   __shared__ int32_t lds_ids[MAXM * (kMaxTopK + 1)];
   route_tail_rows<NK>(p, lds_ids);
   if (p.do_align) {
-    __shared__ uint32_t bm[kMaxRouteExperts + 1];
-    __shared__ uint32_t off[kMaxRouteExperts + 1];
-    __shared__ uint32_t scan_tmp[kThreads / kWave + 1];
+    __shared__ uint32_t bm[kWave * NK];
+    __shared__ uint32_t offl[kWave * NK];
+    __shared__ int32_t mark[kMaxSmallBlocks];
     __syncthreads();
-    align_tail_small(p, lds_ids, bm, off, scan_tmp);
+    if (wave == 0) align_wave<NK>(p, lds_ids, bm, offl, mark);
   }
-  if (tid == 0) reset_counter(p.ticket);
 }
 
 template <int RPB, int MAXM>
@@ -213,27 +298,21 @@ hipError_t launch_nk(const SmallParams &p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int RPB>
-hipError_t launch_m(const SmallParams &p, hipStream_t stream) {
-  if (p.M <= 4) return launch_nk<RPB, 4>(p, stream);
-  if (p.M <= 8) return launch_nk<RPB, 8>(p, stream);
-  return launch_nk<RPB, 16>(p, stream);
-}
-
 }  // namespace
 
-int small_rows_per_block(int Ep) {
-  // Enough blocks to spread the weight stream over the CUs: one or two gate
-  // rows per block up to 512 rows, four beyond.
-  return Ep <= 256 ? 1 : (Ep <= 1024 ? 2 : 4);
+int small_rows_per_block(int Ep, int M) {
+  // Two gate rows per block at M <= 4 (257 blocks for 513 rows: a thread
+  // holds 4 row chunks and 4x4 token chunks); one row per block above that
+  // or for small E' (a thread then holds 2 row chunks and up to 8x2 token
+  // chunks per load group).
+  return (M <= 4 && Ep > 256) ? 2 : 1;
 }
 
 hipError_t launch_route_small(const SmallParams &p, hipStream_t stream) {
-  switch (small_rows_per_block(p.Ep)) {
-    case 1: return launch_m<1>(p, stream);
-    case 2: return launch_m<2>(p, stream);
-    default: return launch_m<4>(p, stream);
-  }
+  if (small_rows_per_block(p.Ep, p.M) == 2) return launch_nk<2, 4>(p, stream);
+  if (p.M <= 4) return launch_nk<1, 4>(p, stream);
+  if (p.M <= 8) return launch_nk<1, 8>(p, stream);
+  return launch_nk<1, 16>(p, stream);
 }
 
 }  // namespace mr

@@ -82,7 +82,7 @@ def test_router_sweep_small_m(M):
     (128, 8, 2048, False, 16, 1.0),
     (1024, 32, 512, True, 7, 0.5),
     (100, 7, 200, True, 9, 1.0),     # ragged: E and H not multiples of the wave
-    (33, 33, 8, False, 3, 1.0),      # k = E: every expert chosen
+    (32, 32, 8, False, 3, 1.0),      # k = E: every expert chosen
 ])
 def test_router_shapes(E, k, H, shared, M, scale):
     _say("shape", E, k, H, shared, M, scale)
