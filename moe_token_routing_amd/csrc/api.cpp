@@ -59,25 +59,36 @@ int64_t tight_capacity(int64_t n, int64_t Ep, int64_t A) {
   return n + touched * (A - 1);
 }
 
-// Workspace regions for one call.
+// Workspace regions for one call.  Every region grows with M, so a workspace
+// sized for M_max serves every M <= M_max.
 struct Layout {
-  size_t counters = 0, keys = 0, shared = 0, counts = 0, ranks = 0, total = 0;
+  size_t counters = 0, keys = 0, shared = 0;             // small-M route
+  size_t tile_ticket = 0, cand = 0, lshared = 0, tcounts = 0;  // large-M route
+  size_t counts = 0, ranks = 0;                          // align / large-M ranks
+  size_t total = 0;
 };
 
 Layout layout_for(int64_t M, int64_t E, int64_t k, int64_t sh) {
   Layout L;
   const int64_t S = k + sh, Ep = E + sh, n = M * S;
+  const int64_t NE = (E + mr::kLargeBE - 1) / mr::kLargeBE;
+  const int64_t MTmax = (M + 15) / 16;  // row tiles at the smallest tile height
+  auto take = [](size_t &o, size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + (bytes ? bytes : 4), 256);
+    return at;
+  };
   size_t o = mr::kCounterBytes;
-  L.keys = o;  // small-M selection keys [16, E]
-  o = align_up(o + (size_t)mr::kSmallMaxTokens * (size_t)(E > 0 ? E : 1) * 4, 256);
-  L.shared = o;  // small-M shared logits [16] (64-bit words)
-  o = align_up(o + (size_t)mr::kSmallMaxTokens * 8, 256);
+  L.keys = take(o, (size_t)mr::kSmallMaxTokens * (size_t)E * 4);
+  L.shared = take(o, (size_t)mr::kSmallMaxTokens * 8);
+  L.tile_ticket = take(o, (size_t)MTmax * 4);
+  L.cand = take(o, (size_t)(M * NE * k) * 4);
+  L.lshared = take(o, (size_t)M * 4);
+  L.tcounts = take(o, (size_t)(MTmax * Ep) * 4);
   const int W = mr::align_words_per_expert((int)(Ep > 0 ? Ep : 1));
   const int64_t nch = (n + 64 * W - 1) / (64 * W);
-  L.counts = o;
-  o = align_up(o + (size_t)(nch > 0 ? nch : 1) * (size_t)(Ep > 0 ? Ep : 1) * 4, 256);
-  L.ranks = o;
-  o = align_up(o + (size_t)(n > 0 ? n : 1) * 4, 256);
+  L.counts = take(o, (size_t)(nch * Ep) * 4);
+  L.ranks = take(o, (size_t)n * 4);
   L.total = o;
   return L;
 }
@@ -148,8 +159,6 @@ int route_impl(const char *fn, const void *x, const void *gate_w, const void *sh
   if (do_align) check_align_outputs(ck, n, Ep, A, sorted, sorted_cap, expert_ids, expert_cap, npp);
   const Layout L = layout_for(M, E > 0 ? E : 1, k > 0 ? k : 1, sh);
   check_workspace(ck, ws, ws_bytes, L.total);
-  if (M > mr::kSmallMaxTokens)
-    ck.fail(MR_EUNSUPPORTED, "M=%d > %d is not supported by this build yet", M, mr::kSmallMaxTokens);
   if (ck.code() != MR_OK) return ck.finish(fn);
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -160,6 +169,55 @@ int route_impl(const char *fn, const void *x, const void *gate_w, const void *sh
   }
   char *wsb = static_cast<char *>(ws);
   uint32_t *ctr = reinterpret_cast<uint32_t *>(wsb + L.counters);
+  int log2A = 0;
+  while ((1 << log2A) < A) ++log2A;
+  const uint32_t S_magic = (uint32_t)((((uint64_t)1 << 32) + (uint64_t)S - 1) / (uint64_t)S);
+  int64_t fill = 0;
+  if (do_align) {
+    fill = tight_capacity(n, Ep, A);
+    if (fill > sorted_cap) fill = sorted_cap;
+  }
+
+  if (M > mr::kSmallMaxTokens) {
+    mr::LargeParams q{};
+    q.x = static_cast<const uint16_t *>(x);
+    q.w = static_cast<const uint16_t *>(gate_w);
+    q.ws_row = static_cast<const uint16_t *>(shared_w);
+    q.M = M;
+    q.H = H;
+    q.E = E;
+    q.k = logits_only ? 1 : k;
+    q.S = (int)S;
+    q.Ep = (int)Ep;
+    q.has_shared = sh;
+    q.scale = scale;
+    q.ids = ids;
+    q.wts = wts;
+    const int BT = mr::large_tile_tokens(M, E);
+    q.MT = (M + BT - 1) / BT;
+    q.NE = (E + mr::kLargeBE - 1) / mr::kLargeBE;
+    q.row_groups = (q.MT + 7) / 8;
+    q.ctr = ctr;
+    q.tile_ticket = reinterpret_cast<uint32_t *>(wsb + L.tile_ticket);
+    q.cand = reinterpret_cast<uint32_t *>(wsb + L.cand);
+    q.shared_logit = reinterpret_cast<float *>(wsb + L.lshared);
+    q.tile_counts = reinterpret_cast<int32_t *>(wsb + L.tcounts);
+    q.ranks = reinterpret_cast<int32_t *>(wsb + L.ranks);
+    q.do_align = do_align ? 1 : 0;
+    q.A = do_align ? A : 64;
+    q.log2A = do_align ? log2A : 6;
+    q.S_magic = S_magic;
+    q.sorted = sorted;
+    q.sorted_cap = sorted_cap;
+    q.expert_ids = expert_ids;
+    q.expert_cap = expert_cap;
+    q.npp = npp;
+    q.fill_count = fill;
+    q.may_help = (do_align && mr::large_grid(q) <= mr::large_max_resident_blocks(BT)) ? 1 : 0;
+    q.logits_out = logits_out;
+    q.logits_only = logits_only ? 1 : 0;
+    return launch_result(mr::launch_route_large(q, BT, s), fn);
+  }
 
   mr::SmallParams p{};
   p.x = static_cast<const uint16_t *>(x);
@@ -168,7 +226,7 @@ int route_impl(const char *fn, const void *x, const void *gate_w, const void *sh
   p.M = M;
   p.H = H;
   p.E = E;
-  p.k = k;
+  p.k = logits_only ? 1 : k;
   p.S = (int)S;
   p.Ep = (int)Ep;
   p.has_shared = sh;
@@ -182,18 +240,14 @@ int route_impl(const char *fn, const void *x, const void *gate_w, const void *sh
   p.logits_only = logits_only ? 1 : 0;
   p.do_align = do_align ? 1 : 0;
   p.A = do_align ? A : 64;
-  p.log2A = 0;
-  while ((1 << p.log2A) < p.A) ++p.log2A;
-  p.S_magic = (uint32_t)((((uint64_t)1 << 32) + (uint64_t)S - 1) / (uint64_t)S);
+  p.log2A = do_align ? log2A : 6;
+  p.S_magic = S_magic;
   p.sorted = sorted;
   p.sorted_cap = sorted_cap;
   p.expert_ids = expert_ids;
   p.expert_cap = expert_cap;
   p.npp = npp;
-  if (do_align) {
-    const int64_t fill = tight_capacity(n, Ep, A);
-    p.fill_count = fill < sorted_cap ? fill : sorted_cap;
-  }
+  p.fill_count = fill;
   return launch_result(mr::launch_route_small(p, s), fn);
 }
 

@@ -244,21 +244,21 @@ __device__ __forceinline__ bool last_block_ticket(uint32_t *ticket, uint32_t cou
   return *lds_flag != 0u;
 }
 
-// Two-level version of last_block_ticket for large grids: block b first
-// takes a ticket on first-level counter b % kLanes (each in its own 256-byte
-// slot, `stride` words apart); the block that completes a first-level
-// counter then takes a ticket on `top`.  Same contract and return value as
-// last_block_ticket.  The winner must later reset all counters it used
-// (reset_two_level_tickets).
+// Two-level version of last_block_ticket for many arrivals: arrival `idx`
+// (unique in [0, count)) first takes a ticket on first-level counter
+// idx % kLanes (each in its own 256-byte slot, `stride` words apart); the
+// arrival that completes a first-level counter then takes a ticket on `top`.
+// Same contract and return value as last_block_ticket.  The winner must
+// reset all the counters (first level and top) before anything reuses them.
 template <int kLanes>
 __device__ __forceinline__ bool last_block_ticket2(uint32_t *lanes, int stride, uint32_t *top, uint32_t count,
-                                                   uint32_t *lds_flag) {
+                                                   uint32_t *lds_flag, uint32_t idx) {
   wait_own_stores();
   __syncthreads();
   if (threadIdx.x == 0) {
     const uint32_t nl = count < (uint32_t)kLanes ? count : (uint32_t)kLanes;
-    const uint32_t r = blockIdx.x % nl;
-    const uint32_t in_lane = (count - 1 - r) / nl + 1;  // blocks sharing this counter
+    const uint32_t r = idx % nl;
+    const uint32_t in_lane = (count - 1 - r) / nl + 1;  // arrivals sharing this counter
     uint32_t last = 0;
     const uint32_t t = __hip_atomic_fetch_add(lanes + (size_t)r * stride, 1u, __ATOMIC_RELAXED,
                                               __HIP_MEMORY_SCOPE_AGENT);

@@ -10,6 +10,11 @@
   chosen experts whose fp64 gap is at least one bf16 ulp.  Weights are
   compared per expert id, 1e-5 relative.  The align outputs are bit-exact
   against the oracle's align run on the GPU's own ids.
+* Weights of a row are compared with the oracle's directly only when the
+  kernel's fp32 logits round to the same bf16 values as the oracle's double
+  logits for every chosen expert (the rounding of a logit lying within fp32
+  error of a bf16 midpoint is decided by the accumulation precision); every
+  row's weights are compared through the backstop.
 * Backstop for every row (exempt or not): the oracle's rounding, selection,
   softmax and shared slot applied to the kernel's own fp32 logits reproduce
   the GPU ids bit-exactly and the weights within 1e-5; and each fp32 logit is
@@ -59,6 +64,20 @@ def check_weights(w_gpu, ids_gpu, w_ref, ids_ref, rows=None):
         for e, w in zip(ids_gpu[m].tolist(), w_gpu[m].astype(np.float64).tolist()):
             assert e in ref, (m, e)
             assert abs(w - ref[e]) <= RTOL_W * abs(ref[e]) + ATOL_W, (m, e, w, ref[e])
+
+
+def same_rounding_rows(logits_gpu, ref, ids_gpu, k):
+    """Rows whose chosen experts' logits round to the same bf16 on both
+    sides (kernel fp32 vs oracle double)."""
+    E = ref["z"].shape[1]
+    rg = oracle.round_bf16(logits_gpu[:, :E].astype(np.float64))
+    ro = oracle.round_bf16(ref["z"])
+    rows = []
+    for m in range(ids_gpu.shape[0]):
+        sel = [e for e in ids_gpu[m, :k].tolist() if 0 <= e < E]
+        if np.array_equal(rg[m, sel], ro[m, sel]):
+            rows.append(m)
+    return rows
 
 
 def check_ids_random(ids_gpu, ref, k):

@@ -1,0 +1,168 @@
+"""Parity of the large-M (MFMA) route + align path with the CPU oracle, at the
+prefill workloads' full sizes and on ragged and edge shapes (needs a gfx950
+GPU).  Every case prints its name and shape before it runs."""
+import numpy as np
+import pytest
+
+import oracle
+from moe_token_routing_amd import workloads
+from parity_util import check_align, check_backstop, check_ids_random, check_weights, same_rounding_rows
+from gpu_util import logits_gpu, route_align_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _cuda():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import moe_token_routing_amd as mr
+
+    mr._binding.lib()
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _run(d, k, scale=1.0, A=None, exact=False, backstop=True):
+    M, E = d["x"].shape[0], d["w"].shape[0]
+    has_shared = d["ws"] is not None
+    ref = oracle.route(d["x"], d["w"], d["ws"], k, scale)
+    g = route_align_gpu(d, k, scale, A)
+    lg = logits_gpu(d) if (backstop or not exact) else None
+    if backstop:
+        check_backstop(d["x"], d["w"], d["ws"], lg, g["topk_ids"], g["topk_weights"], k, scale, ref)
+    if exact:
+        assert np.array_equal(g["topk_ids"], ref["ids"]), "ids differ on exact inputs"
+        check_weights(g["topk_weights"], g["topk_ids"], ref["weights"], ref["ids"])
+        exempt = 0
+    else:
+        exempt = check_ids_random(g["topk_ids"], ref, k)
+        rows = same_rounding_rows(lg, ref, g["topk_ids"], k)
+        same = [m for m in rows if sorted(g["topk_ids"][m].tolist()) == sorted(ref["ids"][m].tolist())]
+        check_weights(g["topk_weights"], g["topk_ids"], ref["weights"], ref["ids"], same)
+    check_align(g["topk_ids"], E + has_shared, g["A"], g["sorted_token_ids"], g["expert_ids"], g["npp"][0])
+    return exempt, g
+
+
+def test_prefill_e128_m128():
+    wl = workloads.PREFILL_E128_M128
+    _say(wl)
+    d = workloads.workload_inputs(wl)
+    _run(d, wl.k)                # tier A = 64
+    _run(d, wl.k, A=128)
+
+
+def test_prefill_e128_m2048_zipf_tier128():
+    wl = workloads.PREFILL_E128_M2048_ZIPF
+    _say(wl)
+    d = workloads.workload_inputs(wl)
+    exempt, g = _run(d, wl.k)
+    assert g["A"] == 128
+    print("exempt rows", exempt)
+
+
+@pytest.mark.parametrize("M", [m for m in workloads.SWEEP_M if m > 16])
+def test_router_sweep_large_m(M):
+    wl = workloads.sweep_workload(M)
+    _say(wl)
+    exempt, g = _run(workloads.workload_inputs(wl), wl.k)
+    assert g["A"] == 64
+
+
+@pytest.mark.parametrize("M", [17, 64, 200])
+def test_exact_inputs_large_m(M):
+    _say("exact", M)
+    d = workloads.make_inputs(M, 512, 4096, True, "int", seed=300 + M)
+    _run(d, 10, exact=True)
+
+
+@pytest.mark.parametrize("E,k,H,shared,M,scale", [
+    (1024, 32, 512, True, 100, 0.5),   # largest E and k
+    (100, 7, 200, True, 50, 1.0),      # ragged E, H % 32 != 0
+    (16, 16, 64, False, 33, 1.0),      # k = E
+    (130, 3, 96, True, 257, 2.0),      # two expert tiles, second nearly empty
+    (512, 10, 8, True, 70, 1.0),       # H smaller than one MFMA step
+    (256, 8, 1024, False, 1000, 1.0),
+])
+def test_large_shapes(E, k, H, shared, M, scale):
+    _say("shape", E, k, H, shared, M, scale)
+    d = workloads.make_inputs(M, E, H, shared, "normal", seed=E * 7 + k)
+    _run(d, k, scale)
+
+
+def test_exact_large_alignment_variants():
+    d = workloads.make_inputs(96, 512, 4096, True, "int", seed=5)
+    for A in [16, 32, 256]:
+        _say("A", A)
+        _run(d, 10, A=A, exact=True, backstop=False)
+
+
+def test_grid_larger_than_gpu():
+    """More tiles than fit on the GPU at once: blocks then never wait for the
+    published offsets and the winner scatters alone."""
+    _say("M=20000 E=512")
+    d = workloads.make_inputs(20000, 512, 256, True, "normal", seed=21)
+    _run(d, 10)
+
+
+def test_large_consecutive_and_graph():
+    import torch
+    import moe_token_routing_amd as mr
+
+    ws = mr.new_workspace(2048, 512, 10, True)
+    for it, (M, seed) in enumerate([(512, 1), (2048, 2), (40, 3), (17, 4), (512, 1)]):
+        _say("consecutive", it, M)
+        d = workloads.make_inputs(M, 512, 4096, True, "int", seed=seed)
+        ref = oracle.route(d["x"], d["w"], d["ws"], 10, 1.0)
+        g = route_align_gpu(d, 10, 1.0, ws=ws)
+        assert np.array_equal(g["topk_ids"], ref["ids"])
+        check_align(g["topk_ids"], 513, g["A"], g["sorted_token_ids"], g["expert_ids"], g["npp"][0])
+    assert int(ws[:4352].view(torch.int32).abs().sum().item()) == 0
+
+    d = workloads.make_inputs(512, 512, 4096, True, "normal", seed=8)
+    x, w, s = to_dev(d["x"]), to_dev(d["w"]), to_dev(d["ws"])
+    eager = mr.mr_route_align(x, w, s, 10, 1.0, workspace=ws)
+    torch.cuda.synchronize()
+    ref = {kk: v.clone() for kk, v in eager.items() if hasattr(v, "clone")}
+    bufs = {kk: torch.full_like(v, -5) for kk, v in ref.items()}
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=torch.cuda.Stream()):
+        mr.mr_route_align(x, w, s, 10, 1.0, workspace=ws, topk_ids=bufs["topk_ids"],
+                          topk_weights=bufs["topk_weights"], sorted_token_ids=bufs["sorted_token_ids"],
+                          expert_ids=bufs["expert_ids"], npp=bufs["npp"])
+    npp = int(ref["npp"].item())
+    for rep in range(4):
+        _say("graph replay", rep)
+        for v in bufs.values():
+            v.fill_(-5)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bufs["topk_ids"], ref["topk_ids"])
+        assert torch.equal(bufs["topk_weights"], ref["topk_weights"])
+        assert int(bufs["npp"].item()) == npp
+        assert torch.equal(bufs["sorted_token_ids"][:npp], ref["sorted_token_ids"][:npp])
+        assert torch.equal(bufs["expert_ids"][: npp // 64], ref["expert_ids"][: npp // 64])
+
+
+def test_large_route_only_matches_route_align():
+    import moe_token_routing_amd as mr
+
+    d = workloads.make_inputs(300, 512, 4096, True, "normal", seed=9)
+    x, w, s = to_dev(d["x"]), to_dev(d["w"]), to_dev(d["ws"])
+    ws = mr.new_workspace(300, 512, 10, True)
+    ids, wts = mr.mr_route(x, w, s, 10, 1.0, workspace=ws)
+    g = mr.mr_route_align(x, w, s, 10, 1.0, workspace=ws)
+    assert np.array_equal(ids.cpu().numpy(), g["topk_ids"].cpu().numpy())
+    assert np.array_equal(wts.cpu().numpy(), g["topk_weights"].cpu().numpy())
+
+
+def test_large_debug_logits_exact():
+    d = workloads.make_inputs(100, 512, 4096, True, "int", seed=12)
+    z, s = oracle.gate(d["x"], d["w"], d["ws"])
+    lg = logits_gpu(d)
+    assert np.array_equal(lg[:, :512].astype(np.float64), z)
+    assert np.array_equal(lg[:, 512].astype(np.float64), s)

@@ -5,7 +5,7 @@ import pytest
 
 import oracle
 from moe_token_routing_amd import workloads
-from parity_util import check_align, check_backstop, check_ids_random, check_weights
+from parity_util import check_align, check_backstop, check_ids_random, check_weights, same_rounding_rows
 from gpu_util import logits_gpu, route_align_gpu, to_dev
 
 pytestmark = pytest.mark.gpu
@@ -32,19 +32,18 @@ def _run_and_check(d, k, scale, A=None, exact=False):
     ref = oracle.route(d["x"], d["w"], d["ws"], k, scale)
     g = route_align_gpu(d, k, scale, A)
     A = g["A"]
+    lg = logits_gpu(d)
+    check_backstop(d["x"], d["w"], d["ws"], lg, g["topk_ids"], g["topk_weights"], k, scale, ref)
     if exact:
         assert np.array_equal(g["topk_ids"], ref["ids"]), "ids differ on exact inputs"
         check_weights(g["topk_weights"], g["topk_ids"], ref["weights"], ref["ids"])
         exempt = 0
     else:
         exempt = check_ids_random(g["topk_ids"], ref, k)
-        rows = [m for m in range(M)]
-        # weights per expert id in rows whose chosen set matches
+        rows = same_rounding_rows(lg, ref, g["topk_ids"], k)
         same = [m for m in rows if sorted(g["topk_ids"][m].tolist()) == sorted(ref["ids"][m].tolist())]
         check_weights(g["topk_weights"], g["topk_ids"], ref["weights"], ref["ids"], same)
     check_align(g["topk_ids"], E + has_shared, A, g["sorted_token_ids"], g["expert_ids"], g["npp"][0])
-    lg = logits_gpu(d)
-    check_backstop(d["x"], d["w"], d["ws"], lg, g["topk_ids"], g["topk_weights"], k, scale, ref)
     return exempt
 
 
