@@ -63,7 +63,7 @@ int64_t tight_capacity(int64_t n, int64_t Ep, int64_t A) {
 // sized for M_max serves every M <= M_max.
 struct Layout {
   size_t counters = 0, keys = 0, shared = 0;             // small-M route
-  size_t tile_ticket = 0, cand = 0, lshared = 0, tcounts = 0;  // large-M route
+  size_t tile_ticket = 0, cand = 0, lshared = 0, tcounts = 0, eoff = 0;  // large-M route
   size_t counts = 0, ranks = 0;                          // align / large-M ranks
   size_t total = 0;
 };
@@ -85,6 +85,7 @@ Layout layout_for(int64_t M, int64_t E, int64_t k, int64_t sh) {
   L.cand = take(o, (size_t)(M * NE * k) * 4);
   L.lshared = take(o, (size_t)M * 4);
   L.tcounts = take(o, (size_t)(MTmax * Ep) * 4);
+  L.eoff = take(o, (size_t)Ep * 4);
   const int W = mr::align_words_per_expert((int)(Ep > 0 ? Ep : 1));
   const int64_t nch = (n + 64 * W - 1) / (64 * W);
   L.counts = take(o, (size_t)(nch * Ep) * 4);
@@ -202,6 +203,7 @@ int route_impl(const char *fn, const void *x, const void *gate_w, const void *sh
     q.cand = reinterpret_cast<uint32_t *>(wsb + L.cand);
     q.shared_logit = reinterpret_cast<float *>(wsb + L.lshared);
     q.tile_counts = reinterpret_cast<int32_t *>(wsb + L.tcounts);
+    q.expert_off = reinterpret_cast<int32_t *>(wsb + L.eoff);
     q.ranks = reinterpret_cast<int32_t *>(wsb + L.ranks);
     q.do_align = do_align ? 1 : 0;
     q.A = do_align ? A : 64;

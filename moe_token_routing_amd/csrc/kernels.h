@@ -91,7 +91,8 @@ struct LargeParams {
   uint32_t *tile_ticket;  // [MT] per-row-tile tickets
   uint32_t *cand;         // [M, NE, k] candidate keys of every expert tile
   float *shared_logit;    // [M]
-  int32_t *tile_counts;   // [MT, Ep]: per-tile counts, then per-tile bases
+  int32_t *tile_counts;   // [MT, Ep]: per-tile counts, then per-tile exclusive prefixes
+  int32_t *expert_off;    // [Ep] padded offset of each expert
   int32_t *ranks;         // [M * S] rank of each pair inside its row tile
   int do_align, A, log2A;
   uint32_t S_magic;

@@ -148,45 +148,48 @@ __global__ __launch_bounds__(kThreads) void route_large_kernel(LargeParams p) {
       const int t = min(t0 + c * 16 + (lane & 15), M - 1);
       xp[c] = p.x + (size_t)t * H + kg;
     }
-    const uint16_t *sp = p.has_shared ? p.ws_row + kg : nullptr;
-    const int nfull = H >> 5;  // full 32-wide k steps
+    // the shared row (or, without one, gate row 0 as a harmless stand-in) is
+    // dotted in every wave so the main loop has no branches; only wave 0 of
+    // expert tile 0 keeps the result
+    const uint16_t *sp = (p.has_shared ? p.ws_row : p.w) + kg;
+    const int nfull = H >> 5;                // full 32-wide k steps
+    const int nmain = nfull - nfull % PD;    // steps in whole groups of PD
 
     uint4 abuf[PD][2], bbuf[PD][NB], sbuf[PD];
+    auto load_step = [&](int u, int s) {
 #pragma unroll
-    for (int u = 0; u < PD; ++u) {
-      if (u < nfull) {
+      for (int a = 0; a < 2; ++a) abuf[u][a] = ld16(wp[a] + 32 * s);
 #pragma unroll
-        for (int a = 0; a < 2; ++a) abuf[u][a] = ld16(wp[a] + 32 * u);
+      for (int c = 0; c < NB; ++c) bbuf[u][c] = ld16(xp[c] + 32 * s);
+      sbuf[u] = ld16(sp + 32 * s);
+    };
+    auto compute_step = [&](int u) {
 #pragma unroll
-        for (int c = 0; c < NB; ++c) bbuf[u][c] = ld16(xp[c] + 32 * u);
-        if (do_sh) sbuf[u] = ld16(sp + 32 * u);
-      }
-    }
-    for (int s0 = 0; s0 < nfull; s0 += PD) {
+      for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int u = 0; u < PD; ++u) {
-        const int s = s0 + u;
-        if (s < nfull) {
+        for (int c = 0; c < NB; ++c)
+          acc[a][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(abuf[u][a]), as_bf16x8(bbuf[u][c]),
+                                                             acc[a][c], 0, 0, 0);
 #pragma unroll
-          for (int a = 0; a < 2; ++a)
+      for (int c = 0; c < NB; ++c) sacc[c] = dot8_bf16(bbuf[u][c], sbuf[u], sacc[c]);
+    };
+    if (nmain > 0) {
 #pragma unroll
-            for (int c = 0; c < NB; ++c)
-              acc[a][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(abuf[u][a]), as_bf16x8(bbuf[u][c]),
-                                                                 acc[a][c], 0, 0, 0);
-          if (do_sh) {
+      for (int u = 0; u < PD; ++u) load_step(u, u);
+      // steady state: PD steps always in flight, no branches inside a group
+      for (int s0 = 0; s0 + PD < nmain; s0 += PD) {
 #pragma unroll
-            for (int c = 0; c < NB; ++c) sacc[c] = dot8_bf16(bbuf[u][c], sbuf[u], sacc[c]);
-          }
-          const int sn = s + PD;
-          if (sn < nfull) {
-#pragma unroll
-            for (int a = 0; a < 2; ++a) abuf[u][a] = ld16(wp[a] + 32 * sn);
-#pragma unroll
-            for (int c = 0; c < NB; ++c) bbuf[u][c] = ld16(xp[c] + 32 * sn);
-            if (do_sh) sbuf[u] = ld16(sp + 32 * sn);
-          }
+        for (int u = 0; u < PD; ++u) {
+          compute_step(u);
+          load_step(u, s0 + PD + u);
         }
       }
+#pragma unroll
+      for (int u = 0; u < PD; ++u) compute_step(u);
+    }
+    for (int s = nmain; s < nfull; ++s) {  // leftover full steps
+      load_step(0, s);
+      compute_step(0);
     }
     if ((H & 31) != 0) {  // ragged last step: lanes past H contribute zeros
       const int kk = nfull * 32;
@@ -196,16 +199,14 @@ __global__ __launch_bounds__(kThreads) void route_large_kernel(LargeParams p) {
       for (int a = 0; a < 2; ++a) av[a] = ok ? ld16(wp[a] + kk) : make_uint4(0, 0, 0, 0);
 #pragma unroll
       for (int c = 0; c < NB; ++c) bv[c] = ok ? ld16(xp[c] + kk) : make_uint4(0, 0, 0, 0);
-      if (do_sh && ok) sv = ld16(sp + kk);
+      if (ok) sv = ld16(sp + kk);
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int c = 0; c < NB; ++c)
           acc[a][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[a]), as_bf16x8(bv[c]), acc[a][c], 0, 0, 0);
-      if (do_sh) {
 #pragma unroll
-        for (int c = 0; c < NB; ++c) sacc[c] = dot8_bf16(bv[c], sv, sacc[c]);
-      }
+      for (int c = 0; c < NB; ++c) sacc[c] = dot8_bf16(bv[c], sv, sacc[c]);
     }
     // shared logits: sum the four lane groups holding the same token
     if (do_sh) {
@@ -356,42 +357,40 @@ __global__ __launch_bounds__(kThreads) void route_large_kernel(LargeParams p) {
     if (tid < kTicketLanes) reset_counter(ctr + 64 + tid * kTicketLaneStride);
     if (tid == 0) reset_counter(ctr + kCtrTicket);
     const int MT = p.MT, A = p.A, sh = p.log2A;
-    const int per = (Ep + kThreads - 1) / kThreads;
-    const int e0 = tid * per;
-    // per-expert totals over the row tiles, 8 independent loads at a time
-    uint32_t local = 0;
-    for (int e = e0; e < e0 + per && e < Ep; ++e) {
-      uint32_t tot = 0;
-      for (int r0 = 0; r0 < MT; r0 += 8) {
-        uint32_t v[8];
+    const uint32_t amask = (uint32_t)A - 1u;
+    // Thread t owns expert columns t, t + 256, ...: the column's per-tile
+    // counts become per-tile exclusive prefixes (loads issued 32 rows at a
+    // time), and its padded total feeds a block scan per 256 experts.
+    uint32_t carry = 0;
+    for (int e0 = 0; e0 < Ep; e0 += kThreads) {
+      const int e = e0 + tid;
+      uint32_t run = 0;
+      if (e < Ep) {
+        for (int r0 = 0; r0 < MT; r0 += 32) {
+          uint32_t v[32];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = (uint32_t)ld_agent(p.tile_counts + (size_t)min(r0 + u, MT - 1) * Ep + e);
+          for (int u = 0; u < 32; ++u)
+            v[u] = (uint32_t)ld_agent(p.tile_counts + (size_t)min(r0 + u, MT - 1) * Ep + e);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) tot += (r0 + u < MT) ? v[u] : 0u;
-      }
-      local += (tot + A - 1) & ~(uint32_t)(A - 1);
-    }
-    uint32_t total;
-    uint32_t base = block_excl_scan_u32<kThreads>(local, scan_tmp, &total);
-    for (int e = e0; e < e0 + per && e < Ep; ++e) {
-      uint32_t run = base;
-      for (int r0 = 0; r0 < MT; r0 += 8) {
-        uint32_t v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = (uint32_t)ld_agent(p.tile_counts + (size_t)min(r0 + u, MT - 1) * Ep + e);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          if (r0 + u < MT) {
-            st_agent(p.tile_counts + (size_t)(r0 + u) * Ep + e, (int32_t)run);
-            run += v[u];
+          for (int u = 0; u < 32; ++u) {
+            if (r0 + u < MT) {
+              st_agent(p.tile_counts + (size_t)(r0 + u) * Ep + e, (int32_t)run);
+              run += v[u];
+            }
           }
         }
       }
-      const uint32_t P = (run - base + A - 1) & ~(uint32_t)(A - 1);
-      for (uint32_t blk = base >> sh; blk < (base + P) >> sh; ++blk)
-        if (blk < (uint64_t)p.expert_cap) p.expert_ids[blk] = e;
-      base += P;
+      const uint32_t P = (run + amask) & ~amask;
+      uint32_t tot;
+      const uint32_t off = carry + block_excl_scan_u32<kThreads>(P, scan_tmp, &tot);
+      carry += tot;
+      if (e < Ep) {
+        st_agent(p.expert_off + e, (int32_t)off);
+        for (uint32_t blk = off >> sh; blk < (off + P) >> sh; ++blk)
+          if (blk < (uint64_t)p.expert_cap) p.expert_ids[blk] = e;
+      }
     }
+    const uint32_t total = carry;
     if (tid == 0) *p.npp = (int32_t)total;
     publish(&ctr[kCtrPublished]);
   } else if (p.may_help) {
@@ -413,7 +412,8 @@ __global__ __launch_bounds__(kThreads) void route_large_kernel(LargeParams p) {
         ev[u] = ld_agent(p.ids + i);
         rk[u] = ld_agent(p.ranks + i);
       }
-      for (int e = tid; e < Ep; e += kThreads) base_lds[e] = ld_agent(p.tile_counts + (size_t)rr * Ep + e);
+      for (int e = tid; e < Ep; e += kThreads)
+        base_lds[e] = ld_agent(p.expert_off + e) + ld_agent(p.tile_counts + (size_t)rr * Ep + e);
       __syncthreads();
 #pragma unroll
       for (int u = 0; u < kPer; ++u) {
