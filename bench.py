@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--workload", default="m4", choices=["m4", "m2048", "c3", "c4"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall time spent timing the CPU oracle (0 disables)")
+    ap.add_argument("--secondary-steps", type=int, default=1024,
+                    help="launches timed on the M=2048 workload reported beside the M=4 line (0 disables)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain device copy of known size (HBM counter calibration)")
     return ap.parse_args()
@@ -90,6 +92,8 @@ def cpu_baseline(d, wl, seconds):
     import oracle
 
     threads = os.cpu_count() or 1
+    if os.environ.get("OMP_NUM_THREADS", "").isdigit():
+        threads = max(1, min(threads, int(os.environ["OMP_NUM_THREADS"])))
     n = 0
     t0 = time.perf_counter()
     while True:
@@ -122,23 +126,46 @@ def calibrate_copy():
     print(json.dumps({"calibration": "device copy", "bytes_read": nbytes, "bytes_written": nbytes, "launches": 10}))
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (routing shards by token: "
-              "each GPU would run this same launch on its own tokens)", file=sys.stderr)
-        sys.exit(2)
+def source_digest(kernel):
+    """sha256 over the sources the kernel is compiled from."""
+    import hashlib
+
+    csrc = os.path.join(ROOT, "moe_token_routing_amd", "csrc")
+    main = {"route_small_kernel": "route_small.hip", "route_large_kernel": "route_large.hip"}[kernel]
+    h = hashlib.sha256()
+    for f in [main, "device_common.h", "kernels.h"]:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(kernel, wl_name):
+    """HBM bytes per launch from the committed counter summary for this
+    kernel and workload (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled
+    by what the counter reads for a device copy of known size), or None when
+    there is none or it was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}__{wl_name}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line:
+                key, val = line.split(":", 1)
+                fields[key.strip()] = val.strip()
+    if fields.get("source_sha256") != source_digest(kernel) or "hbm_bytes_per_launch" not in fields:
+        return None
+    return int(float(fields["hbm_bytes_per_launch"]))
+
+
+def measure(wl, steps, warmup):
+    """Times `steps` route+align launches on workload `wl`; returns the seeded
+    input and the result fields."""
     import torch
 
-    if args.calibrate_copy:
-        calibrate_copy()
-        return
     import moe_token_routing_amd as mr
 
-    mr._binding.lib()
     device = "cuda:0"
-    torch.cuda.set_device(0)
-    wl = workload(args.workload)
     per_copy = (wl.E + int(wl.shared)) * wl.H * 2 + wl.M * wl.H * 2
     R = max(8, math.ceil(ROTATE_BYTES / per_copy))
     d, copies = make_copies(wl, R, device)
@@ -165,12 +192,12 @@ def main():
         return g
 
     graphs[R] = capture(R)
-    rem = args.steps % R
+    rem = steps % R
     if rem:
         graphs[rem] = capture(rem)
 
     cur = torch.cuda.current_stream(device)
-    for _ in range(max(1, math.ceil(args.warmup / R))):
+    for _ in range(max(1, math.ceil(warmup / R))):
         graphs[R].replay()
     torch.cuda.synchronize()
 
@@ -178,14 +205,14 @@ def main():
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(cur)
-    for _ in range(args.steps // R):
+    for _ in range(steps // R):
         graphs[R].replay()
     if rem:
         graphs[rem].replay()
     end.record(cur)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / args.steps
+    ms_per_step = total_ms / steps
 
     npps = [int(o["npp"].item()) for o in outs]
     mean_npp = sum(npps) / len(npps)
@@ -207,17 +234,17 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": None}
-    roof["kernel"] = "route_small_kernel" if wl.M <= 16 else "route_large"
+    roof["kernel"] = "route_small_kernel" if wl.M <= 16 else "route_large_kernel"
+    roof["traffic"] = profiled_traffic(roof["kernel"], wl.name)
     roof["bytes_per_launch"] = int(nbytes)
     roof["flops_per_launch"] = int(flops)
 
     result = {
-        "metric": METRIC,
         "value": round(value, 3) if unit == "us/layer" else round(value, 1),
         "unit": unit,
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_per_step, 6),
         "higher_is_better": hib,
         "scaling": "weak",
@@ -229,6 +256,30 @@ def main():
                    "timing": "HIP graph of launches over rotated inputs; HIP events on the launch stream"},
         "roofline": roof,
     }
+    return d, result
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (routing shards by token: "
+              "each GPU would run this same launch on its own tokens)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    import moe_token_routing_amd as mr
+
+    mr._binding.lib()
+    torch.cuda.set_device(0)
+    wl = workload(args.workload)
+    d, result = measure(wl, args.steps, args.warmup)
+    result = {"metric": METRIC, **result}
+    if args.secondary_steps > 0 and args.workload == "m4":
+        _, sec = measure(workload("m2048"), args.secondary_steps, min(args.warmup, 256))
+        result["secondary"] = {kk: sec[kk] for kk in ["value", "unit", "ms_per_step", "steps", "config", "roofline"]}
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(d, wl, args.cpu_seconds)
     print(json.dumps(result), flush=True)
