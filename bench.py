@@ -131,7 +131,7 @@ def source_digest(kernel):
     import hashlib
 
     csrc = os.path.join(ROOT, "moe_token_routing_amd", "csrc")
-    main = {"route_small_kernel": "route_small.hip", "route_large_kernel": "route_large.hip"}[kernel]
+    main = {"route_small_kernel": "route_small.hip", "route_mfma_kernel": "route_mfma.hip"}[kernel]
     h = hashlib.sha256()
     for f in [main, "device_common.h", "kernels.h"]:
         with open(os.path.join(csrc, f), "rb") as fh:
@@ -234,7 +234,7 @@ def measure(wl, steps, warmup):
     else:
         roof = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": None}
-    roof["kernel"] = "route_small_kernel" if wl.M <= 16 else "route_large_kernel"
+    roof["kernel"] = "route_small_kernel" if wl.M <= 16 else "route_mfma_kernel"
     roof["traffic"] = profiled_traffic(roof["kernel"], wl.name)
     roof["bytes_per_launch"] = int(nbytes)
     roof["flops_per_launch"] = int(flops)

@@ -10,6 +10,8 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <string>
 
 #include "kernels.h"
@@ -65,6 +67,7 @@ struct Layout {
   size_t counters = 0, keys = 0, shared = 0;             // small-M route
   size_t tile_ticket = 0, cand = 0, lshared = 0, tcounts = 0, eoff = 0;  // large-M route
   size_t counts = 0, ranks = 0;                          // align / large-M ranks
+  size_t part = 0, c16 = 0;                              // prefill (split-K) route
   size_t total = 0;
 };
 
@@ -90,8 +93,25 @@ Layout layout_for(int64_t M, int64_t E, int64_t k, int64_t sh) {
   const int64_t nch = (n + 64 * W - 1) / (64 * W);
   L.counts = take(o, (size_t)(nch * Ep) * 4);
   L.ranks = take(o, (size_t)n * 4);
+  // split-K partials: for any M' <= M, splits * M' <= max(M, (grid / NE) * min(M, 128))
+  const int64_t Epad = (E + 3) / 4 * 4;
+  const int64_t NT = (M + 127) / 128;
+  int64_t rows = (mr::kMfmaMaxGrid / (NE > 0 ? NE : 1)) * (M < 128 ? M : 128);
+  if (rows < M) rows = M;
+  L.part = take(o, (size_t)(rows * Epad) * 4);
+  L.c16 = take(o, (size_t)(NT * ((Ep + 3) / 4 * 4)) * 4);
   L.total = o;
   return L;
+}
+
+// The prefill path is the split-K kernel unless MR_PREFILL_KERNEL=tiles
+// selects the per-row-tile kernel (kept for comparison).
+bool use_mfma_path() {
+  static const bool v = [] {
+    const char *e = getenv("MR_PREFILL_KERNEL");
+    return !(e && strcmp(e, "tiles") == 0);
+  }();
+  return v;
 }
 
 int launch_result(hipError_t e, const char *fn) {
@@ -179,6 +199,56 @@ int route_impl(const char *fn, const void *x, const void *gate_w, const void *sh
     if (fill > sorted_cap) fill = sorted_cap;
   }
 
+  if (M > mr::kSmallMaxTokens && use_mfma_path()) {
+    const int cap = mr::mfma_capacity(E);
+    if (cap > 0) {
+      mr::MfmaParams q{};
+      q.x = static_cast<const uint16_t *>(x);
+      q.w = static_cast<const uint16_t *>(gate_w);
+      q.ws_row = static_cast<const uint16_t *>(shared_w);
+      q.M = M;
+      q.H = H;
+      q.E = E;
+      q.k = logits_only ? 1 : k;
+      q.S = (int)S;
+      q.Ep = (int)Ep;
+      q.has_shared = sh;
+      q.scale = scale;
+      q.ids = ids;
+      q.wts = wts;
+      q.NE = (E + 127) / 128;
+      q.NT = (M + 127) / 128;
+      q.nstages = (H + 63) / 64;
+      const int grid = cap < mr::kMfmaMaxGrid ? cap : mr::kMfmaMaxGrid;
+      int sk = grid / (q.NE * q.NT);
+      if (sk < 1) sk = 1;
+      if (sk > q.nstages) sk = q.nstages;
+      q.spp = (q.nstages + sk - 1) / sk;
+      q.SK = (q.nstages + q.spp - 1) / q.spp;
+      q.items = q.NE * q.NT * q.SK;
+      q.grid = grid;
+      q.xcd_map = (grid % 8 == 0) ? 1 : 0;
+      q.Epad = (E + 3) / 4 * 4;
+      q.part = reinterpret_cast<float *>(wsb + L.part);
+      q.c16 = reinterpret_cast<uint32_t *>(wsb + L.c16);
+      q.Ep4 = (int)((Ep + 3) / 4 * 4);
+      q.zero16 = reinterpret_cast<const uint4 *>(ctr + mr::kCtrZero16);
+      q.ctr = ctr;
+      int tpb = 1;
+      while (tpb < 128 && (int64_t)tpb * grid < M) tpb *= 2;
+      q.tpb = tpb;
+      q.ngroups = (M + tpb - 1) / tpb;
+      q.do_align = do_align ? 1 : 0;
+      q.A = do_align ? A : 64;
+      q.log2A = do_align ? log2A : 6;
+      q.sorted = sorted;
+      q.expert_ids = expert_ids;
+      q.npp = npp;
+      q.logits_out = logits_out;
+      q.logits_only = logits_only ? 1 : 0;
+      return launch_result(mr::launch_route_mfma(q, s), fn);
+    }
+  }
   if (M > mr::kSmallMaxTokens) {
     mr::LargeParams q{};
     q.x = static_cast<const uint16_t *>(x);

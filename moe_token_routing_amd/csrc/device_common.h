@@ -225,6 +225,59 @@ __device__ __forceinline__ float ld_agent(const float *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Batched coherent loads.  Each reads like a relaxed agent-scope atomic load
+// (sc1: fetched past this XCD's L2, so never a stale copy of data another XCD
+// wrote through), but the eight loads of a batch are all issued before one
+// wait; the compiler waits for every atomic load before issuing the next.
+// The loads and the wait sit in one asm statement, so no result register is
+// read or copied before its data has arrived.
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_coh;
+__device__ __forceinline__ void ld_coherent8(uint32_t (&v)[8], const uint32_t *const (&a)[8]) {
+  asm volatile(
+      "global_load_dword %0, %8, off sc1\n\t"
+      "global_load_dword %1, %9, off sc1\n\t"
+      "global_load_dword %2, %10, off sc1\n\t"
+      "global_load_dword %3, %11, off sc1\n\t"
+      "global_load_dword %4, %12, off sc1\n\t"
+      "global_load_dword %5, %13, off sc1\n\t"
+      "global_load_dword %6, %14, off sc1\n\t"
+      "global_load_dword %7, %15, off sc1\n\t"
+      "s_waitcnt vmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "memory");
+}
+__device__ __forceinline__ void ld_coherent8(unsigned long long (&v)[8], const unsigned long long *const (&a)[8]) {
+  asm volatile(
+      "global_load_dwordx2 %0, %8, off sc1\n\t"
+      "global_load_dwordx2 %1, %9, off sc1\n\t"
+      "global_load_dwordx2 %2, %10, off sc1\n\t"
+      "global_load_dwordx2 %3, %11, off sc1\n\t"
+      "global_load_dwordx2 %4, %12, off sc1\n\t"
+      "global_load_dwordx2 %5, %13, off sc1\n\t"
+      "global_load_dwordx2 %6, %14, off sc1\n\t"
+      "global_load_dwordx2 %7, %15, off sc1\n\t"
+      "s_waitcnt vmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "memory");
+}
+__device__ __forceinline__ void ld_coherent8(u32x4_coh (&v)[8], const u32x4_coh *const (&a)[8]) {
+  asm volatile(
+      "global_load_dwordx4 %0, %8, off sc1\n\t"
+      "global_load_dwordx4 %1, %9, off sc1\n\t"
+      "global_load_dwordx4 %2, %10, off sc1\n\t"
+      "global_load_dwordx4 %3, %11, off sc1\n\t"
+      "global_load_dwordx4 %4, %12, off sc1\n\t"
+      "global_load_dwordx4 %5, %13, off sc1\n\t"
+      "global_load_dwordx4 %6, %14, off sc1\n\t"
+      "global_load_dwordx4 %7, %15, off sc1\n\t"
+      "s_waitcnt vmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "memory");
+}
+
 // Waits until every global store and atomic this wave issued has completed
 // (s_waitcnt with all counters at zero).
 __device__ __forceinline__ void wait_own_stores() { __builtin_amdgcn_s_waitcnt(0); }

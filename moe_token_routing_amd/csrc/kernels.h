@@ -25,6 +25,7 @@ enum CounterIndex : int {
   kCtrWork = 4,       // work-queue head
   kCtrExited = 5,     // block exits
   kCtrError = 6,      // set to 1 if a bounded wait gave up (never expected)
+  kCtrZero16 = 60,    // words 60..63: always zero (a 16-byte zero source)
 };
 constexpr int kTicketLanes = 16;
 constexpr int kTicketLaneStride = 64;  // words (256 bytes)
@@ -106,6 +107,42 @@ struct LargeParams {
   float *logits_out;  // logits_only: the caller's [M, Ep] fp32 buffer
   int logits_only;
 };
+
+// Prefill route (+ align) in one persistent launch: split-K MFMA gate,
+// top-k per token, align; grid barriers between the phases.
+constexpr int kMfmaMaxGrid = 256;  // blocks of one launch (one per CU on MI355X)
+struct MfmaParams {
+  const uint16_t *x;       // [M, H] bf16
+  const uint16_t *w;       // [E, H] bf16
+  const uint16_t *ws_row;  // [H] bf16 or null
+  int M, H, E, k, S, Ep, has_shared;
+  float scale;
+  int32_t *ids;  // [M, S]
+  float *wts;    // [M, S]
+  int NE, NT;    // expert tiles (ceil(E / 128)) and token tiles (ceil(M / 128))
+  int SK;        // K splits
+  int spp;       // 64-wide k stages per split
+  int nstages;   // ceil(H / 64)
+  int items;     // NE * NT * SK
+  int grid;      // blocks (all resident)
+  int xcd_map;   // deal items to XCDs (grid % 8 == 0)
+  int Epad;      // row stride of the partials (E rounded up to 4)
+  float *part;   // [SK, M, Epad] fp32 gate partials
+  uint32_t *c16;        // [NT, Ep4] pairs per (128-token tile, expert); cleared by the kernel
+  int Ep4;              // Ep rounded up to 4 (row stride of c16)
+  const uint4 *zero16;  // 16 zero bytes (stands in for k past H): kCtrZero16 of the counters
+  uint32_t *ctr;        // counter words
+  int tpb, ngroups;     // tokens per top-k group (power of two <= 128) and groups
+  int do_align, A, log2A;
+  int32_t *sorted;
+  int32_t *expert_ids;
+  int32_t *npp;
+  float *logits_out;  // logits_only: the caller's [M, Ep] fp32 buffer
+  int logits_only;
+};
+size_t mfma_lds_bytes();
+int mfma_capacity(int E);
+hipError_t launch_route_mfma(const MfmaParams &p, hipStream_t stream);
 
 int large_tile_tokens(int M, int E);
 int large_grid(const LargeParams &p);

@@ -1,0 +1,650 @@
+// route_mfma.hip -- one-launch router + align for prefill token counts
+// (M > 16): the gate pass is a split-K MFMA tile contraction.
+//
+// Computes what "[AMD] One-launch small-M MoE router ... on gfx950"
+// (sglang), Modifications, and "W4A16 MoE prefill: M-aware moe_align block
+// size" (ROCm vLLM), Purpose, describe: routed logits z = x W^T and the
+// shared logit s = x ws in fp32, r = bf16(z) (nearest even), the k largest r
+// with the lower id winning ties, softmax renormalised over the chosen k,
+// slot k = (E, scale * sigmoid(s)), then moe_align_block_size over the M*S
+// (token, slot) pairs.
+//
+// One persistent launch of `grid` blocks (every block resident: the host
+// sizes the grid from the occupancy API), 256 threads each, in three phases
+// separated by grid barriers:
+//
+// G. Gate.  Work items are (expert tile of 128, token tile of 128, K split).
+//    Operands stream into a 4-stage LDS ring with gfx950's 16-byte global ->
+//    LDS loads (64 k-values per stage: 16 KB of gate rows + 16 KB of
+//    tokens); 16-byte chunks are XOR-swizzled inside each 128-byte row so
+//    the MFMA fragment reads are free of bank conflicts.  The 4 waves form a
+//    2 x 2 grid of 64 x 64 wave tiles, each 2 x 2 v_mfma_f32_32x32x16_bf16
+//    tiles; the LDS reads of one 16-k step are issued before the MFMAs of
+//    the previous one.  Each item writes its fp32 partial tile, transposed
+//    through LDS into whole token rows, with write-through stores.  Before
+//    the barrier each block also dots its own tokens' rows with the shared
+//    gate row (no other block's data is needed for that).  Items are dealt so that the 32
+//    blocks of one XCD share a K split and half the token tiles: the operand
+//    working set of an XCD fits its 4 MB L2.
+// T. Top-k.  Block b owns token groups of tpb tokens; one wave per token sums
+//    the K-split partials in a fixed order (so the logits do not depend on
+//    which block finished first), builds the packed selection keys, takes k
+//    rounds of a wave-wide maximum, then the softmax, the shared slot and
+//    the stores.  Each routed pair also bumps a per-(128-token tile, expert)
+//    counter.
+// A. Align.  Every block turns the tile counters into padded expert offsets
+//    (block scan) and the prefix of earlier tiles, adds the counts of the
+//    earlier tokens of its own tile (read back from topk_ids), and scatters
+//    its pairs: inside an expert, pairs keep ascending flat index.  Blocks
+//    also pad the experts dealt to them and write expert_ids; block 0 writes
+//    npp.  The last block to leave re-zeroes the counters.
+//
+// Workspace: only the counter words must be zero at launch (and are zero
+// again after it); the tile counters are cleared during phase G.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace mr {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTE = 128, kTT = 128;      // experts x tokens per work item
+constexpr int kKS = 64;                  // k-values per pipeline stage
+constexpr int kNS = 4;                   // pipeline stages
+constexpr int kRowBytes = kKS * 2;       // one operand row of a stage
+constexpr int kStageBytes = (kTE + kTT) * kRowBytes;  // 32 KB
+constexpr int kRingBytes = kNS * kStageBytes;          // 128 KB
+constexpr int kTilePitch = kTT + 4;      // fp32 pitch of the transpose tile
+constexpr int kBarrierSpin = 1 << 22;    // bound on a grid-barrier wait
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+// Slot of 16-byte chunk c of LDS row r (rows of 128 bytes).  Rows r and r+1
+// differ in bank half, and the 8 even (odd) rows of any 16 consecutive rows
+// take 8 different slots, so 16 lanes reading one chunk of 16 rows hit 16
+// different bank groups.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+// s_waitcnt on the vector memory counter only (GFX9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt and lgkmcnt at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// 16-byte global -> LDS load: this lane's 16 bytes at `src` land at
+// lds_base + 16 * lane.  Issued through inline assembly so the compiler does
+// not treat every later LDS read as dependent on it (it would wait for all
+// outstanding loads); the pipeline waits for these loads itself with
+// wait_vmcnt before the barrier that publishes a stage.
+__device__ __forceinline__ void load_lds16(const void *src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds_base)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint4 lds16(const uint8_t *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+__device__ __forceinline__ void st_agent2(float *p, float a, float b) {
+  const unsigned long long v = (unsigned long long)__float_as_uint(a) | ((unsigned long long)__float_as_uint(b) << 32);
+  st_agent(reinterpret_cast<unsigned long long *>(p), v);
+}
+
+// Waits until this wave has at most n younger stages of DMA loads in flight
+// (per = loads per stage for this wave).
+template <int PER>
+__device__ __forceinline__ void wait_stages(int n) {
+  if (n >= 2) wait_vmcnt<2 * PER>();
+  else if (n == 1) wait_vmcnt<PER>();
+  else wait_vmcnt<0>();
+}
+
+// Grid barrier over all `grid` blocks, generation `gen` (1, 2, ...): each
+// block takes a ticket on one of up to kTicketLanes first-level counters
+// (256 bytes apart, so arrivals do not serialise on one address); the
+// arrival that completes a lane bumps `top`; everybody waits for `top` to
+// reach gen * lanes.  Data written with st_agent (or agent-scope atomics)
+// before the barrier is visible to coherent loads (ld_agent, ld_coherent8)
+// after it.  The wait is bounded: if it gives up, the
+// error word is set and the block goes on.
+__device__ __forceinline__ void grid_barrier(uint32_t *ctr, uint32_t gen, uint32_t grid) {
+  wait_own_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t nl = grid < (uint32_t)kTicketLanes ? grid : (uint32_t)kTicketLanes;
+    const uint32_t r = blockIdx.x % nl;
+    const uint32_t in_lane = (grid - 1 - r) / nl + 1;
+    uint32_t *lane_ctr = ctr + 64 + (size_t)r * kTicketLaneStride;
+    const uint32_t t = __hip_atomic_fetch_add(lane_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (t == gen * in_lane - 1)
+      __hip_atomic_fetch_add(ctr + kCtrTicket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t target = gen * nl;
+    int it = 0;
+    while (__hip_atomic_load(ctr + kCtrTicket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      if (++it == kBarrierSpin) {
+        __hip_atomic_store(ctr + kCtrError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  __syncthreads();
+}
+
+// ------------------------------------------------------------- phase G ---
+
+__device__ void gate_item(const MfmaParams &p, uint8_t *smem, int et, int tt, int sp) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int M = p.M, H = p.H, E = p.E;
+  const int st0 = sp * p.spp;
+  const int nst = min(p.spp, p.nstages - st0);
+  const uint32_t sbase = (uint32_t)(uintptr_t)smem;
+
+  // DMA sources: this wave fills rows [32w, 32w+32) of both operand tiles, 8
+  // rows per instruction; lane = row (lane / 8), destination slot lane % 8.
+  const int lr = lane >> 3, slot = lane & 7;
+  const uint16_t *arow[4], *brow[4];
+  int acol[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = wave * 32 + i * 8 + lr;
+    arow[i] = p.w + (size_t)min(et * kTE + r, E - 1) * H;
+    brow[i] = p.x + (size_t)min(tt * kTT + r, M - 1) * H;
+    acol[i] = swz(r, slot) * 8;  // element offset of the chunk this lane fetches
+  }
+  auto issue = [&](int st) {  // stage st of this item into ring slot st % kNS
+    const int k0 = (st0 + st) * kKS;
+    const uint32_t dst = sbase + (st % kNS) * kStageBytes;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kk = k0 + acol[i];
+      const void *src = kk < H ? (const void *)(arow[i] + kk) : (const void *)p.zero16;
+      load_lds16(src, __builtin_amdgcn_readfirstlane(dst + (wave * 32 + i * 8) * kRowBytes));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kk = k0 + acol[i];
+      const void *src = kk < H ? (const void *)(brow[i] + kk) : (const void *)p.zero16;
+      load_lds16(src, __builtin_amdgcn_readfirstlane(dst + kTE * kRowBytes + (wave * 32 + i * 8) * kRowBytes));
+    }
+  };
+  constexpr int kPerStage = 8;  // loads per stage per wave
+
+  const int wr = wave >> 1, wc = wave & 1;
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+  int ra[2], rb[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    ra[i] = wr * 64 + i * 32 + (lane & 31);
+    rb[i] = wc * 64 + i * 32 + (lane & 31);
+  }
+
+  // Fragments of one 16-k step: a[2] (gate rows), b[2] (tokens).  Step g
+  // reads stage g / 4, chunk pair g % 4.
+  auto load_frags = [&](int g, uint4 (&a)[2], uint4 (&b)[2]) {
+    const int st = g >> 2, q = g & 3;
+    const uint8_t *As = smem + (st % kNS) * kStageBytes;
+    const uint8_t *Bs = As + kTE * kRowBytes;
+    const int c = q * 2 + (lane >> 5);  // this lane's 8-value chunk of the step
+#pragma unroll
+    for (int i = 0; i < 2; ++i) a[i] = lds16(As + ra[i] * kRowBytes + swz(ra[i], c) * 16);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) b[j] = lds16(Bs + rb[j] * kRowBytes + swz(rb[j], c) * 16);
+  };
+  auto mma = [&](const uint4 (&a)[2], const uint4 (&b)[2]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[i]), as_bf16x8(b[j]), acc[i][j], 0, 0, 0);
+  };
+  // Stage st is usable once this wave has waited for its own loads of it
+  // and every wave has passed the barrier; the barrier also frees the ring
+  // slot of stage st - 1, which takes stage st + kNS - 1.  While st + kNS - 1
+  // < nst the lookahead is full (kNS - 2 younger stages may stay in flight).
+  auto enter_full = [&](int st) {
+    wait_vmcnt<kPerStage * (kNS - 2)>();
+    __syncthreads();
+    issue(st + kNS - 1);
+  };
+  auto enter_tail = [&](int st) {
+    wait_stages<kPerStage>(nst - st - 1);  // every remaining stage is already issued
+    __syncthreads();
+  };
+
+  const int npre = min(nst, kNS - 1);
+  for (int st = 0; st < npre; ++st) issue(st);
+  // Software pipeline over 16-k steps (4 per stage): the LDS reads of step
+  // g + 1 are issued before the MFMAs of step g, so the two overlap.  Stage
+  // boundaries sit between the MFMAs of a stage's third step and its last.
+  uint4 a0[2], b0[2], a1[2], b1[2];
+  if (kNS - 1 < nst) enter_full(0);
+  else enter_tail(0);
+  load_frags(0, a0, b0);
+  auto stage_head = [&](int st) {  // steps 4st .. 4st+2 and the reads of 4st+3
+    const int g = st * 4;
+    load_frags(g + 1, a1, b1);
+    mma(a0, b0);
+    load_frags(g + 2, a0, b0);
+    mma(a1, b1);
+    load_frags(g + 3, a1, b1);
+    mma(a0, b0);
+  };
+  int st = 0;
+  for (; st + kNS < nst; ++st) {  // the next stage enters with full lookahead
+    stage_head(st);
+    enter_full(st + 1);
+    load_frags(st * 4 + 4, a0, b0);
+    mma(a1, b1);
+  }
+  for (; st + 1 < nst; ++st) {  // the next stage enters from the tail
+    stage_head(st);
+    enter_tail(st + 1);
+    load_frags(st * 4 + 4, a0, b0);
+    mma(a1, b1);
+  }
+  stage_head(st);  // last stage
+  mma(a1, b1);
+
+  // partial tile -> LDS [token][expert] -> whole token rows in global memory
+  __syncthreads();  // every wave is done with the ring
+  float *tile = reinterpret_cast<float *>(smem);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        // 32x32 output layout: lane holds column (token) lane % 32 and rows
+        // (experts) 8g + 4 (lane / 32) + {0..3} in elements 4g..4g+3
+        const int t = rb[j];
+        const int e0 = wr * 64 + i * 32 + 8 * g + 4 * (lane >> 5);
+        float4 v;
+        v.x = acc[i][j][4 * g + 0];
+        v.y = acc[i][j][4 * g + 1];
+        v.z = acc[i][j][4 * g + 2];
+        v.w = acc[i][j][4 * g + 3];
+        *reinterpret_cast<float4 *>(tile + t * kTilePitch + e0) = v;
+      }
+  __syncthreads();
+  const int ecol = et * kTE + 2 * lane;
+  for (int rr = wave; rr < kTT; rr += kThreads / kWave) {
+    const int t = tt * kTT + rr;
+    if (t < M && ecol < E) {
+      const float2 v = *reinterpret_cast<const float2 *>(tile + rr * kTilePitch + 2 * lane);
+      st_agent2(p.part + ((size_t)sp * M + t) * p.Epad + ecol, v.x, v.y);
+    }
+  }
+  __syncthreads();  // the tile region is the next item's ring
+}
+
+// Shared-expert logits of tokens [t0, t1) (t1 - t0 <= 128) into sh[]: x rows
+// dotted with the shared gate row in fp32, a fixed summation order.  x and
+// the gate rows are never written by the launch, so plain loads are fine.
+__device__ void shared_logits(const MfmaParams &p, int t0, int t1, float *sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int H = p.H, nch = H >> 3;  // 16-byte chunks per row
+  // each wave takes tokens wave, wave + 4, ...; a lane takes chunks lane, lane + 64, ...
+  for (int m = t0 + wave; m < t1; m += kThreads / kWave) {
+    const uint4 *xr = reinterpret_cast<const uint4 *>(p.x + (size_t)m * H);
+    const uint4 *wr = reinterpret_cast<const uint4 *>(p.ws_row);
+    float acc0 = 0.f, acc1 = 0.f;
+    int c = lane;
+    for (; c + 64 < nch; c += 128) {
+      acc0 = dot8_bf16(xr[c], wr[c], acc0);
+      acc1 = dot8_bf16(xr[c + 64], wr[c + 64], acc1);
+    }
+    if (c < nch) acc0 = dot8_bf16(xr[c], wr[c], acc0);
+    const float v = wave_sum_f32(acc0 + acc1);
+    if (lane == 0) sh[m - t0] = v;
+  }
+}
+
+// ------------------------------------------------------------- phase T ---
+
+template <int NKP>  // pairs of experts per lane: E <= 128 * NKP
+__device__ void topk_group(const MfmaParams &p, int32_t *own, const float *sh, int g) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int M = p.M, E = p.E, k = p.k, S = p.S, SK = p.SK;
+  const int t0 = g * p.tpb, t1 = min(M, t0 + p.tpb);
+  for (int m = t0 + wave; m < t1; m += kThreads / kWave) {
+    // sum the K-split partials in split order (the result does not depend on
+    // timing); lanes past E read a clamped in-bounds pair and are masked below
+    float z[2 * NKP];
+#pragma unroll
+    for (int j = 0; j < 2 * NKP; ++j) z[j] = 0.f;
+    const unsigned long long *row = reinterpret_cast<const unsigned long long *>(p.part + (size_t)m * p.Epad);
+    const size_t split2 = (size_t)M * p.Epad / 2;  // one split, in pairs
+    const int nload = SK * NKP;                     // load index = split * NKP + pair
+    for (int base = 0; base < nload; base += 8) {   // NKP divides 8: pair = u % NKP
+      const unsigned long long *a[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int s = min(base + u, nload - 1) / NKP;
+        const int e = min(2 * lane + 128 * (u % NKP), p.Epad - 2);
+        a[u] = row + s * split2 + (e >> 1);
+      }
+      unsigned long long v[8];
+      ld_coherent8(v, a);
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (base + u < nload) {
+          z[2 * (u % NKP)] += __uint_as_float((uint32_t)v[u]);
+          z[2 * (u % NKP) + 1] += __uint_as_float((uint32_t)(v[u] >> 32));
+        }
+    }
+    const float sl = p.has_shared ? sh[m - t0] : 0.f;
+    if (p.logits_only) {
+#pragma unroll
+      for (int j = 0; j < NKP; ++j) {
+        const int e = 2 * lane + 128 * j;
+        if (e < E) p.logits_out[(size_t)m * p.Ep + e] = z[2 * j];
+        if (e + 1 < E) p.logits_out[(size_t)m * p.Ep + e + 1] = z[2 * j + 1];
+      }
+      if (p.has_shared && lane == 0) p.logits_out[(size_t)m * p.Ep + E] = sl;
+      continue;
+    }
+    uint32_t keys[2 * NKP];
+#pragma unroll
+    for (int j = 0; j < NKP; ++j) {
+      const int e = 2 * lane + 128 * j;
+      keys[2 * j] = e < E ? make_key(z[2 * j], (uint32_t)e) : 0u;
+      keys[2 * j + 1] = e + 1 < E ? make_key(z[2 * j + 1], (uint32_t)(e + 1)) : 0u;
+    }
+    uint32_t mine = 0u;  // lane j < k keeps the j-th chosen key
+    for (int j = 0; j < k; ++j) {
+      uint32_t best = keys[0];
+#pragma unroll
+      for (int i = 1; i < 2 * NKP; ++i) best = max(best, keys[i]);
+      const uint32_t top = wave_max_all_u32(best);
+      mine = (lane == j) ? top : mine;
+#pragma unroll
+      for (int i = 0; i < 2 * NKP; ++i) keys[i] = (keys[i] == top) ? 0u : keys[i];
+    }
+    const float r = key_value(mine);
+    const float r0 = readlane_f32(r, 0);
+    const float ex = (lane < k) ? expf(r - r0) : 0.0f;
+    const float den = wave_sum_f32(ex);
+    int32_t id = (int32_t)key_id(mine);
+    float w = ex / den;
+    if (p.has_shared && lane == k) {
+      id = E;
+      w = p.scale / (1.0f + expf(-sl));
+    }
+    if (lane < S) {
+      st_agent(p.ids + (size_t)m * S + lane, id);
+      p.wts[(size_t)m * S + lane] = w;
+      own[(m - t0) * S + lane] = id;
+      if (p.do_align && lane < k)
+        __hip_atomic_fetch_add(p.c16 + (size_t)(m >> 7) * p.Ep4 + id, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// ------------------------------------------------------------- phase A ---
+
+// Column sums of the tile counters: tot[e] over all tiles and pre[e] over
+// the tiles before `tile`, for every expert.  The table is fetched in 16-byte
+// coherent loads into LDS (`tab`, kTabWords words), a slab of tiles at a time.
+constexpr int kTabWords = 16384;
+__device__ void tile_sums(const MfmaParams &p, int tile, uint32_t *tot, uint32_t *pre, uint32_t *tab) {
+  const int tid = threadIdx.x;
+  const int E = p.E, Ep = p.Ep, Ep4 = p.Ep4, NT = p.NT;
+  for (int e = tid; e < Ep; e += kThreads) {
+    tot[e] = (e < E) ? 0u : (uint32_t)p.M;         // the shared expert takes every token
+    pre[e] = (e < E) ? 0u : (uint32_t)(tile << 7);
+  }
+  const int R = kTabWords / Ep4 > 0 ? kTabWords / Ep4 : 1;
+  for (int t0 = 0; t0 < NT; t0 += R) {
+    const int nr = min(R, NT - t0);
+    const int nchunk = nr * Ep4 / 4;
+    const u32x4_coh *src = reinterpret_cast<const u32x4_coh *>(p.c16 + (size_t)t0 * Ep4);
+    u32x4_coh *dst = reinterpret_cast<u32x4_coh *>(tab);
+    for (int c0 = 0; c0 < nchunk; c0 += kThreads * 8) {
+      const u32x4_coh *a[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) a[u] = src + min(c0 + u * kThreads + tid, nchunk - 1);
+      u32x4_coh v[8];
+      ld_coherent8(v, a);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int c = c0 + u * kThreads + tid;
+        if (c < nchunk) dst[c] = v[u];
+      }
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += kThreads) {
+      uint32_t t = tot[e], q = pre[e];
+      for (int r = 0; r < nr; ++r) {
+        const uint32_t w = tab[r * Ep4 + e];
+        t += w;
+        q += (t0 + r < tile) ? w : 0u;
+      }
+      tot[e] = t;
+      pre[e] = q;
+    }
+    __syncthreads();
+  }
+}
+
+// Padded expert offsets (exclusive scan of ceil(tot / A) * A) into off[];
+// returns npp.
+__device__ uint32_t expert_offsets(const MfmaParams &p, const uint32_t *tot, uint32_t *off, uint32_t *scan_tmp) {
+  const int tid = threadIdx.x;
+  const int Ep = p.Ep;
+  const uint32_t amask = (uint32_t)p.A - 1u;
+  uint32_t carry = 0;
+  for (int e0 = 0; e0 < Ep; e0 += kThreads) {
+    const int e = e0 + tid;
+    const uint32_t c = e < Ep ? tot[e] : 0u;
+    const uint32_t P = (c + amask) & ~amask;
+    uint32_t blk_total;
+    const uint32_t o = carry + block_excl_scan_u32<kThreads>(P, scan_tmp, &blk_total);
+    carry += blk_total;
+    if (e < Ep) off[e] = o;
+  }
+  __syncthreads();
+  return carry;
+}
+
+// Scatter of group g's pairs: sorted[off + pre + (earlier pairs of the same
+// expert in this tile)] = flat index.
+__device__ void align_group(const MfmaParams &p, const uint32_t *off, const uint32_t *pre, uint32_t *offp,
+                            uint32_t *hist, const int32_t *own, int g) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int M = p.M, E = p.E, Ep = p.Ep, S = p.S;
+  const int t0 = g * p.tpb, t1 = min(M, t0 + p.tpb);
+  const int tstart = (t0 >> 7) << 7;
+  for (int e = tid; e < Ep; e += kThreads) {
+    offp[e] = off[e] + pre[e];
+    hist[e] = (e < E) ? 0u : (uint32_t)(t0 - tstart);  // shared: one pair per earlier token
+  }
+  __syncthreads();
+  // routed pairs of the tile's earlier tokens (contiguous in topk_ids)
+  const int nprev = (t0 - tstart) * S;
+  const uint32_t *prev = reinterpret_cast<const uint32_t *>(p.ids + (size_t)tstart * S);
+  for (int i0 = 0; i0 < nprev; i0 += kThreads * 8) {
+    const uint32_t *a[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a[u] = prev + min(i0 + u * kThreads + tid, nprev - 1);
+    uint32_t v[8];
+    ld_coherent8(v, a);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (i0 + u * kThreads + tid < nprev && v[u] < (uint32_t)E) atomicAdd(hist + v[u], 1u);
+  }
+  __syncthreads();
+  // own pairs, token by token (experts of one token are distinct)
+  if (wave == 0) {
+    for (int m = t0; m < t1; ++m) {
+      if (lane < S) {
+        const int32_t e = own[(m - t0) * S + lane];
+        if ((uint32_t)e < (uint32_t)Ep) {
+          const uint32_t dst = offp[e] + hist[e];
+          hist[e] += 1u;
+          p.sorted[dst] = m * S + lane;
+        }
+      }
+      wave_lds_sync();
+    }
+  }
+  __syncthreads();
+}
+
+template <int NKP>
+__global__ __launch_bounds__(kThreads) void route_mfma_kernel(MfmaParams p) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  __shared__ uint32_t scan_tmp[kThreads / kWave + 1];
+  __shared__ uint32_t flag;
+  __shared__ float sh[128];  // shared-expert logits of the current token group
+  const int b = blockIdx.x;
+  const uint32_t grid = gridDim.x;
+
+  // ---- G: gate partials -------------------------------------------------
+  // the tile counters start from zero in every launch (the workspace layout
+  // moves with M, so nothing else may be assumed about this region)
+  if (p.do_align && !p.logits_only)
+    for (int i = b * kThreads + threadIdx.x; i < p.NT * p.Ep4; i += (int)grid * kThreads) st_agent(p.c16 + i, 0u);
+  const int per_xcd = p.xcd_map ? (int)grid / 8 : 0;
+  for (int it = 0;; ++it) {
+    const int L = it * (int)grid + (p.xcd_map ? (b % 8) * per_xcd + b / 8 : b);
+    if (L >= p.items) break;
+    const int et = L % p.NE, tt = (L / p.NE) % p.NT, sp = L / (p.NE * p.NT);
+    gate_item(p, smem, et, tt, sp);
+  }
+  // the shared logits of this block's first token group need no other block:
+  // computing them here overlaps the wait at the barrier
+  if (p.has_shared && b < p.ngroups) shared_logits(p, b * p.tpb, min(p.M, b * p.tpb + p.tpb), sh);
+  grid_barrier(p.ctr, 1, grid);
+
+  // ---- T: logits, top-k, weights ----------------------------------------
+  // LDS from here on: [0, 32K) this block's ids; then per-expert arrays; the
+  // tile-counter slab from 64K
+  int32_t *own = reinterpret_cast<int32_t *>(smem);
+  const bool align = p.do_align && !p.logits_only;
+  uint32_t *tot = reinterpret_cast<uint32_t *>(smem + 32768);
+  uint32_t *pre = tot + kMaxRouteExperts + 4;
+  uint32_t *off = pre + kMaxRouteExperts + 4;
+  uint32_t *offp = off + kMaxRouteExperts + 4;
+  uint32_t *hist = offp + kMaxRouteExperts + 4;
+  uint32_t *tab = reinterpret_cast<uint32_t *>(smem + 65536);
+  // A block owns more than one group only for M > 128 * grid; then `own`
+  // holds one group at a time and is reloaded in phase A.
+  const bool multi = (int)grid < p.ngroups;
+  for (int g = b; g < p.ngroups; g += grid) {
+    if (g != b && p.has_shared) {
+      __syncthreads();
+      shared_logits(p, g * p.tpb, min(p.M, g * p.tpb + p.tpb), sh);
+      __syncthreads();
+    }
+    topk_group<NKP>(p, own, sh, g);
+  }
+  if (align) {
+    grid_barrier(p.ctr, 2, grid);
+    if (!multi) {
+      tile_sums(p, b < p.ngroups ? (b * p.tpb) >> 7 : 0, tot, pre, tab);
+      const uint32_t npp = expert_offsets(p, tot, off, scan_tmp);
+      if (b < p.ngroups) align_group(p, off, pre, offp, hist, own, b);
+      if (b == 0 && threadIdx.x == 0) *p.npp = (int32_t)npp;
+    } else {
+      uint32_t npp = 0;
+      for (int g = b; g < p.ngroups; g += grid) {
+        tile_sums(p, (g * p.tpb) >> 7, tot, pre, tab);
+        npp = expert_offsets(p, tot, off, scan_tmp);
+        const int t0 = g * p.tpb, t1 = min(p.M, t0 + p.tpb);
+        for (int i = threadIdx.x; i < (t1 - t0) * p.S; i += kThreads) own[i] = ld_agent(p.ids + (size_t)t0 * p.S + i);
+        __syncthreads();
+        align_group(p, off, pre, offp, hist, own, g);
+      }
+      if (b == 0 && threadIdx.x == 0) *p.npp = (int32_t)npp;
+    }
+    // padding and expert_ids of the experts dealt to this block
+    for (int e = b; e < p.Ep; e += grid) {
+      const uint32_t c = tot[e], o = off[e];
+      const uint32_t P = (c + (uint32_t)p.A - 1u) & ~((uint32_t)p.A - 1u);
+      for (uint32_t i = c + threadIdx.x; i < P; i += kThreads) p.sorted[o + i] = p.M * p.S;
+      for (uint32_t blk = (o >> p.log2A) + threadIdx.x; blk < ((o + P) >> p.log2A); blk += kThreads)
+        p.expert_ids[blk] = e;
+    }
+  }
+
+  // ---- exit: the last block re-zeroes the counters ----------------------
+  const uint32_t gens = align ? 3u : 2u;
+  wait_own_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t nl = grid < (uint32_t)kTicketLanes ? grid : (uint32_t)kTicketLanes;
+    const uint32_t r = b % nl;
+    const uint32_t in_lane = (grid - 1 - r) / nl + 1;
+    uint32_t last = 0;
+    const uint32_t t = __hip_atomic_fetch_add(p.ctr + 64 + (size_t)r * kTicketLaneStride, 1u, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    if (t == gens * in_lane - 1) {
+      const uint32_t u = __hip_atomic_fetch_add(p.ctr + kCtrTicket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last = (u == gens * nl - 1) ? 1u : 0u;
+    }
+    flag = last;
+  }
+  __syncthreads();
+  if (flag) {
+    if (threadIdx.x < kTicketLanes) reset_counter(p.ctr + 64 + (size_t)threadIdx.x * kTicketLaneStride);
+    if (threadIdx.x == 0) reset_counter(p.ctr + kCtrTicket);
+  }
+}
+
+template <int NKP>
+const void *kernel_ptr() {
+  return reinterpret_cast<const void *>(&route_mfma_kernel<NKP>);
+}
+
+}  // namespace
+
+size_t mfma_lds_bytes() { return (size_t)kRingBytes; }
+
+int mfma_nkp(int E) {
+  const int need = (E + 127) / 128;
+  return need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
+}
+
+int mfma_capacity(int E) {
+  static int cached[4][64];  // [nkp index][device]
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  const int nkp = mfma_nkp(E);
+  const int ki = nkp == 1 ? 0 : nkp == 2 ? 1 : nkp == 4 ? 2 : 3;
+  if (cached[ki][dev] > 0) return cached[ki][dev];
+  const void *fn = ki == 0 ? kernel_ptr<1>() : ki == 1 ? kernel_ptr<2>() : ki == 2 ? kernel_ptr<4>() : kernel_ptr<8>();
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)mfma_lds_bytes()) != hipSuccess)
+    return 0;
+  int ncu = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, mfma_lds_bytes()) != hipSuccess) return 0;
+  const int cap = ncu * per_cu;
+  cached[ki][dev] = cap;
+  return cap;
+}
+
+hipError_t launch_route_mfma(const MfmaParams &p, hipStream_t stream) {
+  const size_t lds = mfma_lds_bytes();
+  switch (mfma_nkp(p.E)) {
+    case 1: route_mfma_kernel<1><<<p.grid, kThreads, lds, stream>>>(p); break;
+    case 2: route_mfma_kernel<2><<<p.grid, kThreads, lds, stream>>>(p); break;
+    case 4: route_mfma_kernel<4><<<p.grid, kThreads, lds, stream>>>(p); break;
+    default: route_mfma_kernel<8><<<p.grid, kThreads, lds, stream>>>(p); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mr
