@@ -278,6 +278,33 @@ __device__ __forceinline__ void ld_coherent8(u32x4_coh (&v)[8], const u32x4_coh 
       : "memory");
 }
 
+// Sixteen 16-byte coherent loads, one wait (see ld_coherent8).
+__device__ __forceinline__ void ld_coherent16(u32x4_coh (&v)[16], const u32x4_coh *const (&a)[16]) {
+  asm volatile(
+      "global_load_dwordx4 %0, %16, off sc1\n\t"
+      "global_load_dwordx4 %1, %17, off sc1\n\t"
+      "global_load_dwordx4 %2, %18, off sc1\n\t"
+      "global_load_dwordx4 %3, %19, off sc1\n\t"
+      "global_load_dwordx4 %4, %20, off sc1\n\t"
+      "global_load_dwordx4 %5, %21, off sc1\n\t"
+      "global_load_dwordx4 %6, %22, off sc1\n\t"
+      "global_load_dwordx4 %7, %23, off sc1\n\t"
+      "global_load_dwordx4 %8, %24, off sc1\n\t"
+      "global_load_dwordx4 %9, %25, off sc1\n\t"
+      "global_load_dwordx4 %10, %26, off sc1\n\t"
+      "global_load_dwordx4 %11, %27, off sc1\n\t"
+      "global_load_dwordx4 %12, %28, off sc1\n\t"
+      "global_load_dwordx4 %13, %29, off sc1\n\t"
+      "global_load_dwordx4 %14, %30, off sc1\n\t"
+      "global_load_dwordx4 %15, %31, off sc1\n\t"
+      "s_waitcnt vmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]),
+        "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]), "=&v"(v[12]), "=&v"(v[13]), "=&v"(v[14]), "=&v"(v[15])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
+        "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12]), "v"(a[13]), "v"(a[14]), "v"(a[15])
+      : "memory");
+}
+
 // Waits until every global store and atomic this wave issued has completed
 // (s_waitcnt with all counters at zero).
 __device__ __forceinline__ void wait_own_stores() { __builtin_amdgcn_s_waitcnt(0); }

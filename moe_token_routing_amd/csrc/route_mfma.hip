@@ -139,7 +139,12 @@ __device__ __forceinline__ void grid_barrier(uint32_t *ctr, uint32_t gen, uint32
 
 // ------------------------------------------------------------- phase G ---
 
-__device__ void gate_item(const MfmaParams &p, uint8_t *smem, int et, int tt, int sp) {
+__device__ void shared_logits(const MfmaParams &p, int t0, int t1, float *sh);
+
+// sh_out: when not null, the shared logits of tokens [sh_t0, sh_t1) are
+// computed into it while the item's first stages are in flight.
+__device__ void gate_item(const MfmaParams &p, uint8_t *smem, int et, int tt, int sp, float *sh_out, int sh_t0,
+                          int sh_t1) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int M = p.M, H = p.H, E = p.E;
   const int st0 = sp * p.spp;
@@ -226,6 +231,7 @@ __device__ void gate_item(const MfmaParams &p, uint8_t *smem, int et, int tt, in
 
   const int npre = min(nst, kNS - 1);
   for (int st = 0; st < npre; ++st) issue(st);
+  if (sh_out) shared_logits(p, sh_t0, sh_t1, sh_out);  // registers only; overlaps the loads
   // Software pipeline over 16-k steps (4 per stage): the LDS reads of step
   // g + 1 are issued before the MFMAs of step g, so the two overlap.  Stage
   // boundaries sit between the MFMAs of a stage's third step and its last.
@@ -293,38 +299,97 @@ __device__ void gate_item(const MfmaParams &p, uint8_t *smem, int et, int tt, in
 // Shared-expert logits of tokens [t0, t1) (t1 - t0 <= 128) into sh[]: x rows
 // dotted with the shared gate row in fp32, a fixed summation order.  x and
 // the gate rows are never written by the launch, so plain loads are fine.
+// Each wave takes tokens wave, wave + 4, ...; a lane takes the 16-byte
+// chunks lane + 64 u of the row, 8 chunks per batch, all loads of a batch
+// issued before its arithmetic.
 __device__ void shared_logits(const MfmaParams &p, int t0, int t1, float *sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int H = p.H, nch = H >> 3;  // 16-byte chunks per row
-  // each wave takes tokens wave, wave + 4, ...; a lane takes chunks lane, lane + 64, ...
+  const uint4 *wrow = reinterpret_cast<const uint4 *>(p.ws_row);
   for (int m = t0 + wave; m < t1; m += kThreads / kWave) {
     const uint4 *xr = reinterpret_cast<const uint4 *>(p.x + (size_t)m * H);
-    const uint4 *wr = reinterpret_cast<const uint4 *>(p.ws_row);
-    float acc0 = 0.f, acc1 = 0.f;
-    int c = lane;
-    for (; c + 64 < nch; c += 128) {
-      acc0 = dot8_bf16(xr[c], wr[c], acc0);
-      acc1 = dot8_bf16(xr[c + 64], wr[c + 64], acc1);
+    float acc[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] = 0.f;
+    for (int c0 = 0; c0 < nch; c0 += 64 * 8) {
+      uint4 xv[8], wv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int c = min(c0 + 64 * u + lane, nch - 1);
+        xv[u] = xr[c];
+        wv[u] = wrow[c];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (c0 + 64 * u + lane < nch) acc[u] = dot8_bf16(xv[u], wv[u], acc[u]);
     }
-    if (c < nch) acc0 = dot8_bf16(xr[c], wr[c], acc0);
-    const float v = wave_sum_f32(acc0 + acc1);
+    const float v = wave_sum_f32(((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7])));
     if (lane == 0) sh[m - t0] = v;
   }
 }
 
 // ------------------------------------------------------------- phase T ---
 
+constexpr int kWaveStage = 24576;  // LDS bytes per wave for staging partial rows (4 waves from 32 KB)
+
 template <int NKP>  // pairs of experts per lane: E <= 128 * NKP
-__device__ void topk_group(const MfmaParams &p, int32_t *own, const float *sh, int g) {
+__device__ void topk_group(const MfmaParams &p, int32_t *own, const float *sh, uint8_t *stage, int g) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int M = p.M, E = p.E, k = p.k, S = p.S, SK = p.SK;
+  const int M = p.M, E = p.E, k = p.k, S = p.S, SK = p.SK, Epad = p.Epad;
   const int t0 = g * p.tpb, t1 = min(M, t0 + p.tpb);
-  for (int m = t0 + wave; m < t1; m += kThreads / kWave) {
+  // This wave's tokens are t0 + wave + 4i, i < ntw.  When their partial rows
+  // (ntw * SK rows of Epad floats) fit the wave's LDS slice, they are staged
+  // there with one batch of coherent 16-byte loads per 16 KB; otherwise
+  // each token loads its own pairs.
+  const int ntw = (t1 - t0 > wave) ? (t1 - t0 - wave + 3) / 4 : 0;
+  const int rowc = Epad >> 2;  // 16-byte chunks per partial row
+  const int nch = ntw * SK * rowc;
+  float *wst = reinterpret_cast<float *>(stage + wave * kWaveStage);
+  const bool staged = nch * 16 <= kWaveStage;
+  if (staged && nch > 0) {
+    const float inv_rowc = 1.0f / (float)rowc, inv_sk = 1.0f / (float)SK;
+    for (int c0 = 0; c0 < nch; c0 += 64 * 16) {
+      const u32x4_coh *a[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int c = min(c0 + 64 * u + lane, nch - 1);
+        // row = c / rowc, token i = row / SK, split = row % SK (exact: the
+        // quotients' fractional parts stay far from integers at these sizes)
+        const int row = (int)(((float)c + 0.5f) * inv_rowc);
+        const int i = (int)(((float)row + 0.5f) * inv_sk);
+        const int sp = row - i * SK, q = c - row * rowc;
+        const int m = t0 + wave + 4 * i;
+        a[u] = reinterpret_cast<const u32x4_coh *>(p.part + ((size_t)sp * M + m) * Epad) + q;
+      }
+      u32x4_coh v[16];
+      ld_coherent16(v, a);
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int c = c0 + 64 * u + lane;
+        if (c < nch) reinterpret_cast<u32x4_coh *>(wst)[c] = v[u];
+      }
+    }
+    wave_lds_sync();
+  }
+  for (int ti = 0; ti < ntw; ++ti) {
+    const int m = t0 + wave + 4 * ti;
     // sum the K-split partials in split order (the result does not depend on
     // timing); lanes past E read a clamped in-bounds pair and are masked below
     float z[2 * NKP];
 #pragma unroll
     for (int j = 0; j < 2 * NKP; ++j) z[j] = 0.f;
+    if (staged) {
+      const float *rows = wst + (size_t)ti * SK * Epad;
+      for (int sp = 0; sp < SK; ++sp) {
+#pragma unroll
+        for (int j = 0; j < NKP; ++j) {
+          const int e = min(2 * lane + 128 * j, Epad - 2);
+          const float2 v = *reinterpret_cast<const float2 *>(rows + sp * Epad + e);
+          z[2 * j] += v.x;
+          z[2 * j + 1] += v.y;
+        }
+      }
+    } else {
     const unsigned long long *row = reinterpret_cast<const unsigned long long *>(p.part + (size_t)m * p.Epad);
     const size_t split2 = (size_t)M * p.Epad / 2;  // one split, in pairs
     const int nload = SK * NKP;                     // load index = split * NKP + pair
@@ -344,6 +409,7 @@ __device__ void topk_group(const MfmaParams &p, int32_t *own, const float *sh, i
           z[2 * (u % NKP)] += __uint_as_float((uint32_t)v[u]);
           z[2 * (u % NKP) + 1] += __uint_as_float((uint32_t)(v[u] >> 32));
         }
+    }
     }
     const float sl = p.has_shared ? sh[m - t0] : 0.f;
     if (p.logits_only) {
@@ -412,14 +478,14 @@ __device__ void tile_sums(const MfmaParams &p, int tile, uint32_t *tot, uint32_t
     const int nchunk = nr * Ep4 / 4;
     const u32x4_coh *src = reinterpret_cast<const u32x4_coh *>(p.c16 + (size_t)t0 * Ep4);
     u32x4_coh *dst = reinterpret_cast<u32x4_coh *>(tab);
-    for (int c0 = 0; c0 < nchunk; c0 += kThreads * 8) {
-      const u32x4_coh *a[8];
+    for (int c0 = 0; c0 < nchunk; c0 += kThreads * 16) {
+      const u32x4_coh *a[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) a[u] = src + min(c0 + u * kThreads + tid, nchunk - 1);
-      u32x4_coh v[8];
-      ld_coherent8(v, a);
+      for (int u = 0; u < 16; ++u) a[u] = src + min(c0 + u * kThreads + tid, nchunk - 1);
+      u32x4_coh v[16];
+      ld_coherent16(v, a);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < 16; ++u) {
         const int c = c0 + u * kThreads + tid;
         if (c < nchunk) dst[c] = v[u];
       }
@@ -518,15 +584,18 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(MfmaParams p) {
   if (p.do_align && !p.logits_only)
     for (int i = b * kThreads + threadIdx.x; i < p.NT * p.Ep4; i += (int)grid * kThreads) st_agent(p.c16 + i, 0u);
   const int per_xcd = p.xcd_map ? (int)grid / 8 : 0;
+  // the shared logits of this block's first token group need no other
+  // block's data: they are computed during the first item's load latency
+  const int sh_t0 = b * p.tpb, sh_t1 = min(p.M, sh_t0 + p.tpb);
+  bool sh_pending = p.has_shared && b < p.ngroups;
   for (int it = 0;; ++it) {
     const int L = it * (int)grid + (p.xcd_map ? (b % 8) * per_xcd + b / 8 : b);
     if (L >= p.items) break;
     const int et = L % p.NE, tt = (L / p.NE) % p.NT, sp = L / (p.NE * p.NT);
-    gate_item(p, smem, et, tt, sp);
+    gate_item(p, smem, et, tt, sp, sh_pending ? sh : nullptr, sh_t0, sh_t1);
+    sh_pending = false;
   }
-  // the shared logits of this block's first token group need no other block:
-  // computing them here overlaps the wait at the barrier
-  if (p.has_shared && b < p.ngroups) shared_logits(p, b * p.tpb, min(p.M, b * p.tpb + p.tpb), sh);
+  if (sh_pending) shared_logits(p, sh_t0, sh_t1, sh);
   grid_barrier(p.ctr, 1, grid);
 
   // ---- T: logits, top-k, weights ----------------------------------------
@@ -549,7 +618,7 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(MfmaParams p) {
       shared_logits(p, g * p.tpb, min(p.M, g * p.tpb + p.tpb), sh);
       __syncthreads();
     }
-    topk_group<NKP>(p, own, sh, g);
+    topk_group<NKP>(p, own, sh, smem + 32768, g);
   }
   if (align) {
     grid_barrier(p.ctr, 2, grid);
