@@ -102,6 +102,51 @@ __device__ __forceinline__ uint32_t wave_max_all_u32(uint32_t v) {
   return max(b[0], b[1]);
 }
 
+// Sorts N (a power of two) keys held in registers into descending order
+// with a bitonic network (all indices compile-time: no register indexing).
+template <int N>
+__device__ __forceinline__ void sort_desc_u32(uint32_t (&a)[N]) {
+#pragma unroll
+  for (int k = 2; k <= N; k <<= 1)
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1)
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const int l = i ^ j;
+        if (l > i) {
+          const uint32_t x = a[i], y = a[l];
+          if ((i & k) == 0) {
+            a[i] = max(x, y);
+            a[l] = min(x, y);
+          } else {
+            a[i] = min(x, y);
+            a[l] = max(x, y);
+          }
+        }
+      }
+}
+
+// The k largest of the wave's keys (each lane's N keys sorted descending,
+// every key unique or zero): round j takes the wave-wide maximum of the
+// lanes' heads, lane j keeps it, and the lane that held it drops its head.
+// Returns lane j's key for j < k (0 elsewhere).  Every lane must be active.
+template <int N>
+__device__ __forceinline__ uint32_t topk_sorted_u32(uint32_t (&a)[N], int k, int lane) {
+  uint32_t mine = 0u;
+  for (int j = 0; j < k; ++j) {
+    const uint32_t top = wave_max_all_u32(a[0]);
+    mine = (lane == j) ? top : mine;
+    // keep = all ones except in the lane whose head was taken; there the
+    // list shifts up by one (a sorted list never grows along the shift, so
+    // the minimum picks the shifted value exactly where keep is 0)
+    const uint32_t keep = (uint32_t)(a[0] != top) * 0xFFFFFFFFu;
+#pragma unroll
+    for (int i = 0; i + 1 < N; ++i) a[i] = min(a[i], a[i + 1] | keep);
+    a[N - 1] &= keep;
+  }
+  return mine;
+}
+
 // Sum over the 64 lanes (fixed butterfly order, so deterministic); every
 // lane must be active.  Returns a wave-uniform value.
 __device__ __forceinline__ float wave_sum_f32(float v) {

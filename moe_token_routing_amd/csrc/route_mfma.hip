@@ -429,16 +429,8 @@ __device__ void topk_group(const MfmaParams &p, int32_t *own, const float *sh, u
       keys[2 * j] = e < E ? make_key(z[2 * j], (uint32_t)e) : 0u;
       keys[2 * j + 1] = e + 1 < E ? make_key(z[2 * j + 1], (uint32_t)(e + 1)) : 0u;
     }
-    uint32_t mine = 0u;  // lane j < k keeps the j-th chosen key
-    for (int j = 0; j < k; ++j) {
-      uint32_t best = keys[0];
-#pragma unroll
-      for (int i = 1; i < 2 * NKP; ++i) best = max(best, keys[i]);
-      const uint32_t top = wave_max_all_u32(best);
-      mine = (lane == j) ? top : mine;
-#pragma unroll
-      for (int i = 0; i < 2 * NKP; ++i) keys[i] = (keys[i] == top) ? 0u : keys[i];
-    }
+    sort_desc_u32(keys);
+    const uint32_t mine = topk_sorted_u32(keys, k, lane);  // lane j < k: the j-th chosen key
     const float r = key_value(mine);
     const float r0 = readlane_f32(r, 0);
     const float ex = (lane < k) ? expf(r - r0) : 0.0f;

@@ -95,13 +95,8 @@ __device__ void route_tail_rows(const SmallParams &p, int32_t *lds_ids) {
       else keys[i] = 0u;
     }
     if (p.has_shared && lane == 0) st_agent(p.shared_logit + m, 0ull);
-    uint32_t mine = 0u;  // lane j < k keeps the j-th chosen key
-    for (int j = 0; j < k; ++j) {
-      const uint32_t top = wave_max_all_u32(max_of(keys));
-      mine = (lane == j) ? top : mine;
-#pragma unroll
-      for (int i = 0; i < NK; ++i) keys[i] = (keys[i] == top) ? 0u : keys[i];
-    }
+    sort_desc_u32(keys);
+    const uint32_t mine = topk_sorted_u32(keys, k, lane);  // lane j < k: the j-th chosen key
     const float r = key_value(mine);
     const float r0 = readlane_f32(r, 0);
     const float ex = (lane < k) ? expf(r - r0) : 0.0f;
