@@ -99,7 +99,7 @@ Layout layout_for(int64_t M, int64_t E, int64_t k, int64_t sh) {
   int64_t rows = (mr::kMfmaMaxGrid / (NE > 0 ? NE : 1)) * (M < 128 ? M : 128);
   if (rows < M) rows = M;
   L.part = take(o, (size_t)(rows * Epad) * 4);
-  L.c16 = take(o, (size_t)(NT * ((Ep + 3) / 4 * 4)) * 4);
+  L.c16 = take(o, (size_t)(NT * ((Ep + 15) / 16 * 4)) * 4);
   L.total = o;
   return L;
 }
@@ -231,7 +231,7 @@ int route_impl(const char *fn, const void *x, const void *gate_w, const void *sh
       q.Epad = (E + 3) / 4 * 4;
       q.part = reinterpret_cast<float *>(wsb + L.part);
       q.c16 = reinterpret_cast<uint32_t *>(wsb + L.c16);
-      q.Ep4 = (int)((Ep + 3) / 4 * 4);
+      q.c16_row = (int)((Ep + 15) / 16 * 4);
       q.zero16 = reinterpret_cast<const uint4 *>(ctr + mr::kCtrZero16);
       q.ctr = ctr;
       int tpb = 1;

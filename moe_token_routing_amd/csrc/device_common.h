@@ -147,6 +147,30 @@ __device__ __forceinline__ uint32_t topk_sorted_u32(uint32_t (&a)[N], int k, int
   return mine;
 }
 
+// topk_sorted_u32 for two independent lists at once: the two dependency
+// chains interleave, so two selections take little longer than one.
+template <int N>
+__device__ __forceinline__ void topk_sorted2_u32(uint32_t (&a)[N], uint32_t (&b)[N], int k, int lane,
+                                                 uint32_t &mine_a, uint32_t &mine_b) {
+  mine_a = 0u;
+  mine_b = 0u;
+  for (int j = 0; j < k; ++j) {
+    const uint32_t ta = wave_max_all_u32(a[0]);
+    const uint32_t tb = wave_max_all_u32(b[0]);
+    mine_a = (lane == j) ? ta : mine_a;
+    mine_b = (lane == j) ? tb : mine_b;
+    const uint32_t keep_a = (uint32_t)(a[0] != ta) * 0xFFFFFFFFu;
+    const uint32_t keep_b = (uint32_t)(b[0] != tb) * 0xFFFFFFFFu;
+#pragma unroll
+    for (int i = 0; i + 1 < N; ++i) {
+      a[i] = min(a[i], a[i + 1] | keep_a);
+      b[i] = min(b[i], b[i + 1] | keep_b);
+    }
+    a[N - 1] &= keep_a;
+    b[N - 1] &= keep_b;
+  }
+}
+
 // Sum over the 64 lanes (fixed butterfly order, so deterministic); every
 // lane must be active.  Returns a wave-uniform value.
 __device__ __forceinline__ float wave_sum_f32(float v) {

@@ -40,7 +40,8 @@
 //    npp.  The last block to leave re-zeroes the counters.
 //
 // Workspace: only the counter words must be zero at launch (and are zero
-// again after it); the tile counters are cleared during phase G.
+// again after it); the tile counters (one byte per expert and 128-token tile)
+// are cleared during phase G.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -286,11 +287,18 @@ __device__ void gate_item(const MfmaParams &p, uint8_t *smem, int et, int tt, in
       }
   __syncthreads();
   const int ecol = et * kTE + 2 * lane;
-  for (int rr = wave; rr < kTT; rr += kThreads / kWave) {
-    const int t = tt * kTT + rr;
-    if (t < M && ecol < E) {
-      const float2 v = *reinterpret_cast<const float2 *>(tile + rr * kTilePitch + 2 * lane);
-      st_agent2(p.part + ((size_t)sp * M + t) * p.Epad + ecol, v.x, v.y);
+  // each wave writes rows wave, wave + 4, ...: 8 rows' LDS reads are issued
+  // before their 8 stores
+  for (int r0 = wave; r0 < kTT; r0 += 8 * (kThreads / kWave)) {
+    float2 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float2 *>(tile + (r0 + 4 * u) * kTilePitch + 2 * lane);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int t = tt * kTT + r0 + 4 * u;
+      if (t < M && ecol < E)
+        st_agent(reinterpret_cast<unsigned long long *>(p.part + ((size_t)sp * M + t) * p.Epad + ecol),
+                 (unsigned long long)__float_as_uint(v[u].x) | ((unsigned long long)__float_as_uint(v[u].y) << 32));
     }
   }
   __syncthreads();  // the tile region is the next item's ring
@@ -337,32 +345,32 @@ __device__ void topk_group(const MfmaParams &p, int32_t *own, const float *sh, u
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int M = p.M, E = p.E, k = p.k, S = p.S, SK = p.SK, Epad = p.Epad;
   const int t0 = g * p.tpb, t1 = min(M, t0 + p.tpb);
-  // This wave's tokens are t0 + wave + 4i, i < ntw.  When their partial rows
-  // (ntw * SK rows of Epad floats) fit the wave's LDS slice, they are staged
-  // there with one batch of coherent 16-byte loads per 16 KB; otherwise
-  // each token loads its own pairs.
+  // This wave's tokens are t0 + wave + 4i, i < ntw, taken two at a time.  A
+  // pair's partial rows are staged in the wave's LDS slice, sc splits per
+  // batch of 16-byte loads, and summed in split order (the logits do not
+  // depend on timing).  Lanes past E read clamped in-bounds pairs and are
+  // masked when the keys are built.
   const int ntw = (t1 - t0 > wave) ? (t1 - t0 - wave + 3) / 4 : 0;
   const int rowc = Epad >> 2;  // 16-byte chunks per partial row
-  const int nch = ntw * SK * rowc;
   float *wst = reinterpret_cast<float *>(stage + wave * kWaveStage);
-  const bool staged = nch * 16 <= kWaveStage;
-  if (staged && nch > 0) {
-    const float inv_rowc = 1.0f / (float)rowc, inv_sk = 1.0f / (float)SK;
+  const int sc = max(1, min(SK, kWaveStage / (2 * Epad * 4)));
+  // rows of tokens ma, mb for splits [s0, s0 + n) -> wst[tok][split][Epad]
+  auto stage_rows = [&](int ma, int mb, int s0, int n) {
+    const int nch = 2 * n * rowc;
+    const float inv_rowc = 1.0f / (float)rowc;
     for (int c0 = 0; c0 < nch; c0 += 64 * 16) {
       const u32x4_coh *a[16];
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
         const int c = min(c0 + 64 * u + lane, nch - 1);
-        // row = c / rowc, token i = row / SK, split = row % SK (exact: the
-        // quotients' fractional parts stay far from integers at these sizes)
+        // row = c / rowc (exact: the fractional part stays far from an integer)
         const int row = (int)(((float)c + 0.5f) * inv_rowc);
-        const int i = (int)(((float)row + 0.5f) * inv_sk);
-        const int sp = row - i * SK, q = c - row * rowc;
-        const int m = t0 + wave + 4 * i;
-        a[u] = reinterpret_cast<const u32x4_coh *>(p.part + ((size_t)sp * M + m) * Epad) + q;
+        const int q = c - row * rowc, tok = row >= n ? 1 : 0, sp = s0 + row - tok * n;
+        a[u] = reinterpret_cast<const u32x4_coh *>(p.part + ((size_t)sp * M + (tok ? mb : ma)) * Epad) + q;
       }
       u32x4_coh v[16];
-      ld_coherent16(v, a);
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = *a[u];
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
         const int c = c0 + 64 * u + lane;
@@ -370,59 +378,30 @@ __device__ void topk_group(const MfmaParams &p, int32_t *own, const float *sh, u
       }
     }
     wave_lds_sync();
-  }
-  for (int ti = 0; ti < ntw; ++ti) {
-    const int m = t0 + wave + 4 * ti;
-    // sum the K-split partials in split order (the result does not depend on
-    // timing); lanes past E read a clamped in-bounds pair and are masked below
-    float z[2 * NKP];
+  };
+  auto add_rows = [&](int tok, int n, float (&z)[2 * NKP]) {
+    const float *rows = wst + (size_t)tok * n * Epad;
+    for (int u0 = 0; u0 < n; u0 += 4) {  // 4 splits' reads issued before their sums
+      float2 v[4][NKP];
 #pragma unroll
-    for (int j = 0; j < 2 * NKP; ++j) z[j] = 0.f;
-    if (staged) {
-      const float *rows = wst + (size_t)ti * SK * Epad;
-      for (int sp = 0; sp < SK; ++sp) {
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int j = 0; j < NKP; ++j) {
           const int e = min(2 * lane + 128 * j, Epad - 2);
-          const float2 v = *reinterpret_cast<const float2 *>(rows + sp * Epad + e);
-          z[2 * j] += v.x;
-          z[2 * j + 1] += v.y;
+          v[u][j] = *reinterpret_cast<const float2 *>(rows + min(u0 + u, n - 1) * Epad + e);
         }
-      }
-    } else {
-    const unsigned long long *row = reinterpret_cast<const unsigned long long *>(p.part + (size_t)m * p.Epad);
-    const size_t split2 = (size_t)M * p.Epad / 2;  // one split, in pairs
-    const int nload = SK * NKP;                     // load index = split * NKP + pair
-    for (int base = 0; base < nload; base += 8) {   // NKP divides 8: pair = u % NKP
-      const unsigned long long *a[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int s = min(base + u, nload - 1) / NKP;
-        const int e = min(2 * lane + 128 * (u % NKP), p.Epad - 2);
-        a[u] = row + s * split2 + (e >> 1);
-      }
-      unsigned long long v[8];
-      ld_coherent8(v, a);
+      for (int u = 0; u < 4; ++u)
+        if (u0 + u < n) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (base + u < nload) {
-          z[2 * (u % NKP)] += __uint_as_float((uint32_t)v[u]);
-          z[2 * (u % NKP) + 1] += __uint_as_float((uint32_t)(v[u] >> 32));
+          for (int j = 0; j < NKP; ++j) {
+            z[2 * j] += v[u][j].x;
+            z[2 * j + 1] += v[u][j].y;
+          }
         }
     }
-    }
-    const float sl = p.has_shared ? sh[m - t0] : 0.f;
-    if (p.logits_only) {
-#pragma unroll
-      for (int j = 0; j < NKP; ++j) {
-        const int e = 2 * lane + 128 * j;
-        if (e < E) p.logits_out[(size_t)m * p.Ep + e] = z[2 * j];
-        if (e + 1 < E) p.logits_out[(size_t)m * p.Ep + e + 1] = z[2 * j + 1];
-      }
-      if (p.has_shared && lane == 0) p.logits_out[(size_t)m * p.Ep + E] = sl;
-      continue;
-    }
-    uint32_t keys[2 * NKP];
+  };
+  auto token_keys = [&](const float (&z)[2 * NKP], uint32_t (&keys)[2 * NKP]) {
 #pragma unroll
     for (int j = 0; j < NKP; ++j) {
       const int e = 2 * lane + 128 * j;
@@ -430,7 +409,10 @@ __device__ void topk_group(const MfmaParams &p, int32_t *own, const float *sh, u
       keys[2 * j + 1] = e + 1 < E ? make_key(z[2 * j + 1], (uint32_t)(e + 1)) : 0u;
     }
     sort_desc_u32(keys);
-    const uint32_t mine = topk_sorted_u32(keys, k, lane);  // lane j < k: the j-th chosen key
+  };
+  // softmax over the chosen k, the shared slot, the stores
+  auto finish = [&](int m, uint32_t mine) {
+    const float sl = p.has_shared ? sh[m - t0] : 0.f;
     const float r = key_value(mine);
     const float r0 = readlane_f32(r, 0);
     const float ex = (lane < k) ? expf(r - r0) : 0.0f;
@@ -446,7 +428,47 @@ __device__ void topk_group(const MfmaParams &p, int32_t *own, const float *sh, u
       p.wts[(size_t)m * S + lane] = w;
       own[(m - t0) * S + lane] = id;
       if (p.do_align && lane < k)
-        __hip_atomic_fetch_add(p.c16 + (size_t)(m >> 7) * p.Ep4 + id, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(p.c16 + (size_t)(m >> 7) * p.c16_row + (id >> 2), 1u << (8 * (id & 3)),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
+  for (int ti = 0; ti < ntw; ti += 2) {
+    const bool two = ti + 1 < ntw;
+    const int ma = t0 + wave + 4 * ti, mb = two ? ma + 4 : ma;
+    float za[2 * NKP], zb[2 * NKP];
+#pragma unroll
+    for (int j = 0; j < 2 * NKP; ++j) za[j] = zb[j] = 0.f;
+    for (int s0 = 0; s0 < SK; s0 += sc) {
+      const int n = min(sc, SK - s0);
+      stage_rows(ma, mb, s0, n);
+      add_rows(0, n, za);
+      add_rows(1, n, zb);
+      wave_lds_sync();  // the next batch overwrites the slice
+    }
+    if (p.logits_only) {
+      for (int h = 0; h < (two ? 2 : 1); ++h) {
+        const int m = h ? mb : ma;
+        const float(&z)[2 * NKP] = h ? zb : za;
+#pragma unroll
+        for (int j = 0; j < NKP; ++j) {
+          const int e = 2 * lane + 128 * j;
+          if (e < E) p.logits_out[(size_t)m * p.Ep + e] = z[2 * j];
+          if (e + 1 < E) p.logits_out[(size_t)m * p.Ep + e + 1] = z[2 * j + 1];
+        }
+        if (p.has_shared && lane == 0) p.logits_out[(size_t)m * p.Ep + E] = sh[m - t0];
+      }
+      continue;
+    }
+    uint32_t ka[2 * NKP], kb[2 * NKP];
+    token_keys(za, ka);
+    if (two) {
+      token_keys(zb, kb);
+      uint32_t mine_a, mine_b;  // the two selections interleave
+      topk_sorted2_u32(ka, kb, k, lane, mine_a, mine_b);
+      finish(ma, mine_a);
+      finish(mb, mine_b);
+    } else {
+      finish(ma, topk_sorted_u32(ka, k, lane));
     }
   }
 }
@@ -454,28 +476,31 @@ __device__ void topk_group(const MfmaParams &p, int32_t *own, const float *sh, u
 // ------------------------------------------------------------- phase A ---
 
 // Column sums of the tile counters: tot[e] over all tiles and pre[e] over
-// the tiles before `tile`, for every expert.  The table is fetched in 16-byte
-// coherent loads into LDS (`tab`, kTabWords words), a slab of tiles at a time.
+// the tiles before `tile`, for every expert.  A counter row holds one byte
+// per expert (a tile has at most 128 pairs of one expert), c16_row words per
+// row, a multiple of 4.  The table is fetched in 16-byte coherent loads into
+// LDS (`tab`, kTabWords words), a slab of tiles at a time.
 constexpr int kTabWords = 16384;
 __device__ void tile_sums(const MfmaParams &p, int tile, uint32_t *tot, uint32_t *pre, uint32_t *tab) {
   const int tid = threadIdx.x;
-  const int E = p.E, Ep = p.Ep, Ep4 = p.Ep4, NT = p.NT;
+  const int E = p.E, Ep = p.Ep, W = p.c16_row, NT = p.NT;
   for (int e = tid; e < Ep; e += kThreads) {
     tot[e] = (e < E) ? 0u : (uint32_t)p.M;         // the shared expert takes every token
     pre[e] = (e < E) ? 0u : (uint32_t)(tile << 7);
   }
-  const int R = kTabWords / Ep4 > 0 ? kTabWords / Ep4 : 1;
+  const int R = kTabWords / W > 0 ? kTabWords / W : 1;
   for (int t0 = 0; t0 < NT; t0 += R) {
     const int nr = min(R, NT - t0);
-    const int nchunk = nr * Ep4 / 4;
-    const u32x4_coh *src = reinterpret_cast<const u32x4_coh *>(p.c16 + (size_t)t0 * Ep4);
+    const int nchunk = nr * W / 4;
+    const u32x4_coh *src = reinterpret_cast<const u32x4_coh *>(p.c16 + (size_t)t0 * W);
     u32x4_coh *dst = reinterpret_cast<u32x4_coh *>(tab);
     for (int c0 = 0; c0 < nchunk; c0 += kThreads * 16) {
       const u32x4_coh *a[16];
 #pragma unroll
       for (int u = 0; u < 16; ++u) a[u] = src + min(c0 + u * kThreads + tid, nchunk - 1);
       u32x4_coh v[16];
-      ld_coherent16(v, a);
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = *a[u];
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
         const int c = c0 + u * kThreads + tid;
@@ -485,10 +510,17 @@ __device__ void tile_sums(const MfmaParams &p, int tile, uint32_t *tot, uint32_t
     __syncthreads();
     for (int e = tid; e < E; e += kThreads) {
       uint32_t t = tot[e], q = pre[e];
-      for (int r = 0; r < nr; ++r) {
-        const uint32_t w = tab[r * Ep4 + e];
-        t += w;
-        q += (t0 + r < tile) ? w : 0u;
+      const int sh = 8 * (e & 3);
+      for (int r0 = 0; r0 < nr; r0 += 8) {  // 8 rows' reads issued before their sums
+        uint32_t w[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) w[u] = tab[min(r0 + u, nr - 1) * W + (e >> 2)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const uint32_t c = (r0 + u < nr) ? (w[u] >> sh) & 0xFFu : 0u;
+          t += c;
+          q += (t0 + r0 + u < tile) ? c : 0u;
+        }
       }
       tot[e] = t;
       pre[e] = q;
@@ -538,7 +570,8 @@ __device__ void align_group(const MfmaParams &p, const uint32_t *off, const uint
 #pragma unroll
     for (int u = 0; u < 8; ++u) a[u] = prev + min(i0 + u * kThreads + tid, nprev - 1);
     uint32_t v[8];
-    ld_coherent8(v, a);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = *a[u];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
       if (i0 + u * kThreads + tid < nprev && v[u] < (uint32_t)E) atomicAdd(hist + v[u], 1u);
@@ -574,7 +607,8 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(MfmaParams p) {
   // the tile counters start from zero in every launch (the workspace layout
   // moves with M, so nothing else may be assumed about this region)
   if (p.do_align && !p.logits_only)
-    for (int i = b * kThreads + threadIdx.x; i < p.NT * p.Ep4; i += (int)grid * kThreads) st_agent(p.c16 + i, 0u);
+    for (int i = b * kThreads + threadIdx.x; i < p.NT * p.c16_row; i += (int)grid * kThreads)
+      __hip_atomic_fetch_and(p.c16 + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int per_xcd = p.xcd_map ? (int)grid / 8 : 0;
   // the shared logits of this block's first token group need no other
   // block's data: they are computed during the first item's load latency
@@ -588,7 +622,28 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(MfmaParams p) {
     sh_pending = false;
   }
   if (sh_pending) shared_logits(p, sh_t0, sh_t1, sh);
+  // Touch the pages phases T and A read (this block's partial rows of every
+  // split, the tile counters, its tile's ids) so that their address
+  // translations are cached when those phases start; the latency overlaps
+  // the wait at the barrier.  The values only keep the loads alive.  These
+  // lines must not be cached in L2 before their writers are done (phases T
+  // and A read them with plain loads after the barriers), hence ld_agent.
+  uint32_t touch = 0;
+  if (b < p.ngroups) {
+    const int lane = threadIdx.x & 63, m0 = b * p.tpb;
+    const int tstart = (m0 >> 7) << 7;
+    if (threadIdx.x < 64) {
+      const uint32_t *a = reinterpret_cast<const uint32_t *>(p.c16);
+      if (lane < p.SK) a = reinterpret_cast<const uint32_t *>(p.part + ((size_t)lane * p.M + m0) * p.Epad);
+      else if (lane == p.SK + 1 && p.ids) a = reinterpret_cast<const uint32_t *>(p.ids + (size_t)tstart * p.S);
+      else if (lane == p.SK + 2 && p.ids) a = reinterpret_cast<const uint32_t *>(p.ids + (size_t)m0 * p.S);
+      // a coherent load: it warms the translation without leaving a copy of
+      // the line in this XCD's L2 (the data is written only after this)
+      touch = ld_agent(a);
+    }
+  }
   grid_barrier(p.ctr, 1, grid);
+  if (touch == 0xFFFFFFFFu && threadIdx.x == 1000) p.npp[0] = 0;  // never true
 
   // ---- T: logits, top-k, weights ----------------------------------------
   // LDS from here on: [0, 32K) this block's ids; then per-expert arrays; the
