@@ -64,18 +64,16 @@ int64_t tight_capacity(int64_t n, int64_t Ep, int64_t A) {
 // Workspace regions for one call.  Every region grows with M, so a workspace
 // sized for M_max serves every M <= M_max.
 struct Layout {
-  size_t counters = 0, keys = 0, shared = 0;             // small-M route
-  size_t tile_ticket = 0, cand = 0, lshared = 0, tcounts = 0, eoff = 0;  // large-M route
-  size_t counts = 0, ranks = 0;                          // align / large-M ranks
-  size_t part = 0, c16 = 0;                              // prefill (split-K) route
+  size_t counters = 0, keys = 0, shared = 0;  // small-M route
+  size_t counts = 0, ranks = 0;               // standalone align
+  size_t part = 0, c16 = 0;                   // prefill route (split-K partials, tile counters)
   size_t total = 0;
 };
 
 Layout layout_for(int64_t M, int64_t E, int64_t k, int64_t sh) {
   Layout L;
   const int64_t S = k + sh, Ep = E + sh, n = M * S;
-  const int64_t NE = (E + mr::kLargeBE - 1) / mr::kLargeBE;
-  const int64_t MTmax = (M + 15) / 16;  // row tiles at the smallest tile height
+  const int64_t NE = (E + 127) / 128;  // expert tiles of the prefill route
   auto take = [](size_t &o, size_t bytes) {
     const size_t at = o;
     o = align_up(o + (bytes ? bytes : 4), 256);
@@ -84,11 +82,6 @@ Layout layout_for(int64_t M, int64_t E, int64_t k, int64_t sh) {
   size_t o = mr::kCounterBytes;
   L.keys = take(o, (size_t)mr::kSmallMaxTokens * (size_t)E * 4);
   L.shared = take(o, (size_t)mr::kSmallMaxTokens * 8);
-  L.tile_ticket = take(o, (size_t)MTmax * 4);
-  L.cand = take(o, (size_t)(M * NE * k) * 4);
-  L.lshared = take(o, (size_t)M * 4);
-  L.tcounts = take(o, (size_t)(MTmax * Ep) * 4);
-  L.eoff = take(o, (size_t)Ep * 4);
   const int W = mr::align_words_per_expert((int)(Ep > 0 ? Ep : 1));
   const int64_t nch = (n + 64 * W - 1) / (64 * W);
   L.counts = take(o, (size_t)(nch * Ep) * 4);
@@ -102,16 +95,6 @@ Layout layout_for(int64_t M, int64_t E, int64_t k, int64_t sh) {
   L.c16 = take(o, (size_t)(NT * ((Ep + 15) / 16 * 4)) * 4);
   L.total = o;
   return L;
-}
-
-// The prefill path is the split-K kernel unless MR_PREFILL_KERNEL=tiles
-// selects the per-row-tile kernel (kept for comparison).
-bool use_mfma_path() {
-  static const bool v = [] {
-    const char *e = getenv("MR_PREFILL_KERNEL");
-    return !(e && strcmp(e, "tiles") == 0);
-  }();
-  return v;
 }
 
 int launch_result(hipError_t e, const char *fn) {
@@ -199,58 +182,13 @@ int route_impl(const char *fn, const void *x, const void *gate_w, const void *sh
     if (fill > sorted_cap) fill = sorted_cap;
   }
 
-  if (M > mr::kSmallMaxTokens && use_mfma_path()) {
-    const int cap = mr::mfma_capacity(E);
-    if (cap > 0) {
-      mr::MfmaParams q{};
-      q.x = static_cast<const uint16_t *>(x);
-      q.w = static_cast<const uint16_t *>(gate_w);
-      q.ws_row = static_cast<const uint16_t *>(shared_w);
-      q.M = M;
-      q.H = H;
-      q.E = E;
-      q.k = logits_only ? 1 : k;
-      q.S = (int)S;
-      q.Ep = (int)Ep;
-      q.has_shared = sh;
-      q.scale = scale;
-      q.ids = ids;
-      q.wts = wts;
-      q.NE = (E + 127) / 128;
-      q.NT = (M + 127) / 128;
-      q.nstages = (H + 63) / 64;
-      const int grid = cap < mr::kMfmaMaxGrid ? cap : mr::kMfmaMaxGrid;
-      int sk = grid / (q.NE * q.NT);
-      if (sk < 1) sk = 1;
-      if (sk > q.nstages) sk = q.nstages;
-      q.spp = (q.nstages + sk - 1) / sk;
-      q.SK = (q.nstages + q.spp - 1) / q.spp;
-      q.items = q.NE * q.NT * q.SK;
-      q.grid = grid;
-      q.xcd_map = (grid % 8 == 0) ? 1 : 0;
-      q.Epad = (E + 3) / 4 * 4;
-      q.part = reinterpret_cast<float *>(wsb + L.part);
-      q.c16 = reinterpret_cast<uint32_t *>(wsb + L.c16);
-      q.c16_row = (int)((Ep + 15) / 16 * 4);
-      q.zero16 = reinterpret_cast<const uint4 *>(ctr + mr::kCtrZero16);
-      q.ctr = ctr;
-      int tpb = 1;
-      while (tpb < 128 && (int64_t)tpb * grid < M) tpb *= 2;
-      q.tpb = tpb;
-      q.ngroups = (M + tpb - 1) / tpb;
-      q.do_align = do_align ? 1 : 0;
-      q.A = do_align ? A : 64;
-      q.log2A = do_align ? log2A : 6;
-      q.sorted = sorted;
-      q.expert_ids = expert_ids;
-      q.npp = npp;
-      q.logits_out = logits_out;
-      q.logits_only = logits_only ? 1 : 0;
-      return launch_result(mr::launch_route_mfma(q, s), fn);
-    }
-  }
   if (M > mr::kSmallMaxTokens) {
-    mr::LargeParams q{};
+    const int cap = mr::mfma_capacity(E);
+    if (cap < 1) {
+      g_last_error = std::string(fn) + ": could not size the prefill launch (no device or occupancy query failed)";
+      return MR_ELAUNCH;
+    }
+    mr::MfmaParams q{};
     q.x = static_cast<const uint16_t *>(x);
     q.w = static_cast<const uint16_t *>(gate_w);
     q.ws_row = static_cast<const uint16_t *>(shared_w);
@@ -264,31 +202,37 @@ int route_impl(const char *fn, const void *x, const void *gate_w, const void *sh
     q.scale = scale;
     q.ids = ids;
     q.wts = wts;
-    const int BT = mr::large_tile_tokens(M, E);
-    q.MT = (M + BT - 1) / BT;
-    q.NE = (E + mr::kLargeBE - 1) / mr::kLargeBE;
-    q.row_groups = (q.MT + 7) / 8;
+    q.NE = (E + 127) / 128;
+    q.NT = (M + 127) / 128;
+    q.nstages = (H + 63) / 64;
+    const int grid = cap < mr::kMfmaMaxGrid ? cap : mr::kMfmaMaxGrid;
+    int sk = grid / (q.NE * q.NT);
+    if (sk < 1) sk = 1;
+    if (sk > q.nstages) sk = q.nstages;
+    q.spp = (q.nstages + sk - 1) / sk;
+    q.SK = (q.nstages + q.spp - 1) / q.spp;
+    q.items = q.NE * q.NT * q.SK;
+    q.grid = grid;
+    q.xcd_map = (grid % 8 == 0) ? 1 : 0;
+    q.Epad = (E + 3) / 4 * 4;
+    q.part = reinterpret_cast<float *>(wsb + L.part);
+    q.c16 = reinterpret_cast<uint32_t *>(wsb + L.c16);
+    q.c16_row = (int)((Ep + 15) / 16 * 4);
+    q.zero16 = reinterpret_cast<const uint4 *>(ctr + mr::kCtrZero16);
     q.ctr = ctr;
-    q.tile_ticket = reinterpret_cast<uint32_t *>(wsb + L.tile_ticket);
-    q.cand = reinterpret_cast<uint32_t *>(wsb + L.cand);
-    q.shared_logit = reinterpret_cast<float *>(wsb + L.lshared);
-    q.tile_counts = reinterpret_cast<int32_t *>(wsb + L.tcounts);
-    q.expert_off = reinterpret_cast<int32_t *>(wsb + L.eoff);
-    q.ranks = reinterpret_cast<int32_t *>(wsb + L.ranks);
+    int tpb = 1;
+    while (tpb < 128 && (int64_t)tpb * grid < M) tpb *= 2;
+    q.tpb = tpb;
+    q.ngroups = (M + tpb - 1) / tpb;
     q.do_align = do_align ? 1 : 0;
     q.A = do_align ? A : 64;
     q.log2A = do_align ? log2A : 6;
-    q.S_magic = S_magic;
     q.sorted = sorted;
-    q.sorted_cap = sorted_cap;
     q.expert_ids = expert_ids;
-    q.expert_cap = expert_cap;
     q.npp = npp;
-    q.fill_count = fill;
-    q.may_help = (do_align && mr::large_grid(q) <= mr::large_max_resident_blocks(BT)) ? 1 : 0;
     q.logits_out = logits_out;
     q.logits_only = logits_only ? 1 : 0;
-    return launch_result(mr::launch_route_large(q, BT, s), fn);
+    return launch_result(mr::launch_route_mfma(q, s), fn);
   }
 
   mr::SmallParams p{};

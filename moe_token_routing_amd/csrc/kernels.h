@@ -76,38 +76,6 @@ struct AlignParams {
   int32_t *ranks;   // [n] rank of each pair inside its chunk
 };
 
-// Large-M fused route (+ align): MFMA tiles of BT tokens x 128 experts.
-constexpr int kLargeBE = 128;  // experts per tile
-struct LargeParams {
-  const uint16_t *x;       // [M, H] bf16
-  const uint16_t *w;       // [E, H] bf16
-  const uint16_t *ws_row;  // [H] bf16 or null
-  int M, H, E, k, S, Ep, has_shared;
-  float scale;
-  int32_t *ids;  // [M, S]
-  float *wts;    // [M, S]
-  int MT, NE;    // row tiles (ceil(M / BT)) and expert tiles (ceil(E / 128))
-  int row_groups;  // ceil(MT / 8): row tiles are dealt to the 8 XCDs in groups
-  uint32_t *ctr;          // counter words
-  uint32_t *tile_ticket;  // [MT] per-row-tile tickets
-  uint32_t *cand;         // [M, NE, k] candidate keys of every expert tile
-  float *shared_logit;    // [M]
-  int32_t *tile_counts;   // [MT, Ep]: per-tile counts, then per-tile exclusive prefixes
-  int32_t *expert_off;    // [Ep] padded offset of each expert
-  int32_t *ranks;         // [M * S] rank of each pair inside its row tile
-  int do_align, A, log2A;
-  uint32_t S_magic;
-  int32_t *sorted;
-  int64_t sorted_cap;
-  int32_t *expert_ids;
-  int64_t expert_cap;
-  int32_t *npp;
-  int64_t fill_count;
-  int may_help;       // the whole grid fits on the GPU at once
-  float *logits_out;  // logits_only: the caller's [M, Ep] fp32 buffer
-  int logits_only;
-};
-
 // Prefill route (+ align) in one persistent launch: split-K MFMA gate,
 // top-k per token, align; grid barriers between the phases.
 constexpr int kMfmaMaxGrid = 256;  // blocks of one launch (one per CU on MI355X)
@@ -144,10 +112,6 @@ size_t mfma_lds_bytes();
 int mfma_capacity(int E);
 hipError_t launch_route_mfma(const MfmaParams &p, hipStream_t stream);
 
-int large_tile_tokens(int M, int E);
-int large_grid(const LargeParams &p);
-hipError_t launch_route_large(const LargeParams &p, int BT, hipStream_t stream);
-int large_max_resident_blocks(int BT);
 
 int small_rows_per_block(int Ep, int M);
 hipError_t launch_route_small(const SmallParams &p, hipStream_t stream);

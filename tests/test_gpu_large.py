@@ -1,4 +1,4 @@
-"""Parity of the large-M (MFMA) route + align path with the CPU oracle, at the
+"""Parity of the prefill (split-K MFMA) route + align path with the CPU oracle, at the
 prefill workloads' full sizes and on ragged and edge shapes (needs a gfx950
 GPU).  Every case prints its name and shape before it runs."""
 import numpy as np
@@ -102,8 +102,8 @@ def test_exact_large_alignment_variants():
 
 
 def test_grid_larger_than_gpu():
-    """More tiles than fit on the GPU at once: blocks then never wait for the
-    published offsets and the winner scatters alone."""
+    """More token groups than blocks of the persistent launch: every block
+    handles several groups through the top-k and align phases."""
     _say("M=20000 E=512")
     d = workloads.make_inputs(20000, 512, 256, True, "normal", seed=21)
     _run(d, 10)
