@@ -50,7 +50,9 @@
  *   are skipped (never written out of bounds).
  * - Workspace `ws` (ws_bytes >= mr_workspace_bytes(...)) must be zeroed ONCE
  *   by the caller before first use (e.g. torch.zeros).  Every launch leaves
- *   its counters at zero again, so the same workspace can be reused and
+ *   it ready for the next one (its counters at zero again, apart from a
+ *   launch count kept by the prefill kernel, whose parity selects one of two
+ *   grid-barrier counter sets), so the same workspace can be reused and
  *   replayed from a graph.  Launches that may overlap in time (different
  *   streams) need different workspaces.  If a launch was aborted,
  *   mr_workspace_reset() re-zeroes the counters.

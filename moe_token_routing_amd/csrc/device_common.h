@@ -393,34 +393,6 @@ __device__ __forceinline__ bool last_block_ticket(uint32_t *ticket, uint32_t cou
   return *lds_flag != 0u;
 }
 
-// Two-level version of last_block_ticket for many arrivals: arrival `idx`
-// (unique in [0, count)) first takes a ticket on first-level counter
-// idx % kLanes (each in its own 256-byte slot, `stride` words apart); the
-// arrival that completes a first-level counter then takes a ticket on `top`.
-// Same contract and return value as last_block_ticket.  The winner must
-// reset all the counters (first level and top) before anything reuses them.
-template <int kLanes>
-__device__ __forceinline__ bool last_block_ticket2(uint32_t *lanes, int stride, uint32_t *top, uint32_t count,
-                                                   uint32_t *lds_flag, uint32_t idx) {
-  wait_own_stores();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t nl = count < (uint32_t)kLanes ? count : (uint32_t)kLanes;
-    const uint32_t r = idx % nl;
-    const uint32_t in_lane = (count - 1 - r) / nl + 1;  // arrivals sharing this counter
-    uint32_t last = 0;
-    const uint32_t t = __hip_atomic_fetch_add(lanes + (size_t)r * stride, 1u, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-    if (t == in_lane - 1) {
-      const uint32_t u = __hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      last = (u == nl - 1) ? 1u : 0u;
-    }
-    *lds_flag = last;
-  }
-  __syncthreads();
-  return *lds_flag != 0u;
-}
-
 __device__ __forceinline__ void reset_counter(uint32_t *c) {
   __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

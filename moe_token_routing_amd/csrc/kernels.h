@@ -13,22 +13,27 @@ constexpr int kMaxRouteExperts = 1024;  // routed E for the route kernels
 constexpr int kMaxAlignExperts = 4096;  // E' for align
 constexpr int kSmallMaxTokens = 16;     // route_small handles M <= 16
 
-// Counter words at the start of the workspace (all zero between launches).
-// The first 256 bytes hold single counters; then kTicketLanes first-level
-// ticket counters follow, each alone in its own 256-byte slot so that blocks
-// taking tickets spread their atomics over several addresses.
+// Counter words at the start of the workspace.  The first 256 bytes hold
+// single counters; then kTicketLanes first-level barrier counters follow,
+// each in its own 256-byte slot so that blocks arriving at a grid barrier
+// spread their atomics over several addresses.  Every counter is zero
+// between launches except the prefill kernel's launch count (kCtrEpoch): its
+// parity picks which of two barrier counter sets a launch uses, and each
+// launch clears the other set for the next one.
 enum CounterIndex : int {
-  kCtrTicket = 0,     // last-block election (second level)
+  kCtrBarTop0 = 0,    // prefill grid barrier, set 0: completed lanes
   kCtrStarted = 1,    // blocks that have begun
   kCtrDone = 2,       // phase-one completions
   kCtrPublished = 3,  // winner's publication flag
   kCtrWork = 4,       // work-queue head
   kCtrExited = 5,     // block exits
   kCtrError = 6,      // set to 1 if a bounded wait gave up (never expected)
+  kCtrEpoch = 16,     // prefill launches so far (any value is a valid start)
+  kCtrBarTop1 = 32,   // prefill grid barrier, set 1: completed lanes
   kCtrZero16 = 60,    // words 60..63: always zero (a 16-byte zero source)
 };
 constexpr int kTicketLanes = 16;
-constexpr int kTicketLaneStride = 64;  // words (256 bytes)
+constexpr int kTicketLaneStride = 64;  // words (256 bytes); set s of lane r at word 64 + 64 r + 32 s
 constexpr size_t kCounterBytes = 256 + (size_t)kTicketLanes * kTicketLaneStride * 4;
 
 // Small-M fused route (+ align).

@@ -34,14 +34,17 @@
 //    counter.
 // A. Align.  Every block turns the tile counters into padded expert offsets
 //    (block scan) and the prefix of earlier tiles, adds the counts of the
-//    earlier tokens of its own tile (read back from topk_ids), and scatters
-//    its pairs: inside an expert, pairs keep ascending flat index.  Blocks
-//    also pad the experts dealt to them and write expert_ids; block 0 writes
-//    npp.  The last block to leave re-zeroes the counters.
+//    earlier tokens of its own tile (read back from topk_ids, in the same
+//    round of loads as the counters) and of its own earlier tokens (a bit
+//    mask per expert), and scatters its pairs in parallel: inside an expert,
+//    pairs keep ascending flat index.  Blocks also pad the experts dealt to
+//    them and write expert_ids; block 0 writes npp.
 //
-// Workspace: only the counter words must be zero at launch (and are zero
-// again after it); the tile counters (one byte per expert and 128-token tile)
-// are cleared during phase G.
+// Workspace: the counter words as the library leaves them (the grid
+// barriers use one of two counter sets by the parity of a launch count; each
+// launch clears the other set and block 0 advances the count at the end);
+// the tile counters (one byte per expert and 128-token tile) are cleared
+// during phase G.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -106,28 +109,34 @@ __device__ __forceinline__ void wait_stages(int n) {
   else wait_vmcnt<0>();
 }
 
-// Grid barrier over all `grid` blocks, generation `gen` (1, 2, ...): each
-// block takes a ticket on one of up to kTicketLanes first-level counters
-// (256 bytes apart, so arrivals do not serialise on one address); the
-// arrival that completes a lane bumps `top`; everybody waits for `top` to
+// Grid barrier over all `grid` blocks, generation `gen` (1, 2, ...) of this
+// launch, on counter set `set` (zero at launch start): each block takes a
+// ticket on one of up to kTicketLanes first-level counters (256 bytes apart,
+// so arrivals do not serialise on one address); the arrival that completes a
+// lane bumps the set's top counter; everybody waits for the top counter to
 // reach gen * lanes.  Data written with st_agent (or agent-scope atomics)
 // before the barrier is visible to coherent loads (ld_agent, ld_coherent8)
-// after it.  The wait is bounded: if it gives up, the
-// error word is set and the block goes on.
-__device__ __forceinline__ void grid_barrier(uint32_t *ctr, uint32_t gen, uint32_t grid) {
+// after it.  The wait is bounded: if it gives up, the error word is set and
+// the block goes on.  Only thread 0's arguments matter.
+__device__ __forceinline__ uint32_t *barrier_lane(uint32_t *ctr, uint32_t set, uint32_t r) {
+  return ctr + 64 + (size_t)r * kTicketLaneStride + 32 * set;
+}
+__device__ __forceinline__ uint32_t *barrier_top(uint32_t *ctr, uint32_t set) {
+  return ctr + (set ? kCtrBarTop1 : kCtrBarTop0);
+}
+__device__ __forceinline__ void grid_barrier(uint32_t *ctr, uint32_t set, uint32_t gen, uint32_t grid) {
   wait_own_stores();
   __syncthreads();
   if (threadIdx.x == 0) {
     const uint32_t nl = grid < (uint32_t)kTicketLanes ? grid : (uint32_t)kTicketLanes;
     const uint32_t r = blockIdx.x % nl;
     const uint32_t in_lane = (grid - 1 - r) / nl + 1;
-    uint32_t *lane_ctr = ctr + 64 + (size_t)r * kTicketLaneStride;
-    const uint32_t t = __hip_atomic_fetch_add(lane_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (t == gen * in_lane - 1)
-      __hip_atomic_fetch_add(ctr + kCtrTicket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t *top = barrier_top(ctr, set);
+    const uint32_t t = __hip_atomic_fetch_add(barrier_lane(ctr, set, r), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (t == gen * in_lane - 1) __hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint32_t target = gen * nl;
     int it = 0;
-    while (__hip_atomic_load(ctr + kCtrTicket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    while (__hip_atomic_load(top, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
       if (++it == kBarrierSpin) {
         __hip_atomic_store(ctr + kCtrError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
@@ -307,32 +316,46 @@ __device__ void gate_item(const MfmaParams &p, uint8_t *smem, int et, int tt, in
 // Shared-expert logits of tokens [t0, t1) (t1 - t0 <= 128) into sh[]: x rows
 // dotted with the shared gate row in fp32, a fixed summation order.  x and
 // the gate rows are never written by the launch, so plain loads are fine.
-// Each wave takes tokens wave, wave + 4, ...; a lane takes the 16-byte
-// chunks lane + 64 u of the row, 8 chunks per batch, all loads of a batch
-// issued before its arithmetic.
+// Each wave takes tokens wave, wave + 4, ..., two at a time; a lane takes the
+// 16-byte chunks lane + 64 u of the rows, 8 chunks per batch, and the gate
+// chunks of a batch serve both tokens; all loads of a batch are issued before
+// its arithmetic.
 __device__ void shared_logits(const MfmaParams &p, int t0, int t1, float *sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int kW = kThreads / kWave;
   const int H = p.H, nch = H >> 3;  // 16-byte chunks per row
   const uint4 *wrow = reinterpret_cast<const uint4 *>(p.ws_row);
-  for (int m = t0 + wave; m < t1; m += kThreads / kWave) {
-    const uint4 *xr = reinterpret_cast<const uint4 *>(p.x + (size_t)m * H);
-    float acc[8];
+  for (int ma = t0 + wave; ma < t1; ma += 2 * kW) {
+    const bool two = ma + kW < t1;
+    const uint4 *xa = reinterpret_cast<const uint4 *>(p.x + (size_t)ma * H);
+    const uint4 *xb = reinterpret_cast<const uint4 *>(p.x + (size_t)(two ? ma + kW : ma) * H);
+    float acc_a[8], acc_b[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc[u] = 0.f;
+    for (int u = 0; u < 8; ++u) acc_a[u] = acc_b[u] = 0.f;
     for (int c0 = 0; c0 < nch; c0 += 64 * 8) {
-      uint4 xv[8], wv[8];
+      uint4 wv[8], av[8], bv[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int c = min(c0 + 64 * u + lane, nch - 1);
-        xv[u] = xr[c];
         wv[u] = wrow[c];
+        av[u] = xa[c];
+        bv[u] = xb[c];
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u)
-        if (c0 + 64 * u + lane < nch) acc[u] = dot8_bf16(xv[u], wv[u], acc[u]);
+        if (c0 + 64 * u + lane < nch) {
+          acc_a[u] = dot8_bf16(av[u], wv[u], acc_a[u]);
+          acc_b[u] = dot8_bf16(bv[u], wv[u], acc_b[u]);
+        }
     }
-    const float v = wave_sum_f32(((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7])));
-    if (lane == 0) sh[m - t0] = v;
+    const float va = wave_sum_f32(((acc_a[0] + acc_a[1]) + (acc_a[2] + acc_a[3])) +
+                                  ((acc_a[4] + acc_a[5]) + (acc_a[6] + acc_a[7])));
+    const float vb = wave_sum_f32(((acc_b[0] + acc_b[1]) + (acc_b[2] + acc_b[3])) +
+                                  ((acc_b[4] + acc_b[5]) + (acc_b[6] + acc_b[7])));
+    if (lane == 0) {
+      sh[ma - t0] = va;
+      if (two) sh[ma + kW - t0] = vb;
+    }
   }
 }
 
@@ -475,24 +498,64 @@ __device__ void topk_group(const MfmaParams &p, int32_t *own, const float *sh, u
 
 // ------------------------------------------------------------- phase A ---
 
-// Column sums of the tile counters: tot[e] over all tiles and pre[e] over
-// the tiles before `tile`, for every expert.  A counter row holds one byte
-// per expert (a tile has at most 128 pairs of one expert), c16_row words per
-// row, a multiple of 4.  The table is fetched in 16-byte coherent loads into
-// LDS (`tab`, kTabWords words), a slab of tiles at a time.
-constexpr int kTabWords = 16384;
-__device__ void tile_sums(const MfmaParams &p, int tile, uint32_t *tot, uint32_t *pre, uint32_t *tab) {
+// LDS layout of phase A (byte offsets into the dynamic LDS).  The group's ids
+// (`own`, written in phase T) stay at the start; the phase-T staging slices
+// above them are free again.
+constexpr int kOwnBytes = 17408;                        // tpb * S <= 128 * 33 ids
+constexpr int kMaskOff = kOwnBytes;                     // per expert: 4 words of token bits
+constexpr int kMaskWords = (kMaxRouteExperts + 1) * 4;
+constexpr int kArrOff = kMaskOff + kMaskWords * 4;      // tot, pre, off, hist: per expert
+constexpr int kArrWords = kMaxRouteExperts + 4;
+constexpr int kTabOff = (kArrOff + 4 * kArrWords * 4 + 1023) & ~1023;
+constexpr int kTabWords = (kRingBytes - kTabOff) / 4;   // tile-counter slab
+static_assert(kTabOff < kRingBytes && kTabWords >= 4096, "phase A layout");
+
+// Places the pairs of token group g (own[] holds its ids) into
+// sorted_token_ids and leaves, for every expert e, tot[e] (pairs over all
+// tokens) and off[e] (padded start of its segment) in LDS; returns npp.
+//
+// A pair (m, j) of routed expert e goes to
+//   off[e] + (pairs of e in the 128-token tiles before m's)
+//          + (pairs of e among the earlier tokens of m's tile),
+// so each expert's pairs keep ascending flat index m * S + j.  The first
+// term comes from the per-(tile, expert) counters, the second from the ids
+// of the tile's tokens before the group (read back from topk_ids) plus a bit
+// mask per expert of the group's own tokens.  The shared slot of token m
+// sits at off[E] + m.  The counter table and the earlier ids are fetched in
+// one round of loads.
+__device__ uint32_t align_group(const MfmaParams &p, int g, const int32_t *own, uint8_t *smem,
+                                uint32_t *scan_tmp) {
   const int tid = threadIdx.x;
-  const int E = p.E, Ep = p.Ep, W = p.c16_row, NT = p.NT;
+  const int M = p.M, E = p.E, Ep = p.Ep, S = p.S, W = p.c16_row, NT = p.NT;
+  uint32_t *mask = reinterpret_cast<uint32_t *>(smem + kMaskOff);
+  uint32_t *tot = reinterpret_cast<uint32_t *>(smem + kArrOff);
+  uint32_t *pre = tot + kArrWords, *off = pre + kArrWords, *hist = off + kArrWords;
+  uint32_t *tab = reinterpret_cast<uint32_t *>(smem + kTabOff);
+  const bool has = g < p.ngroups;
+  const int t0 = has ? g * p.tpb : 0, t1 = has ? min(M, t0 + p.tpb) : 0;
+  const int tile = t0 >> 7, tstart = tile << 7;
+  const int nmw = (p.tpb + 31) >> 5;  // mask words per expert
   for (int e = tid; e < Ep; e += kThreads) {
-    tot[e] = (e < E) ? 0u : (uint32_t)p.M;         // the shared expert takes every token
-    pre[e] = (e < E) ? 0u : (uint32_t)(tile << 7);
+    tot[e] = (e < E) ? 0u : (uint32_t)M;  // the shared expert takes every token
+    pre[e] = 0u;
+    hist[e] = 0u;
+    for (int w = 0; w < nmw; ++w) mask[e * nmw + w] = 0u;
   }
+  // routed pairs of the tile's tokens before the group (contiguous in
+  // topk_ids): the first 8 per thread are loaded now, beside the table
+  const int nprev = (t0 - tstart) * S;
+  const uint32_t *prev = reinterpret_cast<const uint32_t *>(p.ids + (size_t)tstart * S);
+  uint32_t pv[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) pv[u] = prev[min(u * kThreads + tid, max(nprev - 1, 0))];
+  __syncthreads();
+  // column sums of the counter table, a slab of tiles at a time: one byte
+  // per expert, c16_row words per tile
   const int R = kTabWords / W > 0 ? kTabWords / W : 1;
-  for (int t0 = 0; t0 < NT; t0 += R) {
-    const int nr = min(R, NT - t0);
+  for (int r0 = 0; r0 < NT; r0 += R) {
+    const int nr = min(R, NT - r0);
     const int nchunk = nr * W / 4;
-    const u32x4_coh *src = reinterpret_cast<const u32x4_coh *>(p.c16 + (size_t)t0 * W);
+    const u32x4_coh *src = reinterpret_cast<const u32x4_coh *>(p.c16 + (size_t)r0 * W);
     u32x4_coh *dst = reinterpret_cast<u32x4_coh *>(tab);
     for (int c0 = 0; c0 < nchunk; c0 += kThreads * 16) {
       const u32x4_coh *a[16];
@@ -511,15 +574,15 @@ __device__ void tile_sums(const MfmaParams &p, int tile, uint32_t *tot, uint32_t
     for (int e = tid; e < E; e += kThreads) {
       uint32_t t = tot[e], q = pre[e];
       const int sh = 8 * (e & 3);
-      for (int r0 = 0; r0 < nr; r0 += 8) {  // 8 rows' reads issued before their sums
+      for (int i0 = 0; i0 < nr; i0 += 8) {  // 8 rows' reads issued before their sums
         uint32_t w[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) w[u] = tab[min(r0 + u, nr - 1) * W + (e >> 2)];
+        for (int u = 0; u < 8; ++u) w[u] = tab[min(i0 + u, nr - 1) * W + (e >> 2)];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const uint32_t c = (r0 + u < nr) ? (w[u] >> sh) & 0xFFu : 0u;
+          const uint32_t c = (i0 + u < nr) ? (w[u] >> sh) & 0xFFu : 0u;
           t += c;
-          q += (t0 + r0 + u < tile) ? c : 0u;
+          q += (r0 + i0 + u < tile) ? c : 0u;
         }
       }
       tot[e] = t;
@@ -527,81 +590,79 @@ __device__ void tile_sums(const MfmaParams &p, int tile, uint32_t *tot, uint32_t
     }
     __syncthreads();
   }
-}
-
-// Padded expert offsets (exclusive scan of ceil(tot / A) * A) into off[];
-// returns npp.
-__device__ uint32_t expert_offsets(const MfmaParams &p, const uint32_t *tot, uint32_t *off, uint32_t *scan_tmp) {
-  const int tid = threadIdx.x;
-  const int Ep = p.Ep;
-  const uint32_t amask = (uint32_t)p.A - 1u;
-  uint32_t carry = 0;
-  for (int e0 = 0; e0 < Ep; e0 += kThreads) {
-    const int e = e0 + tid;
-    const uint32_t c = e < Ep ? tot[e] : 0u;
-    const uint32_t P = (c + amask) & ~amask;
-    uint32_t blk_total;
-    const uint32_t o = carry + block_excl_scan_u32<kThreads>(P, scan_tmp, &blk_total);
-    carry += blk_total;
-    if (e < Ep) off[e] = o;
-  }
-  __syncthreads();
-  return carry;
-}
-
-// Scatter of group g's pairs: sorted[off + pre + (earlier pairs of the same
-// expert in this tile)] = flat index.
-__device__ void align_group(const MfmaParams &p, const uint32_t *off, const uint32_t *pre, uint32_t *offp,
-                            uint32_t *hist, const int32_t *own, int g) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int M = p.M, E = p.E, Ep = p.Ep, S = p.S;
-  const int t0 = g * p.tpb, t1 = min(M, t0 + p.tpb);
-  const int tstart = (t0 >> 7) << 7;
-  for (int e = tid; e < Ep; e += kThreads) {
-    offp[e] = off[e] + pre[e];
-    hist[e] = (e < E) ? 0u : (uint32_t)(t0 - tstart);  // shared: one pair per earlier token
-  }
-  __syncthreads();
-  // routed pairs of the tile's earlier tokens (contiguous in topk_ids)
-  const int nprev = (t0 - tstart) * S;
-  const uint32_t *prev = reinterpret_cast<const uint32_t *>(p.ids + (size_t)tstart * S);
-  for (int i0 = 0; i0 < nprev; i0 += kThreads * 8) {
-    const uint32_t *a[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) a[u] = prev + min(i0 + u * kThreads + tid, nprev - 1);
+  for (int u = 0; u < 8; ++u)
+    if (u * kThreads + tid < nprev && pv[u] < (uint32_t)E) atomicAdd(hist + pv[u], 1u);
+  for (int i0 = 8 * kThreads; i0 < nprev; i0 += 8 * kThreads) {
     uint32_t v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = *a[u];
+    for (int u = 0; u < 8; ++u) v[u] = prev[min(i0 + u * kThreads + tid, nprev - 1)];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
       if (i0 + u * kThreads + tid < nprev && v[u] < (uint32_t)E) atomicAdd(hist + v[u], 1u);
   }
-  __syncthreads();
-  // own pairs, token by token (experts of one token are distinct)
-  if (wave == 0) {
-    for (int m = t0; m < t1; ++m) {
-      if (lane < S) {
-        const int32_t e = own[(m - t0) * S + lane];
-        if ((uint32_t)e < (uint32_t)Ep) {
-          const uint32_t dst = offp[e] + hist[e];
-          hist[e] += 1u;
-          p.sorted[dst] = m * S + lane;
-        }
-      }
-      wave_lds_sync();
+  const int npairs = (t1 - t0) * S;
+  for (int i = tid; i < npairs; i += kThreads) {
+    const int32_t e = own[i];
+    if ((uint32_t)e < (uint32_t)E) {
+      const int tok = i / S;
+      atomicOr(mask + e * nmw + (tok >> 5), 1u << (tok & 31));
     }
   }
   __syncthreads();
+  // padded offsets: each thread scans a run of q consecutive experts
+  const uint32_t amask = (uint32_t)p.A - 1u;
+  const int q = (Ep + kThreads - 1) / kThreads;
+  const int e0 = tid * q;
+  uint32_t run = 0;
+  for (int j = 0; j < q; ++j)
+    if (e0 + j < Ep) run += (tot[e0 + j] + amask) & ~amask;
+  uint32_t npp;
+  uint32_t o = block_excl_scan_u32<kThreads>(run, scan_tmp, &npp);
+  for (int j = 0; j < q; ++j)
+    if (e0 + j < Ep) {
+      off[e0 + j] = o;
+      o += (tot[e0 + j] + amask) & ~amask;
+    }
+  __syncthreads();
+  for (int i = tid; i < npairs; i += kThreads) {
+    const int32_t e = own[i];
+    const int tok = i / S;
+    uint32_t dst;
+    if ((uint32_t)e < (uint32_t)E) {
+      const uint32_t *mk = mask + e * nmw;
+      uint32_t rank = __popc(mk[tok >> 5] & ((1u << (tok & 31)) - 1u));
+      for (int w = 0; w < (tok >> 5); ++w) rank += __popc(mk[w]);
+      dst = off[e] + pre[e] + hist[e] + rank;
+    } else if (e == E && p.has_shared) {
+      dst = off[E] + (uint32_t)(t0 + tok);
+    } else {
+      continue;
+    }
+    p.sorted[dst] = (t0 + tok) * S + (i - tok * S);
+  }
+  return npp;
 }
 
 template <int NKP>
 __global__ __launch_bounds__(kThreads) void route_mfma_kernel(MfmaParams p) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   __shared__ uint32_t scan_tmp[kThreads / kWave + 1];
-  __shared__ uint32_t flag;
   __shared__ float sh[128];  // shared-expert logits of the current token group
   const int b = blockIdx.x;
   const uint32_t grid = gridDim.x;
+
+  // Barrier counter set of this launch: the parity of the launch count.  The
+  // other set was used by the previous launch (which has finished); block 0
+  // clears it for the next launch.  Every block reads the count before its
+  // first barrier arrival, and block 0 advances it only after the last
+  // barrier, so all blocks agree on the set.
+  uint32_t set = 0;
+  if (threadIdx.x == 0 || (b == 0 && threadIdx.x <= kTicketLanes)) set = ld_agent(p.ctr + kCtrEpoch) & 1u;
+  if (b == 0 && threadIdx.x < kTicketLanes + 1) {
+    uint32_t *c = threadIdx.x < kTicketLanes ? barrier_lane(p.ctr, set ^ 1u, threadIdx.x) : barrier_top(p.ctr, set ^ 1u);
+    __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 
   // ---- G: gate partials -------------------------------------------------
   // the tile counters start from zero in every launch (the workspace layout
@@ -642,20 +703,14 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(MfmaParams p) {
       touch = ld_agent(a);
     }
   }
-  grid_barrier(p.ctr, 1, grid);
+  grid_barrier(p.ctr, set, 1, grid);
   if (touch == 0xFFFFFFFFu && threadIdx.x == 1000) p.npp[0] = 0;  // never true
 
   // ---- T: logits, top-k, weights ----------------------------------------
-  // LDS from here on: [0, 32K) this block's ids; then per-expert arrays; the
-  // tile-counter slab from 64K
+  // LDS from here on: this block's ids at the start (kept until phase A);
+  // phase T stages partial rows from 32 KB; phase A's arrays follow the ids
   int32_t *own = reinterpret_cast<int32_t *>(smem);
   const bool align = p.do_align && !p.logits_only;
-  uint32_t *tot = reinterpret_cast<uint32_t *>(smem + 32768);
-  uint32_t *pre = tot + kMaxRouteExperts + 4;
-  uint32_t *off = pre + kMaxRouteExperts + 4;
-  uint32_t *offp = off + kMaxRouteExperts + 4;
-  uint32_t *hist = offp + kMaxRouteExperts + 4;
-  uint32_t *tab = reinterpret_cast<uint32_t *>(smem + 65536);
   // A block owns more than one group only for M > 128 * grid; then `own`
   // holds one group at a time and is reloaded in phase A.
   const bool multi = (int)grid < p.ngroups;
@@ -668,25 +723,23 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(MfmaParams p) {
     topk_group<NKP>(p, own, sh, smem + 32768, g);
   }
   if (align) {
-    grid_barrier(p.ctr, 2, grid);
+    grid_barrier(p.ctr, set, 2, grid);
+    uint32_t npp = 0;
     if (!multi) {
-      tile_sums(p, b < p.ngroups ? (b * p.tpb) >> 7 : 0, tot, pre, tab);
-      const uint32_t npp = expert_offsets(p, tot, off, scan_tmp);
-      if (b < p.ngroups) align_group(p, off, pre, offp, hist, own, b);
-      if (b == 0 && threadIdx.x == 0) *p.npp = (int32_t)npp;
+      npp = align_group(p, b, own, smem, scan_tmp);
     } else {
-      uint32_t npp = 0;
       for (int g = b; g < p.ngroups; g += grid) {
-        tile_sums(p, (g * p.tpb) >> 7, tot, pre, tab);
-        npp = expert_offsets(p, tot, off, scan_tmp);
         const int t0 = g * p.tpb, t1 = min(p.M, t0 + p.tpb);
+        __syncthreads();  // the previous group is placed
         for (int i = threadIdx.x; i < (t1 - t0) * p.S; i += kThreads) own[i] = ld_agent(p.ids + (size_t)t0 * p.S + i);
         __syncthreads();
-        align_group(p, off, pre, offp, hist, own, g);
+        npp = align_group(p, g, own, smem, scan_tmp);
       }
-      if (b == 0 && threadIdx.x == 0) *p.npp = (int32_t)npp;
     }
+    if (b == 0 && threadIdx.x == 0) *p.npp = (int32_t)npp;
     // padding and expert_ids of the experts dealt to this block
+    const uint32_t *tot = reinterpret_cast<const uint32_t *>(smem + kArrOff);
+    const uint32_t *off = tot + 2 * kArrWords;
     for (int e = b; e < p.Ep; e += grid) {
       const uint32_t c = tot[e], o = off[e];
       const uint32_t P = (c + (uint32_t)p.A - 1u) & ~((uint32_t)p.A - 1u);
@@ -696,28 +749,11 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(MfmaParams p) {
     }
   }
 
-  // ---- exit: the last block re-zeroes the counters ----------------------
-  const uint32_t gens = align ? 3u : 2u;
-  wait_own_stores();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t nl = grid < (uint32_t)kTicketLanes ? grid : (uint32_t)kTicketLanes;
-    const uint32_t r = b % nl;
-    const uint32_t in_lane = (grid - 1 - r) / nl + 1;
-    uint32_t last = 0;
-    const uint32_t t = __hip_atomic_fetch_add(p.ctr + 64 + (size_t)r * kTicketLaneStride, 1u, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-    if (t == gens * in_lane - 1) {
-      const uint32_t u = __hip_atomic_fetch_add(p.ctr + kCtrTicket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      last = (u == gens * nl - 1) ? 1u : 0u;
-    }
-    flag = last;
-  }
-  __syncthreads();
-  if (flag) {
-    if (threadIdx.x < kTicketLanes) reset_counter(p.ctr + 64 + (size_t)threadIdx.x * kTicketLaneStride);
-    if (threadIdx.x == 0) reset_counter(p.ctr + kCtrTicket);
-  }
+  // ---- exit: block 0 advances the launch count ---------------------------
+  // (every block has passed this launch's last barrier, so each has read the
+  // count already)
+  if (b == 0 && threadIdx.x == 0)
+    __hip_atomic_fetch_add(p.ctr + kCtrEpoch, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int NKP>
