@@ -75,6 +75,10 @@ constexpr int kQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
 constexpr int kRowHalfMirror = 0x141; // lane i <- lane 7-i within 8
 constexpr int kRowMirror = 0x140;     // lane i <- lane 15-i within 16
 constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kQuadRev = 0x1B;        // quad_perm [3,2,1,0]
+constexpr int kRowRor8 = 0x128;       // lane i <- lane (i + 8) mod 16 within 16: i ^ 8
+constexpr int kWaveShl1 = 0x130;      // lane i <- lane i + 1 (lane 63: `old`)
+constexpr int kWaveShr1 = 0x138;      // lane i <- lane i - 1 (lane 0: `old`)
 
 // Max over the 64 lanes; every lane must be active.  Returns a wave-uniform
 // value.
@@ -100,6 +104,59 @@ __device__ __forceinline__ uint32_t wave_max_all_u32(uint32_t v) {
   v = max(a[0], a[1]);
   const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
   return max(b[0], b[1]);
+}
+
+// Value held by lane (lane ^ J), for J = 1, 2, 4, 8 (DPP inside a row of 16;
+// J = 4 is the half-row mirror 7 - i = i ^ 7 followed by a quad reversal,
+// i ^ 3) and J = 16, 32 (gfx950's permlane16 / permlane32 swaps, which hand
+// each lane both its own row and the partner row).  Every lane active.
+template <int J>
+__device__ __forceinline__ uint32_t xor_lane_u32(uint32_t v, int lane) {
+  if constexpr (J == 1) {
+    return dpp_u32<kQuadXor1>(v);
+  } else if constexpr (J == 2) {
+    return dpp_u32<kQuadXor2>(v);
+  } else if constexpr (J == 4) {
+    return dpp_u32<kQuadRev>(dpp_u32<kRowHalfMirror>(v));
+  } else if constexpr (J == 8) {
+    return dpp_u32<kRowRor8>(v);
+  } else if constexpr (J == 16) {
+    const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (lane & 16) ? a[0] : a[1];
+  } else {
+    static_assert(J == 32, "lane distance");
+    const auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (lane & 32) ? a[0] : a[1];
+  }
+}
+
+// One value per lane sorted ascending across the 64 lanes: Batcher's bitonic
+// network (merge stages K = 2 .. 64, each with half-cleaner steps J = K/2 ..
+// 1; 21 compare-exchanges).  Every lane must be active.
+template <int K, int J>
+__device__ __forceinline__ uint32_t bitonic_merge_u32(uint32_t v, int lane) {
+  const uint32_t q = xor_lane_u32<J>(v, lane);
+  const bool up = (lane & K) == 0, lower = (lane & J) == 0;
+  v = (lower == up) ? min(v, q) : max(v, q);
+  if constexpr (J > 1) return bitonic_merge_u32<K, J / 2>(v, lane);
+  else return v;
+}
+__device__ __forceinline__ uint32_t wave_sort_asc_u32(uint32_t v, int lane) {
+  v = bitonic_merge_u32<2, 1>(v, lane);
+  v = bitonic_merge_u32<4, 2>(v, lane);
+  v = bitonic_merge_u32<8, 4>(v, lane);
+  v = bitonic_merge_u32<16, 8>(v, lane);
+  v = bitonic_merge_u32<32, 16>(v, lane);
+  return bitonic_merge_u32<64, 32>(v, lane);
+}
+
+// Lane i receives lane i - 1 (shr) or lane i + 1 (shl); the end lane gets
+// `fill`.
+__device__ __forceinline__ uint32_t wave_shr1_u32(uint32_t v, uint32_t fill) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)fill, (int)v, kWaveShr1, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_shl1_u32(uint32_t v, uint32_t fill) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)fill, (int)v, kWaveShl1, 0xF, 0xF, false);
 }
 
 // Sorts N (a power of two) keys held in registers into descending order

@@ -186,6 +186,38 @@ __device__ void align_wave(const SmallParams &p, const int32_t *lds_ids, uint32_
   if (lane == 0) *p.npp = (int32_t)total;
 }
 
+// Align of at most 64 pairs by one wave, in registers: lane i holds pair i
+// as the key (expert << 16 | i) and a bitonic sort across the wave puts the
+// pairs in expert order, ascending flat index inside an expert.  Each
+// expert's pairs are then a run of lanes: the rank is the distance to the
+// run's first lane (a prefix maximum), the run's last lane knows the count
+// and adds the padded size to a prefix sum that gives every run its offset.
+// sorted_token_ids already holds the sentinel everywhere (pre-fill), so only
+// the pairs, the blocks' experts and npp are written.
+__device__ void align_wave64(const SmallParams &p, const int32_t *lds_ids) {
+  const int lane = threadIdx.x & 63;
+  const int n = p.M * p.S, sh = p.log2A;
+  const uint32_t amask = (1u << sh) - 1u, none = 0xFFFFFFFFu;
+  uint32_t key = none;
+  if (lane < n) {
+    const int32_t e = lds_ids[lane];
+    if (e >= 0 && e < p.Ep) key = ((uint32_t)e << 16) | (uint32_t)lane;
+  }
+  key = wave_sort_asc_u32(key, lane);
+  const bool valid = key != none;
+  const uint32_t e = key >> 16;  // 0xFFFF for the empty lanes at the end
+  const bool head = valid && (wave_shr1_u32(key, none) >> 16) != e;
+  const bool last = valid && (wave_shl1_u32(key, none) >> 16) != e;
+  const uint32_t rank = (uint32_t)(lane - wave_incl_max_i32(head ? lane : 0, lane));
+  const uint32_t P = last ? ((rank + 1u + amask) & ~amask) : 0u;
+  const uint32_t incl = wave_incl_scan_u32(P, lane);
+  const uint32_t off = incl - P;  // sum of the padded sizes of the earlier runs
+  if (valid && off + rank < (uint64_t)p.sorted_cap) p.sorted[off + rank] = (int32_t)(key & 0xFFFFu);
+  if (last)
+    for (uint32_t b = off >> sh; b < ((off + P) >> sh) && b < (uint64_t)p.expert_cap; ++b) p.expert_ids[b] = (int32_t)e;
+  if (lane == 0) *p.npp = (int32_t)__builtin_amdgcn_readlane(incl, 63);
+}
+
 template <int RPB, int MAXM, int NK>
 __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
   constexpr int WPR = (kThreads / kWave) / RPB;  // waves per gate row
@@ -278,7 +310,10 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
     __shared__ uint32_t offl[kWave * NK];
     __shared__ int32_t mark[kMaxSmallBlocks];
     __syncthreads();
-    if (wave == 0) align_wave<NK>(p, lds_ids, bm, offl, mark);
+    if (wave == 0) {
+      if (p.M * p.S <= kWave) align_wave64(p, lds_ids);
+      else align_wave<NK>(p, lds_ids, bm, offl, mark);
+    }
   }
 }
 
