@@ -66,7 +66,7 @@ int64_t tight_capacity(int64_t n, int64_t Ep, int64_t A) {
 struct Layout {
   size_t counters = 0, keys = 0, shared = 0;  // small-M route
   size_t counts = 0, ranks = 0;               // standalone align
-  size_t part = 0, c16 = 0;                   // prefill route (split-K partials, tile counters)
+  size_t part = 0, tcnt = 0;                   // prefill route (split-K partials, tile counters)
   size_t total = 0;
 };
 
@@ -92,7 +92,7 @@ Layout layout_for(int64_t M, int64_t E, int64_t k, int64_t sh) {
   int64_t rows = (mr::kMfmaMaxGrid / (NE > 0 ? NE : 1)) * (M < 128 ? M : 128);
   if (rows < M) rows = M;
   L.part = take(o, (size_t)(rows * Epad) * 4);
-  L.c16 = take(o, (size_t)(NT * ((Ep + 15) / 16 * 4)) * 4);
+  L.tcnt = take(o, (size_t)(NT * ((Ep + 3) / 4 * 4)) * 4);
   L.total = o;
   return L;
 }
@@ -216,8 +216,8 @@ int route_impl(const char *fn, const void *x, const void *gate_w, const void *sh
     q.xcd_map = (grid % 8 == 0) ? 1 : 0;
     q.Epad = (E + 3) / 4 * 4;
     q.part = reinterpret_cast<float *>(wsb + L.part);
-    q.c16 = reinterpret_cast<uint32_t *>(wsb + L.c16);
-    q.c16_row = (int)((Ep + 15) / 16 * 4);
+    q.tcnt = reinterpret_cast<uint32_t *>(wsb + L.tcnt);
+    q.tcnt_row = (int)((Ep + 3) / 4 * 4);
     q.zero16 = reinterpret_cast<const uint4 *>(ctr + mr::kCtrZero16);
     q.ctr = ctr;
     int tpb = 1;

@@ -187,8 +187,9 @@ __device__ __forceinline__ void sort_desc_u32(uint32_t (&a)[N]) {
 // every key unique or zero): round j takes the wave-wide maximum of the
 // lanes' heads, lane j keeps it, and the lane that held it drops its head.
 // Returns lane j's key for j < k (0 elsewhere).  Every lane must be active.
+// Modifies a[].
 template <int N>
-__device__ __forceinline__ uint32_t topk_sorted_u32(uint32_t (&a)[N], int k, int lane) {
+__device__ __forceinline__ uint32_t topk_full_u32(uint32_t (&a)[N], int k, int lane) {
   uint32_t mine = 0u;
   for (int j = 0; j < k; ++j) {
     const uint32_t top = wave_max_all_u32(a[0]);
@@ -204,27 +205,90 @@ __device__ __forceinline__ uint32_t topk_sorted_u32(uint32_t (&a)[N], int k, int
   return mine;
 }
 
+// Keys per lane that the fast selection rounds shift.
+constexpr int kHotKeys = 4;
+
+// Same result as topk_full_u32 (a[] is left as it was): the rounds shift
+// only the first kHotKeys keys of each list, since one lane rarely holds
+// more than a few of the k largest.  If some lane gave up all of them, its
+// later keys were never offered, and the rounds are redone on the full
+// lists.
+template <int N>
+__device__ __forceinline__ uint32_t topk_sorted_u32(uint32_t (&a)[N], int k, int lane) {
+  if constexpr (N <= kHotKeys) {
+    uint32_t f[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) f[i] = a[i];
+    return topk_full_u32(f, k, lane);
+  } else {
+    uint32_t h[kHotKeys];
+#pragma unroll
+    for (int i = 0; i < kHotKeys; ++i) h[i] = a[i];
+    uint32_t mine = 0u, pops = 0u;
+    for (int j = 0; j < k; ++j) {
+      const uint32_t top = wave_max_all_u32(h[0]);
+      mine = (lane == j) ? top : mine;
+      const bool taken = h[0] == top;
+      pops += taken ? 1u : 0u;
+      const uint32_t keep = taken ? 0u : 0xFFFFFFFFu;
+#pragma unroll
+      for (int i = 0; i + 1 < kHotKeys; ++i) h[i] = min(h[i], h[i + 1] | keep);
+      h[kHotKeys - 1] &= keep;
+    }
+    if (__builtin_amdgcn_ballot_w64(pops >= (uint32_t)kHotKeys) == 0) return mine;
+    uint32_t f[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) f[i] = a[i];
+    return topk_full_u32(f, k, lane);
+  }
+}
+
 // topk_sorted_u32 for two independent lists at once: the two dependency
 // chains interleave, so two selections take little longer than one.
 template <int N>
 __device__ __forceinline__ void topk_sorted2_u32(uint32_t (&a)[N], uint32_t (&b)[N], int k, int lane,
                                                  uint32_t &mine_a, uint32_t &mine_b) {
+  constexpr int H = N < kHotKeys ? N : kHotKeys;
+  uint32_t ha[H], hb[H];
+#pragma unroll
+  for (int i = 0; i < H; ++i) {
+    ha[i] = a[i];
+    hb[i] = b[i];
+  }
   mine_a = 0u;
   mine_b = 0u;
+  uint32_t pa = 0u, pb = 0u;
   for (int j = 0; j < k; ++j) {
-    const uint32_t ta = wave_max_all_u32(a[0]);
-    const uint32_t tb = wave_max_all_u32(b[0]);
+    const uint32_t ta = wave_max_all_u32(ha[0]);
+    const uint32_t tb = wave_max_all_u32(hb[0]);
     mine_a = (lane == j) ? ta : mine_a;
     mine_b = (lane == j) ? tb : mine_b;
-    const uint32_t keep_a = (uint32_t)(a[0] != ta) * 0xFFFFFFFFu;
-    const uint32_t keep_b = (uint32_t)(b[0] != tb) * 0xFFFFFFFFu;
+    const bool xa = ha[0] == ta, xb = hb[0] == tb;
+    pa += xa ? 1u : 0u;
+    pb += xb ? 1u : 0u;
+    const uint32_t keep_a = xa ? 0u : 0xFFFFFFFFu;
+    const uint32_t keep_b = xb ? 0u : 0xFFFFFFFFu;
 #pragma unroll
-    for (int i = 0; i + 1 < N; ++i) {
-      a[i] = min(a[i], a[i + 1] | keep_a);
-      b[i] = min(b[i], b[i + 1] | keep_b);
+    for (int i = 0; i + 1 < H; ++i) {
+      ha[i] = min(ha[i], ha[i + 1] | keep_a);
+      hb[i] = min(hb[i], hb[i + 1] | keep_b);
     }
-    a[N - 1] &= keep_a;
-    b[N - 1] &= keep_b;
+    ha[H - 1] &= keep_a;
+    hb[H - 1] &= keep_b;
+  }
+  if constexpr (N > kHotKeys) {
+    if (__builtin_amdgcn_ballot_w64(pa >= (uint32_t)kHotKeys) != 0) {
+      uint32_t f[N];
+#pragma unroll
+      for (int i = 0; i < N; ++i) f[i] = a[i];
+      mine_a = topk_full_u32(f, k, lane);
+    }
+    if (__builtin_amdgcn_ballot_w64(pb >= (uint32_t)kHotKeys) != 0) {
+      uint32_t f[N];
+#pragma unroll
+      for (int i = 0; i < N; ++i) f[i] = b[i];
+      mine_b = topk_full_u32(f, k, lane);
+    }
   }
 }
 

@@ -101,8 +101,8 @@ struct MfmaParams {
   int xcd_map;   // deal items to XCDs (grid % 8 == 0)
   int Epad;      // row stride of the partials (E rounded up to 4)
   float *part;   // [SK, M, Epad] fp32 gate partials
-  uint32_t *c16;        // [NT, c16_row] words: pairs per (128-token tile, expert), a byte each
-  int c16_row;          // words per c16 row: ceil(Ep / 16) * 4
+  uint32_t *tcnt;       // [NT, tcnt_row]: pairs per (128-token tile, expert)
+  int tcnt_row;         // words per tcnt row: Ep rounded up to 4
   const uint4 *zero16;  // 16 zero bytes (stands in for k past H): kCtrZero16 of the counters
   uint32_t *ctr;        // counter words
   int tpb, ngroups;     // tokens per top-k group (power of two <= 128) and groups

@@ -43,7 +43,7 @@
 // Workspace: the counter words as the library leaves them (the grid
 // barriers use one of two counter sets by the parity of a launch count; each
 // launch clears the other set and block 0 advances the count at the end);
-// the tile counters (one byte per expert and 128-token tile) are cleared
+// the tile counters (one word per expert and 128-token tile) are cleared
 // during phase G.
 #include "device_common.h"
 #include "kernels.h"
@@ -451,7 +451,7 @@ __device__ void topk_group(const MfmaParams &p, int32_t *own, const float *sh, u
       p.wts[(size_t)m * S + lane] = w;
       own[(m - t0) * S + lane] = id;
       if (p.do_align && lane < k)
-        __hip_atomic_fetch_add(p.c16 + (size_t)(m >> 7) * p.c16_row + (id >> 2), 1u << (8 * (id & 3)),
+        __hip_atomic_fetch_add(p.tcnt + (size_t)(m >> 7) * p.tcnt_row + id, 1u,
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   };
@@ -526,7 +526,7 @@ static_assert(kTabOff < kRingBytes && kTabWords >= 4096, "phase A layout");
 __device__ uint32_t align_group(const MfmaParams &p, int g, const int32_t *own, uint8_t *smem,
                                 uint32_t *scan_tmp) {
   const int tid = threadIdx.x;
-  const int M = p.M, E = p.E, Ep = p.Ep, S = p.S, W = p.c16_row, NT = p.NT;
+  const int M = p.M, E = p.E, Ep = p.Ep, S = p.S, W = p.tcnt_row, NT = p.NT;
   uint32_t *mask = reinterpret_cast<uint32_t *>(smem + kMaskOff);
   uint32_t *tot = reinterpret_cast<uint32_t *>(smem + kArrOff);
   uint32_t *pre = tot + kArrWords, *off = pre + kArrWords, *hist = off + kArrWords;
@@ -549,13 +549,13 @@ __device__ uint32_t align_group(const MfmaParams &p, int g, const int32_t *own, 
 #pragma unroll
   for (int u = 0; u < 8; ++u) pv[u] = prev[min(u * kThreads + tid, max(nprev - 1, 0))];
   __syncthreads();
-  // column sums of the counter table, a slab of tiles at a time: one byte
-  // per expert, c16_row words per tile
+  // column sums of the counter table (one word per expert, tcnt_row words
+  // per tile), a slab of tiles at a time
   const int R = kTabWords / W > 0 ? kTabWords / W : 1;
   for (int r0 = 0; r0 < NT; r0 += R) {
     const int nr = min(R, NT - r0);
     const int nchunk = nr * W / 4;
-    const u32x4_coh *src = reinterpret_cast<const u32x4_coh *>(p.c16 + (size_t)r0 * W);
+    const u32x4_coh *src = reinterpret_cast<const u32x4_coh *>(p.tcnt + (size_t)r0 * W);
     u32x4_coh *dst = reinterpret_cast<u32x4_coh *>(tab);
     for (int c0 = 0; c0 < nchunk; c0 += kThreads * 16) {
       const u32x4_coh *a[16];
@@ -573,14 +573,13 @@ __device__ uint32_t align_group(const MfmaParams &p, int g, const int32_t *own, 
     __syncthreads();
     for (int e = tid; e < E; e += kThreads) {
       uint32_t t = tot[e], q = pre[e];
-      const int sh = 8 * (e & 3);
       for (int i0 = 0; i0 < nr; i0 += 8) {  // 8 rows' reads issued before their sums
         uint32_t w[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) w[u] = tab[min(i0 + u, nr - 1) * W + (e >> 2)];
+        for (int u = 0; u < 8; ++u) w[u] = tab[min(i0 + u, nr - 1) * W + e];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const uint32_t c = (i0 + u < nr) ? (w[u] >> sh) & 0xFFu : 0u;
+          const uint32_t c = (i0 + u < nr) ? w[u] : 0u;
           t += c;
           q += (r0 + i0 + u < tile) ? c : 0u;
         }
@@ -668,8 +667,8 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(MfmaParams p) {
   // the tile counters start from zero in every launch (the workspace layout
   // moves with M, so nothing else may be assumed about this region)
   if (p.do_align && !p.logits_only)
-    for (int i = b * kThreads + threadIdx.x; i < p.NT * p.c16_row; i += (int)grid * kThreads)
-      __hip_atomic_fetch_and(p.c16 + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = b * kThreads + threadIdx.x; i < p.NT * p.tcnt_row; i += (int)grid * kThreads)
+      __hip_atomic_fetch_and(p.tcnt + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int per_xcd = p.xcd_map ? (int)grid / 8 : 0;
   // the shared logits of this block's first token group need no other
   // block's data: they are computed during the first item's load latency
@@ -694,7 +693,7 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(MfmaParams p) {
     const int lane = threadIdx.x & 63, m0 = b * p.tpb;
     const int tstart = (m0 >> 7) << 7;
     if (threadIdx.x < 64) {
-      const uint32_t *a = reinterpret_cast<const uint32_t *>(p.c16);
+      const uint32_t *a = reinterpret_cast<const uint32_t *>(p.tcnt);
       if (lane < p.SK) a = reinterpret_cast<const uint32_t *>(p.part + ((size_t)lane * p.M + m0) * p.Epad);
       else if (lane == p.SK + 1 && p.ids) a = reinterpret_cast<const uint32_t *>(p.ids + (size_t)tstart * p.S);
       else if (lane == p.SK + 2 && p.ids) a = reinterpret_cast<const uint32_t *>(p.ids + (size_t)m0 * p.S);

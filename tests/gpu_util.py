@@ -33,3 +33,29 @@ def logits_gpu(d, ws=None):
     if ws is None:
         ws = mr.new_workspace(M, E, 1, s is not None)
     return mr.mr_debug_gate_logits(x, w, s, workspace=ws).cpu().numpy()
+
+
+def lane_heavy_inputs(M, E, H, favored, seed, alt=None):
+    """Exactly representable inputs (integers in [-3, 3] times 2^-4) whose
+    largest routed logits sit on chosen experts: x[m, 0] = 1 and
+    w[e, 0] = 16 for e in `favored` (0 for the other experts), so those
+    experts lead every row by far.  With `alt`, tokens m with (m // 4) odd
+    use column 1 and the experts in `alt` instead.  The selection rounds see
+    the favored experts together when they share a lane of the wave that
+    holds a token's keys."""
+    from moe_token_routing_amd import workloads
+
+    rng = np.random.default_rng(seed)
+    x = rng.integers(-3, 4, size=(M, H)).astype(np.float64) * 2.0 ** -4
+    w = rng.integers(-3, 4, size=(E, H)).astype(np.float64) * 2.0 ** -4
+    ws = rng.integers(-3, 4, size=H).astype(np.float64) * 2.0 ** -4
+    x[:, :2] = 0.0
+    w[:, :2] = 0.0
+    ws[:2] = 0.0
+    odd = (np.arange(M) // 4) % 2 == 1 if alt is not None else np.zeros(M, dtype=bool)
+    x[~odd, 0] = 1.0
+    x[odd, 1] = 1.0
+    w[list(favored), 0] = 16.0
+    if alt is not None:
+        w[list(alt), 1] = 16.0
+    return {"x": workloads.to_bf16_bits(x), "w": workloads.to_bf16_bits(w), "ws": workloads.to_bf16_bits(ws)}

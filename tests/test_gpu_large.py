@@ -7,7 +7,7 @@ import pytest
 import oracle
 from moe_token_routing_amd import workloads
 from parity_util import check_align, check_backstop, check_ids_random, check_weights, same_rounding_rows
-from gpu_util import logits_gpu, route_align_gpu, to_dev
+from gpu_util import lane_heavy_inputs, logits_gpu, route_align_gpu, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -108,6 +108,20 @@ def test_large_shapes(E, k, H, shared, M, scale):
     _say("shape", E, k, H, shared, M, scale)
     d = workloads.make_inputs(M, E, H, shared, "normal", seed=E * 7 + k)
     _run(d, k, scale)
+
+
+@pytest.mark.parametrize("M,pairs", [(64, False), (1100, True)])
+def test_selection_one_lane_holds_many_large(M, pairs):
+    """Eight chosen experts (2l, 2l + 1 + 128 j for l = 0) share lane 0 of
+    the top-k wave: the rounds over each lane's first keys run out and the
+    full rounds take over.  At M = 1100 a wave selects two tokens at once,
+    and only the first of each pair has the crowded lane (the second favours
+    ten experts in ten different lanes)."""
+    _say("lane-heavy", M, pairs)
+    fav = [0, 1, 128, 129, 256, 257, 384, 385]
+    alt = [10, 30, 50, 70, 90, 110, 150, 170, 190, 210] if pairs else None
+    d = lane_heavy_inputs(M, 512, 512, fav, seed=60 + M, alt=alt)
+    _run(d, 10, exact=True)
 
 
 def test_exact_large_alignment_variants():

@@ -6,7 +6,7 @@ import pytest
 import oracle
 from moe_token_routing_amd import workloads
 from parity_util import check_align, check_backstop, check_ids_random, check_weights, same_rounding_rows
-from gpu_util import logits_gpu, route_align_gpu, to_dev
+from gpu_util import lane_heavy_inputs, logits_gpu, route_align_gpu, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -45,6 +45,16 @@ def _run_and_check(d, k, scale, A=None, exact=False):
         check_weights(g["topk_weights"], g["topk_ids"], ref["weights"], ref["ids"], same)
     check_align(g["topk_ids"], E + has_shared, A, g["sorted_token_ids"], g["expert_ids"], g["npp"][0])
     return exempt
+
+
+@pytest.mark.parametrize("M", [4, 16])
+def test_selection_one_lane_holds_many(M):
+    """Six of the chosen experts (0, 64, ..., 320) sit in lane 0 of the wave
+    that selects a row's top-k, so the rounds over each lane's first keys
+    run out in that lane and the selection is redone on the full lists."""
+    _say("lane-heavy", M)
+    d = lane_heavy_inputs(M, 512, 4096, [0, 64, 128, 192, 256, 320], seed=40 + M)
+    _run_and_check(d, 10, 1.0, exact=True)
 
 
 def test_exact_inputs_m8_bit_exact():
