@@ -507,8 +507,9 @@ constexpr int kMaskWords = (kMaxRouteExperts + 1) * 4;
 constexpr int kArrOff = kMaskOff + kMaskWords * 4;      // tot, pre, off, hist: per expert
 constexpr int kArrWords = kMaxRouteExperts + 4;
 constexpr int kTabOff = (kArrOff + 4 * kArrWords * 4 + 1023) & ~1023;
-constexpr int kTabWords = (kRingBytes - kTabOff) / 4;   // tile-counter slab
-static_assert(kTabOff < kRingBytes && kTabWords >= 4096, "phase A layout");
+constexpr int kSlabLoads = 16;                          // 16-byte loads per thread per slab
+constexpr int kSlabWords = kSlabLoads * kThreads * 4;   // tile-counter slab
+static_assert(kTabOff + kSlabWords * 4 <= kRingBytes, "phase A layout");
 
 // Places the pairs of token group g (own[] holds its ids) into
 // sorted_token_ids and leaves, for every expert e, tot[e] (pairs over all
@@ -535,70 +536,48 @@ __device__ uint32_t align_group(const MfmaParams &p, int g, const int32_t *own, 
   const int t0 = has ? g * p.tpb : 0, t1 = has ? min(M, t0 + p.tpb) : 0;
   const int tile = t0 >> 7, tstart = tile << 7;
   const int nmw = (p.tpb + 31) >> 5;  // mask words per expert
-  for (int e = tid; e < Ep; e += kThreads) {
-    tot[e] = (e < E) ? 0u : (uint32_t)M;  // the shared expert takes every token
-    pre[e] = 0u;
-    hist[e] = 0u;
-    for (int w = 0; w < nmw; ++w) mask[e * nmw + w] = 0u;
-  }
-  // routed pairs of the tile's tokens before the group (contiguous in
-  // topk_ids): the first 8 per thread are loaded now, beside the table
+  // Loads first: the routed ids of the tile's tokens before the group
+  // (contiguous in topk_ids; 8 per thread now, any rest later), then the
+  // first slab of the counter table (one word per expert, tcnt_row words
+  // per tile).  The histogram of the earlier ids and the masks of the own
+  // tokens are built while the table is in flight.
   const int nprev = (t0 - tstart) * S;
   const uint32_t *prev = reinterpret_cast<const uint32_t *>(p.ids + (size_t)tstart * S);
   uint32_t pv[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) pv[u] = prev[min(u * kThreads + tid, max(nprev - 1, 0))];
-  __syncthreads();
-  // column sums of the counter table (one word per expert, tcnt_row words
-  // per tile), a slab of tiles at a time
-  const int R = kTabWords / W > 0 ? kTabWords / W : 1;
-  for (int r0 = 0; r0 < NT; r0 += R) {
-    const int nr = min(R, NT - r0);
-    const int nchunk = nr * W / 4;
+  const int R = max(1, kSlabWords / W);  // tiles per slab
+  u32x4_coh v[kSlabLoads];
+  auto load_slab = [&](int r0) {
+    const int nchunk = min(R, NT - r0) * W / 4;
     const u32x4_coh *src = reinterpret_cast<const u32x4_coh *>(p.tcnt + (size_t)r0 * W);
+#pragma unroll
+    for (int u = 0; u < kSlabLoads; ++u)
+      if (u * kThreads < nchunk) v[u] = src[min(u * kThreads + tid, nchunk - 1)];
+  };
+  auto store_slab = [&](int r0) {
+    const int nchunk = min(R, NT - r0) * W / 4;
     u32x4_coh *dst = reinterpret_cast<u32x4_coh *>(tab);
-    for (int c0 = 0; c0 < nchunk; c0 += kThreads * 16) {
-      const u32x4_coh *a[16];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) a[u] = src + min(c0 + u * kThreads + tid, nchunk - 1);
-      u32x4_coh v[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) v[u] = *a[u];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int c = c0 + u * kThreads + tid;
-        if (c < nchunk) dst[c] = v[u];
-      }
-    }
-    __syncthreads();
-    for (int e = tid; e < E; e += kThreads) {
-      uint32_t t = tot[e], q = pre[e];
-      for (int i0 = 0; i0 < nr; i0 += 8) {  // 8 rows' reads issued before their sums
-        uint32_t w[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) w[u] = tab[min(i0 + u, nr - 1) * W + e];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const uint32_t c = (i0 + u < nr) ? w[u] : 0u;
-          t += c;
-          q += (r0 + i0 + u < tile) ? c : 0u;
-        }
-      }
-      tot[e] = t;
-      pre[e] = q;
-    }
-    __syncthreads();
+    for (int u = 0; u < kSlabLoads; ++u)
+      if (u * kThreads + tid < nchunk) dst[u * kThreads + tid] = v[u];
+  };
+  load_slab(0);
+  for (int e = tid; e < Ep; e += kThreads) {
+    hist[e] = 0u;
+    for (int w = 0; w < nmw; ++w) mask[e * nmw + w] = 0u;
   }
+  __syncthreads();
 #pragma unroll
   for (int u = 0; u < 8; ++u)
     if (u * kThreads + tid < nprev && pv[u] < (uint32_t)E) atomicAdd(hist + pv[u], 1u);
   for (int i0 = 8 * kThreads; i0 < nprev; i0 += 8 * kThreads) {
-    uint32_t v[8];
+    uint32_t w[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = prev[min(i0 + u * kThreads + tid, nprev - 1)];
+    for (int u = 0; u < 8; ++u) w[u] = prev[min(i0 + u * kThreads + tid, nprev - 1)];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      if (i0 + u * kThreads + tid < nprev && v[u] < (uint32_t)E) atomicAdd(hist + v[u], 1u);
+      if (i0 + u * kThreads + tid < nprev && w[u] < (uint32_t)E) atomicAdd(hist + w[u], 1u);
   }
   const int npairs = (t1 - t0) * S;
   for (int i = tid; i < npairs; i += kThreads) {
@@ -608,21 +587,65 @@ __device__ uint32_t align_group(const MfmaParams &p, int g, const int32_t *own, 
       atomicOr(mask + e * nmw + (tok >> 5), 1u << (tok & 31));
     }
   }
+  // column sums: tot over every tile, pre over the tiles before the
+  // group's; a thread keeps its experts' sums in registers across slabs
+  constexpr int kEPT = (kMaxRouteExperts + kThreads - 1) / kThreads;
+  uint32_t st[kEPT], sq[kEPT];
+#pragma unroll
+  for (int j = 0; j < kEPT; ++j) st[j] = sq[j] = 0u;
+  for (int r0 = 0; r0 < NT; r0 += R) {
+    if (r0) load_slab(r0);
+    store_slab(r0);
+    __syncthreads();
+    const int nr = min(R, NT - r0);
+#pragma unroll
+    for (int j = 0; j < kEPT; ++j) {
+      const int e = tid + j * kThreads;
+      if (e < E) {
+        const uint32_t *col = tab + e;
+        for (int i0 = 0; i0 < nr; i0 += 16) {  // 16 rows' reads issued before their sums
+          uint32_t w[16];
+#pragma unroll
+          for (int u = 0; u < 16; ++u) w[u] = col[min(i0 + u, nr - 1) * W];
+#pragma unroll
+          for (int u = 0; u < 16; ++u) {
+            const uint32_t c = (i0 + u < nr) ? w[u] : 0u;
+            st[j] += c;
+            sq[j] += (r0 + i0 + u < tile) ? c : 0u;
+          }
+        }
+      }
+    }
+    __syncthreads();  // the slab region is rewritten next
+  }
+#pragma unroll
+  for (int j = 0; j < kEPT; ++j) {
+    const int e = tid + j * kThreads;
+    if (e < E) {
+      tot[e] = st[j];
+      pre[e] = sq[j];
+    }
+  }
+  if (tid == 0 && Ep > E) tot[E] = (uint32_t)M;  // the shared expert takes every token
   __syncthreads();
   // padded offsets: each thread scans a run of q consecutive experts
   const uint32_t amask = (uint32_t)p.A - 1u;
+  constexpr int kRun = (kMaxRouteExperts + 1 + kThreads - 1) / kThreads;
   const int q = (Ep + kThreads - 1) / kThreads;
   const int e0 = tid * q;
-  uint32_t run = 0;
-  for (int j = 0; j < q; ++j)
-    if (e0 + j < Ep) run += (tot[e0 + j] + amask) & ~amask;
+  uint32_t P[kRun], run = 0;
+#pragma unroll
+  for (int j = 0; j < kRun; ++j) {
+    P[j] = (j < q && e0 + j < Ep) ? (tot[e0 + j] + amask) & ~amask : 0u;
+    run += P[j];
+  }
   uint32_t npp;
   uint32_t o = block_excl_scan_u32<kThreads>(run, scan_tmp, &npp);
-  for (int j = 0; j < q; ++j)
-    if (e0 + j < Ep) {
-      off[e0 + j] = o;
-      o += (tot[e0 + j] + amask) & ~amask;
-    }
+#pragma unroll
+  for (int j = 0; j < kRun; ++j) {
+    if (j < q && e0 + j < Ep) off[e0 + j] = o;
+    o += P[j];
+  }
   __syncthreads();
   for (int i = tid; i < npairs; i += kThreads) {
     const int32_t e = own[i];
