@@ -21,17 +21,17 @@
 //    2 x 2 grid of 64 x 64 wave tiles, each 2 x 2 v_mfma_f32_32x32x16_bf16
 //    tiles; the LDS reads of one 16-k step are issued before the MFMAs of
 //    the previous one.  Each item writes its fp32 partial tile, transposed
-//    through LDS into whole token rows, with write-through stores.  Before
-//    the barrier each block also dots its own tokens' rows with the shared
-//    gate row (no other block's data is needed for that).  Items are dealt so that the 32
-//    blocks of one XCD share a K split and half the token tiles: the operand
-//    working set of an XCD fits its 4 MB L2.
-// T. Top-k.  Block b owns token groups of tpb tokens; one wave per token sums
-//    the K-split partials in a fixed order (so the logits do not depend on
-//    which block finished first), builds the packed selection keys, takes k
-//    rounds of a wave-wide maximum, then the softmax, the shared slot and
-//    the stores.  Each routed pair also bumps a per-(128-token tile, expert)
-//    counter.
+//    through LDS into whole token rows, with write-through stores.  Items
+//    are dealt so that the 32 blocks of one XCD share a K split and half the
+//    token tiles: the operand working set of an XCD fits its 4 MB L2.
+// T. Top-k.  Block b owns token groups of tpb tokens; a wave takes two
+//    tokens at a time, sums their K-split partial rows straight from the
+//    16-byte loads in a fixed split order (so the logits do not depend on
+//    which block finished first), dots the two x rows with the shared gate
+//    row while those loads are in flight, builds the packed selection keys,
+//    takes k rounds of a wave-wide maximum, then the softmax, the shared
+//    slot and the stores.  Each routed pair also bumps a per-(128-token
+//    tile, expert) counter.
 // A. Align.  Every block turns the tile counters into padded expert offsets
 //    (block scan) and the prefix of earlier tiles, adds the counts of the
 //    earlier tokens of its own tile (read back from topk_ids, in the same
@@ -149,12 +149,7 @@ __device__ __forceinline__ void grid_barrier(uint32_t *ctr, uint32_t set, uint32
 
 // ------------------------------------------------------------- phase G ---
 
-__device__ void shared_logits(const MfmaParams &p, int t0, int t1, float *sh);
-
-// sh_out: when not null, the shared logits of tokens [sh_t0, sh_t1) are
-// computed into it while the item's first stages are in flight.
-__device__ void gate_item(const MfmaParams &p, uint8_t *smem, int et, int tt, int sp, float *sh_out, int sh_t0,
-                          int sh_t1) {
+__device__ void gate_item(const MfmaParams &p, uint8_t *smem, int et, int tt, int sp) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int M = p.M, H = p.H, E = p.E;
   const int st0 = sp * p.spp;
@@ -241,7 +236,6 @@ __device__ void gate_item(const MfmaParams &p, uint8_t *smem, int et, int tt, in
 
   const int npre = min(nst, kNS - 1);
   for (int st = 0; st < npre; ++st) issue(st);
-  if (sh_out) shared_logits(p, sh_t0, sh_t1, sh_out);  // registers only; overlaps the loads
   // Software pipeline over 16-k steps (4 per stage): the LDS reads of step
   // g + 1 are issued before the MFMAs of step g, so the two overlap.  Stage
   // boundaries sit between the MFMAs of a stage's third step and its last.
@@ -313,129 +307,108 @@ __device__ void gate_item(const MfmaParams &p, uint8_t *smem, int et, int tt, in
   __syncthreads();  // the tile region is the next item's ring
 }
 
-// Shared-expert logits of tokens [t0, t1) (t1 - t0 <= 128) into sh[]: x rows
-// dotted with the shared gate row in fp32, a fixed summation order.  x and
-// the gate rows are never written by the launch, so plain loads are fine.
-// Each wave takes tokens wave, wave + 4, ..., two at a time; a lane takes the
-// 16-byte chunks lane + 64 u of the rows, 8 chunks per batch, and the gate
-// chunks of a batch serve both tokens; all loads of a batch are issued before
-// its arithmetic.
-__device__ void shared_logits(const MfmaParams &p, int t0, int t1, float *sh) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  constexpr int kW = kThreads / kWave;
-  const int H = p.H, nch = H >> 3;  // 16-byte chunks per row
-  const uint4 *wrow = reinterpret_cast<const uint4 *>(p.ws_row);
-  for (int ma = t0 + wave; ma < t1; ma += 2 * kW) {
-    const bool two = ma + kW < t1;
-    const uint4 *xa = reinterpret_cast<const uint4 *>(p.x + (size_t)ma * H);
-    const uint4 *xb = reinterpret_cast<const uint4 *>(p.x + (size_t)(two ? ma + kW : ma) * H);
-    float acc_a[8], acc_b[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) acc_a[u] = acc_b[u] = 0.f;
-    for (int c0 = 0; c0 < nch; c0 += 64 * 8) {
-      uint4 wv[8], av[8], bv[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int c = min(c0 + 64 * u + lane, nch - 1);
-        wv[u] = wrow[c];
-        av[u] = xa[c];
-        bv[u] = xb[c];
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (c0 + 64 * u + lane < nch) {
-          acc_a[u] = dot8_bf16(av[u], wv[u], acc_a[u]);
-          acc_b[u] = dot8_bf16(bv[u], wv[u], acc_b[u]);
-        }
-    }
-    const float va = wave_sum_f32(((acc_a[0] + acc_a[1]) + (acc_a[2] + acc_a[3])) +
-                                  ((acc_a[4] + acc_a[5]) + (acc_a[6] + acc_a[7])));
-    const float vb = wave_sum_f32(((acc_b[0] + acc_b[1]) + (acc_b[2] + acc_b[3])) +
-                                  ((acc_b[4] + acc_b[5]) + (acc_b[6] + acc_b[7])));
-    if (lane == 0) {
-      sh[ma - t0] = va;
-      if (two) sh[ma + kW - t0] = vb;
-    }
-  }
-}
-
 // ------------------------------------------------------------- phase T ---
 
-constexpr int kWaveStage = 24576;  // LDS bytes per wave for staging partial rows (4 waves from 32 KB)
+// Shared-expert logits of tokens ma and mb: their x rows dotted with the
+// shared gate row in fp32, in a fixed summation order.  A lane takes the
+// 16-byte chunks lane + 64 u of the rows, 8 chunks per batch, and the gate
+// chunks of a batch serve both tokens; all loads of a batch are issued before
+// its arithmetic.  x and the gate rows are never written by the launch, so
+// plain loads are fine.  Returns wave-uniform values.
+__device__ float2 shared_pair(const MfmaParams &p, int ma, int mb) {
+  const int lane = threadIdx.x & 63;
+  const int H = p.H, nch = H >> 3;  // 16-byte chunks per row
+  const uint4 *wrow = reinterpret_cast<const uint4 *>(p.ws_row);
+  const uint4 *xa = reinterpret_cast<const uint4 *>(p.x + (size_t)ma * H);
+  const uint4 *xb = reinterpret_cast<const uint4 *>(p.x + (size_t)mb * H);
+  float acc_a[8], acc_b[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) acc_a[u] = acc_b[u] = 0.f;
+  for (int c0 = 0; c0 < nch; c0 += 64 * 8) {
+    uint4 wv[8], av[8], bv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = min(c0 + 64 * u + lane, nch - 1);
+      wv[u] = wrow[c];
+      av[u] = xa[c];
+      bv[u] = xb[c];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (c0 + 64 * u + lane < nch) {
+        acc_a[u] = dot8_bf16(av[u], wv[u], acc_a[u]);
+        acc_b[u] = dot8_bf16(bv[u], wv[u], acc_b[u]);
+      }
+  }
+  float2 r;
+  r.x = wave_sum_f32(((acc_a[0] + acc_a[1]) + (acc_a[2] + acc_a[3])) + ((acc_a[4] + acc_a[5]) + (acc_a[6] + acc_a[7])));
+  r.y = wave_sum_f32(((acc_b[0] + acc_b[1]) + (acc_b[2] + acc_b[3])) + ((acc_b[4] + acc_b[5]) + (acc_b[6] + acc_b[7])));
+  return r;
+}
 
-template <int NKP>  // pairs of experts per lane: E <= 128 * NKP
-__device__ void topk_group(const MfmaParams &p, int32_t *own, const float *sh, uint8_t *stage, int g) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+template <int NKP>  // E <= 128 * NKP
+__device__ void topk_group(const MfmaParams &p, int32_t *own, int g) {
+  constexpr int NCH = NKP >= 2 ? NKP / 2 : 1;  // 16-byte chunks of a partial row per lane
+  constexpr int NK = 4 * NCH;                  // keys per lane
+  constexpr int SB = 8 / NCH > 0 ? 8 / NCH : 1; // splits per batch of loads (<= 16 loads for two tokens)
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int M = p.M, E = p.E, k = p.k, S = p.S, SK = p.SK, Epad = p.Epad;
   const int t0 = g * p.tpb, t1 = min(M, t0 + p.tpb);
-  // This wave's tokens are t0 + wave + 4i, i < ntw, taken two at a time.  A
-  // pair's partial rows are staged in the wave's LDS slice, sc splits per
-  // batch of 16-byte loads, and summed in split order (the logits do not
-  // depend on timing).  Lanes past E read clamped in-bounds pairs and are
-  // masked when the keys are built.
-  const int ntw = (t1 - t0 > wave) ? (t1 - t0 - wave + 3) / 4 : 0;
   const int rowc = Epad >> 2;  // 16-byte chunks per partial row
-  float *wst = reinterpret_cast<float *>(stage + wave * kWaveStage);
-  const int sc = max(1, min(SK, kWaveStage / (2 * Epad * 4)));
-  // rows of tokens ma, mb for splits [s0, s0 + n) -> wst[tok][split][Epad]
-  auto stage_rows = [&](int ma, int mb, int s0, int n) {
-    const int nch = 2 * n * rowc;
-    const float inv_rowc = 1.0f / (float)rowc;
-    for (int c0 = 0; c0 < nch; c0 += 64 * 16) {
-      const u32x4_coh *a[16];
+  // Lane l holds experts 4c .. 4c + 3 of the chunks c = l + 64 j, j < NCH:
+  // the partial rows are summed straight from their 16-byte loads, in split
+  // order (the logits do not depend on which block finished first).  Lanes
+  // past the row read a clamped in-bounds chunk and are masked in the keys.
+  int chunk[NCH];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int c = min(c0 + 64 * u + lane, nch - 1);
-        // row = c / rowc (exact: the fractional part stays far from an integer)
-        const int row = (int)(((float)c + 0.5f) * inv_rowc);
-        const int q = c - row * rowc, tok = row >= n ? 1 : 0, sp = s0 + row - tok * n;
-        a[u] = reinterpret_cast<const u32x4_coh *>(p.part + ((size_t)sp * M + (tok ? mb : ma)) * Epad) + q;
-      }
-      u32x4_coh v[16];
+  for (int j = 0; j < NCH; ++j) chunk[j] = min(lane + 64 * j, rowc - 1);
+  // This wave's tokens are t0 + wave + 4i, taken two at a time.
+  const int ntw = (t1 - t0 > wave) ? (t1 - t0 - wave + 3) / 4 : 0;
+  auto sum_rows = [&](int ma, int mb, float (&za)[NK], float (&zb)[NK], float2 &shl) {
 #pragma unroll
-      for (int u = 0; u < 16; ++u) v[u] = *a[u];
+    for (int i = 0; i < NK; ++i) za[i] = zb[i] = 0.f;
+    for (int s0 = 0; s0 < SK; s0 += SB) {
+      u32x4_coh va[SB][NCH], vb[SB][NCH];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int c = c0 + 64 * u + lane;
-        if (c < nch) reinterpret_cast<u32x4_coh *>(wst)[c] = v[u];
-      }
-    }
-    wave_lds_sync();
-  };
-  auto add_rows = [&](int tok, int n, float (&z)[2 * NKP]) {
-    const float *rows = wst + (size_t)tok * n * Epad;
-    for (int u0 = 0; u0 < n; u0 += 4) {  // 4 splits' reads issued before their sums
-      float2 v[4][NKP];
+      for (int s = 0; s < SB; ++s) {
+        const int sp = min(s0 + s, SK - 1);
+        const u32x4_coh *ra = reinterpret_cast<const u32x4_coh *>(p.part + ((size_t)sp * M + ma) * Epad);
+        const u32x4_coh *rb = reinterpret_cast<const u32x4_coh *>(p.part + ((size_t)sp * M + mb) * Epad);
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int j = 0; j < NKP; ++j) {
-          const int e = min(2 * lane + 128 * j, Epad - 2);
-          v[u][j] = *reinterpret_cast<const float2 *>(rows + min(u0 + u, n - 1) * Epad + e);
+        for (int j = 0; j < NCH; ++j) {
+          va[s][j] = ra[chunk[j]];
+          vb[s][j] = rb[chunk[j]];
         }
+      }
+      // the shared logits' loads follow the first batch, so their latency
+      // overlaps it
+      if (s0 == 0) shl = p.has_shared ? shared_pair(p, ma, mb) : make_float2(0.f, 0.f);
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (u0 + u < n) {
+      for (int s = 0; s < SB; ++s)
+        if (s0 + s < SK) {
 #pragma unroll
-          for (int j = 0; j < NKP; ++j) {
-            z[2 * j] += v[u][j].x;
-            z[2 * j + 1] += v[u][j].y;
-          }
+          for (int j = 0; j < NCH; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              za[4 * j + i] += __uint_as_float(va[s][j][i]);
+              zb[4 * j + i] += __uint_as_float(vb[s][j][i]);
+            }
         }
     }
   };
-  auto token_keys = [&](const float (&z)[2 * NKP], uint32_t (&keys)[2 * NKP]) {
+  auto token_keys = [&](const float (&z)[NK], uint32_t (&keys)[NK]) {
 #pragma unroll
-    for (int j = 0; j < NKP; ++j) {
-      const int e = 2 * lane + 128 * j;
-      keys[2 * j] = e < E ? make_key(z[2 * j], (uint32_t)e) : 0u;
-      keys[2 * j + 1] = e + 1 < E ? make_key(z[2 * j + 1], (uint32_t)(e + 1)) : 0u;
-    }
+    for (int j = 0; j < NCH; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = 4 * (lane + 64 * j) + i;
+        keys[4 * j + i] = e < E ? make_key(z[4 * j + i], (uint32_t)e) : 0u;
+      }
     sort_desc_u32(keys);
   };
   // softmax over the chosen k, the shared slot, the stores
-  auto finish = [&](int m, uint32_t mine) {
-    const float sl = p.has_shared ? sh[m - t0] : 0.f;
+  auto finish = [&](int m, uint32_t mine, float sl) {
     const float r = key_value(mine);
     const float r0 = readlane_f32(r, 0);
     const float ex = (lane < k) ? expf(r - r0) : 0.0f;
@@ -458,40 +431,34 @@ __device__ void topk_group(const MfmaParams &p, int32_t *own, const float *sh, u
   for (int ti = 0; ti < ntw; ti += 2) {
     const bool two = ti + 1 < ntw;
     const int ma = t0 + wave + 4 * ti, mb = two ? ma + 4 : ma;
-    float za[2 * NKP], zb[2 * NKP];
-#pragma unroll
-    for (int j = 0; j < 2 * NKP; ++j) za[j] = zb[j] = 0.f;
-    for (int s0 = 0; s0 < SK; s0 += sc) {
-      const int n = min(sc, SK - s0);
-      stage_rows(ma, mb, s0, n);
-      add_rows(0, n, za);
-      add_rows(1, n, zb);
-      wave_lds_sync();  // the next batch overwrites the slice
-    }
+    float za[NK], zb[NK];
+    float2 shl;
+    sum_rows(ma, mb, za, zb, shl);
     if (p.logits_only) {
       for (int h = 0; h < (two ? 2 : 1); ++h) {
         const int m = h ? mb : ma;
-        const float(&z)[2 * NKP] = h ? zb : za;
+        const float(&z)[NK] = h ? zb : za;
 #pragma unroll
-        for (int j = 0; j < NKP; ++j) {
-          const int e = 2 * lane + 128 * j;
-          if (e < E) p.logits_out[(size_t)m * p.Ep + e] = z[2 * j];
-          if (e + 1 < E) p.logits_out[(size_t)m * p.Ep + e + 1] = z[2 * j + 1];
-        }
-        if (p.has_shared && lane == 0) p.logits_out[(size_t)m * p.Ep + E] = sh[m - t0];
+        for (int j = 0; j < NCH; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int e = 4 * (lane + 64 * j) + i;
+            if (e < E) p.logits_out[(size_t)m * p.Ep + e] = z[4 * j + i];
+          }
+        if (p.has_shared && lane == 0) p.logits_out[(size_t)m * p.Ep + E] = h ? shl.y : shl.x;
       }
       continue;
     }
-    uint32_t ka[2 * NKP], kb[2 * NKP];
+    uint32_t ka[NK], kb[NK];
     token_keys(za, ka);
     if (two) {
       token_keys(zb, kb);
       uint32_t mine_a, mine_b;  // the two selections interleave
       topk_sorted2_u32(ka, kb, k, lane, mine_a, mine_b);
-      finish(ma, mine_a);
-      finish(mb, mine_b);
+      finish(ma, mine_a, shl.x);
+      finish(mb, mine_b, shl.y);
     } else {
-      finish(ma, topk_sorted_u32(ka, k, lane));
+      finish(ma, topk_sorted_u32(ka, k, lane), shl.x);
     }
   }
 }
@@ -670,7 +637,6 @@ template <int NKP>
 __global__ __launch_bounds__(kThreads) void route_mfma_kernel(MfmaParams p) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   __shared__ uint32_t scan_tmp[kThreads / kWave + 1];
-  __shared__ float sh[128];  // shared-expert logits of the current token group
   const int b = blockIdx.x;
   const uint32_t grid = gridDim.x;
 
@@ -693,18 +659,12 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(MfmaParams p) {
     for (int i = b * kThreads + threadIdx.x; i < p.NT * p.tcnt_row; i += (int)grid * kThreads)
       __hip_atomic_fetch_and(p.tcnt + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int per_xcd = p.xcd_map ? (int)grid / 8 : 0;
-  // the shared logits of this block's first token group need no other
-  // block's data: they are computed during the first item's load latency
-  const int sh_t0 = b * p.tpb, sh_t1 = min(p.M, sh_t0 + p.tpb);
-  bool sh_pending = p.has_shared && b < p.ngroups;
   for (int it = 0;; ++it) {
     const int L = it * (int)grid + (p.xcd_map ? (b % 8) * per_xcd + b / 8 : b);
     if (L >= p.items) break;
     const int et = L % p.NE, tt = (L / p.NE) % p.NT, sp = L / (p.NE * p.NT);
-    gate_item(p, smem, et, tt, sp, sh_pending ? sh : nullptr, sh_t0, sh_t1);
-    sh_pending = false;
+    gate_item(p, smem, et, tt, sp);
   }
-  if (sh_pending) shared_logits(p, sh_t0, sh_t1, sh);
   // Touch the pages phases T and A read (this block's partial rows of every
   // split, the tile counters, its tile's ids) so that their address
   // translations are cached when those phases start; the latency overlaps
@@ -730,20 +690,13 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(MfmaParams p) {
 
   // ---- T: logits, top-k, weights ----------------------------------------
   // LDS from here on: this block's ids at the start (kept until phase A);
-  // phase T stages partial rows from 32 KB; phase A's arrays follow the ids
+  // phase A's arrays follow them
   int32_t *own = reinterpret_cast<int32_t *>(smem);
   const bool align = p.do_align && !p.logits_only;
   // A block owns more than one group only for M > 128 * grid; then `own`
   // holds one group at a time and is reloaded in phase A.
   const bool multi = (int)grid < p.ngroups;
-  for (int g = b; g < p.ngroups; g += grid) {
-    if (g != b && p.has_shared) {
-      __syncthreads();
-      shared_logits(p, g * p.tpb, min(p.M, g * p.tpb + p.tpb), sh);
-      __syncthreads();
-    }
-    topk_group<NKP>(p, own, sh, smem + 32768, g);
-  }
+  for (int g = b; g < p.ngroups; g += grid) topk_group<NKP>(p, own, g);
   if (align) {
     grid_barrier(p.ctr, set, 2, grid);
     uint32_t npp = 0;
