@@ -34,6 +34,7 @@ enum CounterIndex : int {
 };
 constexpr int kTicketLanes = 16;
 constexpr int kTicketLaneStride = 64;  // words (256 bytes); set s of lane r at word 64 + 64 r + 32 s
+constexpr int kReleaseWord = 8;        // words after a lane counter: its barrier release word
 constexpr size_t kCounterBytes = 256 + (size_t)kTicketLanes * kTicketLaneStride * 4;
 
 // Small-M fused route (+ align).

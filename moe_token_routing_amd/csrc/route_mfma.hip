@@ -113,13 +113,18 @@ __device__ __forceinline__ void wait_stages(int n) {
 // launch, on counter set `set` (zero at launch start): each block takes a
 // ticket on one of up to kTicketLanes first-level counters (256 bytes apart,
 // so arrivals do not serialise on one address); the arrival that completes a
-// lane bumps the set's top counter; everybody waits for the top counter to
-// reach gen * lanes.  Data written with st_agent (or agent-scope atomics)
-// before the barrier is visible to coherent loads (ld_agent, ld_coherent8)
-// after it.  The wait is bounded: if it gives up, the error word is set and
-// the block goes on.  Only thread 0's arguments matter.
+// lane takes a ticket on the set's top counter, and the one that completes
+// the top counter writes `gen` into every lane's release word.  A block
+// waits on its own lane's release word, so no address has more than
+// grid / kTicketLanes pollers.  Data written with st_agent (or agent-scope
+// atomics) before the barrier is visible to coherent loads (ld_agent,
+// ld_coherent8) after it.  The wait is bounded: if it gives up, the error
+// word is set and the block goes on.  Only thread 0's arguments matter.
 __device__ __forceinline__ uint32_t *barrier_lane(uint32_t *ctr, uint32_t set, uint32_t r) {
   return ctr + 64 + (size_t)r * kTicketLaneStride + 32 * set;
+}
+__device__ __forceinline__ uint32_t *barrier_release(uint32_t *ctr, uint32_t set, uint32_t r) {
+  return barrier_lane(ctr, set, r) + kReleaseWord;
 }
 __device__ __forceinline__ uint32_t *barrier_top(uint32_t *ctr, uint32_t set) {
   return ctr + (set ? kCtrBarTop1 : kCtrBarTop0);
@@ -131,12 +136,16 @@ __device__ __forceinline__ void grid_barrier(uint32_t *ctr, uint32_t set, uint32
     const uint32_t nl = grid < (uint32_t)kTicketLanes ? grid : (uint32_t)kTicketLanes;
     const uint32_t r = blockIdx.x % nl;
     const uint32_t in_lane = (grid - 1 - r) / nl + 1;
-    uint32_t *top = barrier_top(ctr, set);
     const uint32_t t = __hip_atomic_fetch_add(barrier_lane(ctr, set, r), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (t == gen * in_lane - 1) __hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t target = gen * nl;
+    if (t == gen * in_lane - 1) {
+      const uint32_t u = __hip_atomic_fetch_add(barrier_top(ctr, set), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (u == gen * nl - 1)
+        for (uint32_t l = 0; l < nl; ++l)
+          __hip_atomic_store(barrier_release(ctr, set, l), gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    uint32_t *rel = barrier_release(ctr, set, r);
     int it = 0;
-    while (__hip_atomic_load(top, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    while (__hip_atomic_load(rel, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < gen) {
       if (++it == kBarrierSpin) {
         __hip_atomic_store(ctr + kCtrError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
@@ -648,8 +657,12 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(MfmaParams p) {
   uint32_t set = 0;
   if (threadIdx.x == 0 || (b == 0 && threadIdx.x <= kTicketLanes)) set = ld_agent(p.ctr + kCtrEpoch) & 1u;
   if (b == 0 && threadIdx.x < kTicketLanes + 1) {
-    uint32_t *c = threadIdx.x < kTicketLanes ? barrier_lane(p.ctr, set ^ 1u, threadIdx.x) : barrier_top(p.ctr, set ^ 1u);
-    __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x < kTicketLanes) {
+      __hip_atomic_store(barrier_lane(p.ctr, set ^ 1u, threadIdx.x), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(barrier_release(p.ctr, set ^ 1u, threadIdx.x), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      __hip_atomic_store(barrier_top(p.ctr, set ^ 1u), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 
   // ---- G: gate partials -------------------------------------------------

@@ -31,13 +31,14 @@ def _counters_ready(ws):
     """Checks the counter words as a prefill launch leaves them and returns
     the launch count (word 16): every word is zero except that count and the
     grid-barrier counter set the last launch used (top word 0 or 32, lane
-    words 64 + 64 r + 32 set); the set the next launch takes is zero."""
+    words 64 + 64 r + 32 set and their release words 8 further); the set the
+    next launch takes is zero."""
     import torch
 
     c = ws[:4352].view(torch.int32).cpu().numpy().astype(np.int64)
     count = int(c[16])
     last = (count - 1) & 1
-    keep = {16, 32 * last} | {64 + 64 * r + 32 * last for r in range(16)}
+    keep = {16, 32 * last} | {64 + 64 * r + 32 * last + d for r in range(16) for d in (0, 8)}
     others = np.array([i for i in range(c.size) if i not in keep])
     assert not c[others].any(), np.nonzero(c[others])
     return count
