@@ -22,9 +22,14 @@
 //    tiles; the LDS reads of one 16-k step are issued before the MFMAs of
 //    the previous one.  Each item writes its fp32 partial tile, transposed
 //    through LDS into whole token rows, with write-through stores.  Items
-//    are dealt so that the 32 blocks of one XCD share a K split and half the
-//    token tiles: the operand working set of an XCD fits its 4 MB L2.
-// T. Top-k.  Block b owns token groups of tpb tokens; a wave takes two
+//    are numbered token tile first, then K split, then expert tile, and the
+//    blocks of one XCD (block b runs on XCD b mod 8 when the grid is a
+//    multiple of 8) take consecutive items: every split of a token tile is
+//    computed on one XCD, and the top-k phase reads those partial rows on
+//    the same XCD, from its L2.  Correctness does not depend on this
+//    placement: the partial rows are written through to memory.
+// T. Top-k.  Each block owns token groups of tpb tokens (numbered like its
+//    gate items, so they sit on the XCD that wrote them); a wave takes two
 //    tokens at a time, sums their K-split partial rows straight from the
 //    16-byte loads in a fixed split order (so the logits do not depend on
 //    which block finished first), dots the two x rows with the shared gate
@@ -672,12 +677,16 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(MfmaParams p) {
     for (int i = b * kThreads + threadIdx.x; i < p.NT * p.tcnt_row; i += (int)grid * kThreads)
       __hip_atomic_fetch_and(p.tcnt + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int per_xcd = p.xcd_map ? (int)grid / 8 : 0;
+  const int lmap = p.xcd_map ? (b % 8) * per_xcd + b / 8 : b;
   for (int it = 0;; ++it) {
-    const int L = it * (int)grid + (p.xcd_map ? (b % 8) * per_xcd + b / 8 : b);
+    const int L = it * (int)grid + lmap;
     if (L >= p.items) break;
-    const int et = L % p.NE, tt = (L / p.NE) % p.NT, sp = L / (p.NE * p.NT);
+    const int et = L % p.NE, sp = (L / p.NE) % p.SK, tt = L / (p.NE * p.SK);
     gate_item(p, smem, et, tt, sp);
   }
+  // phases T and A: block b takes token group lmap (+ grid, ...), so a
+  // group's partial rows were written by blocks of its own XCD
+  const int gb = lmap;
   // Touch the pages phases T and A read (this block's partial rows of every
   // split, the tile counters, its tile's ids) so that their address
   // translations are cached when those phases start; the latency overlaps
@@ -685,8 +694,8 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(MfmaParams p) {
   // lines must not be cached in L2 before their writers are done (phases T
   // and A read them with plain loads after the barriers), hence ld_agent.
   uint32_t touch = 0;
-  if (b < p.ngroups) {
-    const int lane = threadIdx.x & 63, m0 = b * p.tpb;
+  if (gb < p.ngroups) {
+    const int lane = threadIdx.x & 63, m0 = gb * p.tpb;
     const int tstart = (m0 >> 7) << 7;
     if (threadIdx.x < 64) {
       const uint32_t *a = reinterpret_cast<const uint32_t *>(p.tcnt);
@@ -709,14 +718,14 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(MfmaParams p) {
   // A block owns more than one group only for M > 128 * grid; then `own`
   // holds one group at a time and is reloaded in phase A.
   const bool multi = (int)grid < p.ngroups;
-  for (int g = b; g < p.ngroups; g += grid) topk_group<NKP>(p, own, g);
+  for (int g = gb; g < p.ngroups; g += grid) topk_group<NKP>(p, own, g);
   if (align) {
     grid_barrier(p.ctr, set, 2, grid);
     uint32_t npp = 0;
     if (!multi) {
-      npp = align_group(p, b, own, smem, scan_tmp);
+      npp = align_group(p, gb, own, smem, scan_tmp);
     } else {
-      for (int g = b; g < p.ngroups; g += grid) {
+      for (int g = gb; g < p.ngroups; g += grid) {
         const int t0 = g * p.tpb, t1 = min(p.M, t0 + p.tpb);
         __syncthreads();  // the previous group is placed
         for (int i = threadIdx.x; i < (t1 - t0) * p.S; i += kThreads) own[i] = ld_agent(p.ids + (size_t)t0 * p.S + i);
