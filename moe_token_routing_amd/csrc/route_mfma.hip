@@ -32,8 +32,11 @@
 //    gate items, so they sit on the XCD that wrote them); a wave takes two
 //    tokens at a time, sums their K-split partial rows straight from the
 //    16-byte loads in a fixed split order (so the logits do not depend on
-//    which block finished first), dots the two x rows with the shared gate
-//    row while those loads are in flight, builds the packed selection keys,
+//    which block finished first), takes the shared-expert logits (those of
+//    the block's first group are computed between its arrival at the first
+//    barrier and the barrier's release, from x and the shared gate row
+//    alone; a further group dots its two x rows with the shared gate row
+//    while its partial-row loads are in flight), builds the packed keys,
 //    takes k rounds of a wave-wide maximum, then the softmax, the shared
 //    slot and the stores.  Each routed pair also bumps a per-(128-token
 //    tile, expert) counter.
@@ -134,7 +137,10 @@ __device__ __forceinline__ uint32_t *barrier_release(uint32_t *ctr, uint32_t set
 __device__ __forceinline__ uint32_t *barrier_top(uint32_t *ctr, uint32_t set) {
   return ctr + (set ? kCtrBarTop1 : kCtrBarTop0);
 }
-__device__ __forceinline__ void grid_barrier(uint32_t *ctr, uint32_t set, uint32_t gen, uint32_t grid) {
+// The barrier is split: grid_arrive publishes this block's arrival, and
+// grid_wait returns once every block has arrived; work that needs no other
+// block's data can run between the two.
+__device__ __forceinline__ void grid_arrive(uint32_t *ctr, uint32_t set, uint32_t gen, uint32_t grid) {
   wait_own_stores();
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -148,7 +154,12 @@ __device__ __forceinline__ void grid_barrier(uint32_t *ctr, uint32_t set, uint32
         for (uint32_t l = 0; l < nl; ++l)
           __hip_atomic_store(barrier_release(ctr, set, l), gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    uint32_t *rel = barrier_release(ctr, set, r);
+  }
+}
+__device__ __forceinline__ void grid_wait(uint32_t *ctr, uint32_t set, uint32_t gen, uint32_t grid) {
+  if (threadIdx.x == 0) {
+    const uint32_t nl = grid < (uint32_t)kTicketLanes ? grid : (uint32_t)kTicketLanes;
+    uint32_t *rel = barrier_release(ctr, set, blockIdx.x % nl);
     int it = 0;
     while (__hip_atomic_load(rel, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < gen) {
       if (++it == kBarrierSpin) {
@@ -159,6 +170,10 @@ __device__ __forceinline__ void grid_barrier(uint32_t *ctr, uint32_t set, uint32
     }
   }
   __syncthreads();
+}
+__device__ __forceinline__ void grid_barrier(uint32_t *ctr, uint32_t set, uint32_t gen, uint32_t grid) {
+  grid_arrive(ctr, set, gen, grid);
+  grid_wait(ctr, set, gen, grid);
 }
 
 // ------------------------------------------------------------- phase G ---
@@ -361,8 +376,25 @@ __device__ float2 shared_pair(const MfmaParams &p, int ma, int mb) {
 }
 
 
+// Shared logits of the tokens [t0, t1) (t1 - t0 <= 128) into sh[m - t0]:
+// wave w takes the token pairs (t0 + w + 8 i, t0 + w + 8 i + 4), the pairs
+// phase T gives it.
+__device__ void shared_logits(const MfmaParams &p, int t0, int t1, float *sh) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int ma = t0 + wave; ma < t1; ma += 8) {
+    const int mb = ma + 4 < t1 ? ma + 4 : ma;
+    const float2 v = shared_pair(p, ma, mb);
+    if (lane == 0) {
+      sh[ma - t0] = v.x;
+      sh[mb - t0] = v.y;
+    }
+  }
+}
+
+// sh: the shared logits of group g's tokens when the caller computed them
+// already (else null).
 template <int NKP>  // E <= 128 * NKP
-__device__ void topk_group(const MfmaParams &p, int32_t *own, int g) {
+__device__ void topk_group(const MfmaParams &p, int32_t *own, int g, const float *sh) {
   constexpr int NCH = NKP >= 2 ? NKP / 2 : 1;  // 16-byte chunks of a partial row per lane
   constexpr int NK = 4 * NCH;                  // keys per lane
   constexpr int SB = 8 / NCH > 0 ? 8 / NCH : 1; // splits per batch of loads (<= 16 loads for two tokens)
@@ -397,7 +429,7 @@ __device__ void topk_group(const MfmaParams &p, int32_t *own, int g) {
       }
       // the shared logits' loads follow the first batch, so their latency
       // overlaps it
-      if (s0 == 0) shl = p.has_shared ? shared_pair(p, ma, mb) : make_float2(0.f, 0.f);
+      if (s0 == 0 && p.has_shared) shl = sh ? make_float2(sh[ma - t0], sh[mb - t0]) : shared_pair(p, ma, mb);
 #pragma unroll
       for (int s = 0; s < SB; ++s)
         if (s0 + s < SK) {
@@ -446,7 +478,7 @@ __device__ void topk_group(const MfmaParams &p, int32_t *own, int g) {
     const bool two = ti + 1 < ntw;
     const int ma = t0 + wave + 4 * ti, mb = two ? ma + 4 : ma;
     float za[NK], zb[NK];
-    float2 shl;
+    float2 shl = make_float2(0.f, 0.f);
     sum_rows(ma, mb, za, zb, shl);
     if (p.logits_only) {
       for (int h = 0; h < (two ? 2 : 1); ++h) {
@@ -651,6 +683,7 @@ template <int NKP>
 __global__ __launch_bounds__(kThreads) void route_mfma_kernel(MfmaParams p) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   __shared__ uint32_t scan_tmp[kThreads / kWave + 1];
+  __shared__ float sh_first[128];  // shared logits of the block's first token group
   const int b = blockIdx.x;
   const uint32_t grid = gridDim.x;
 
@@ -707,7 +740,11 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(MfmaParams p) {
       touch = ld_agent(a);
     }
   }
-  grid_barrier(p.ctr, set, 1, grid);
+  grid_arrive(p.ctr, set, 1, grid);
+  // The shared logits of the block's first token group need only x and the
+  // shared gate row: they are computed while the other blocks arrive.
+  if (p.has_shared && gb < p.ngroups) shared_logits(p, gb * p.tpb, min(p.M, gb * p.tpb + p.tpb), sh_first);
+  grid_wait(p.ctr, set, 1, grid);
   if (touch == 0xFFFFFFFFu && threadIdx.x == 1000) p.npp[0] = 0;  // never true
 
   // ---- T: logits, top-k, weights ----------------------------------------
@@ -718,7 +755,7 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(MfmaParams p) {
   // A block owns more than one group only for M > 128 * grid; then `own`
   // holds one group at a time and is reloaded in phase A.
   const bool multi = (int)grid < p.ngroups;
-  for (int g = gb; g < p.ngroups; g += grid) topk_group<NKP>(p, own, g);
+  for (int g = gb; g < p.ngroups; g += grid) topk_group<NKP>(p, own, g, (p.has_shared && g == gb) ? sh_first : nullptr);
   if (align) {
     grid_barrier(p.ctr, set, 2, grid);
     uint32_t npp = 0;
