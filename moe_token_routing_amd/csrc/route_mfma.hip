@@ -519,10 +519,9 @@ constexpr int kMaskOff = kOwnBytes;                     // per expert: 4 words o
 constexpr int kMaskWords = (kMaxRouteExperts + 1) * 4;
 constexpr int kArrOff = kMaskOff + kMaskWords * 4;      // tot, pre, off, hist: per expert
 constexpr int kArrWords = kMaxRouteExperts + 4;
-constexpr int kTabOff = (kArrOff + 4 * kArrWords * 4 + 1023) & ~1023;
-constexpr int kSlabLoads = 16;                          // 16-byte loads per thread per slab
-constexpr int kSlabWords = kSlabLoads * kThreads * 4;   // tile-counter slab
-static_assert(kTabOff + kSlabWords * 4 <= kRingBytes, "phase A layout");
+constexpr int kRowBatch = 16;                          // tile rows of the counter table per round of loads
+static_assert(kArrOff + 4 * kArrWords * 4 <= kRingBytes, "phase A layout");
+static_assert(kMaxRouteExperts <= 4 * kThreads, "one 4-expert column chunk per thread");
 
 // Places the pairs of token group g (own[] holds its ids) into
 // sorted_token_ids and leaves, for every expert e, tot[e] (pairs over all
@@ -544,14 +543,13 @@ __device__ uint32_t align_group(const MfmaParams &p, int g, const int32_t *own, 
   uint32_t *mask = reinterpret_cast<uint32_t *>(smem + kMaskOff);
   uint32_t *tot = reinterpret_cast<uint32_t *>(smem + kArrOff);
   uint32_t *pre = tot + kArrWords, *off = pre + kArrWords, *hist = off + kArrWords;
-  uint32_t *tab = reinterpret_cast<uint32_t *>(smem + kTabOff);
   const bool has = g < p.ngroups;
   const int t0 = has ? g * p.tpb : 0, t1 = has ? min(M, t0 + p.tpb) : 0;
   const int tile = t0 >> 7, tstart = tile << 7;
   const int nmw = (p.tpb + 31) >> 5;  // mask words per expert
   // Loads first: the routed ids of the tile's tokens before the group
   // (contiguous in topk_ids; 8 per thread now, any rest later), then the
-  // first slab of the counter table (one word per expert, tcnt_row words
+  // first rows of the counter table (one word per expert, tcnt_row words
   // per tile).  The histogram of the earlier ids and the masks of the own
   // tokens are built while the table is in flight.
   const int nprev = (t0 - tstart) * S;
@@ -559,23 +557,18 @@ __device__ uint32_t align_group(const MfmaParams &p, int g, const int32_t *own, 
   uint32_t pv[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) pv[u] = prev[min(u * kThreads + tid, max(nprev - 1, 0))];
-  const int R = max(1, kSlabWords / W);  // tiles per slab
-  u32x4_coh v[kSlabLoads];
-  auto load_slab = [&](int r0) {
-    const int nchunk = min(R, NT - r0) * W / 4;
-    const u32x4_coh *src = reinterpret_cast<const u32x4_coh *>(p.tcnt + (size_t)r0 * W);
+  // The counter table: thread t sums the column chunk of experts 4t .. 4t+3
+  // over every tile row (tot) and over the rows before the group's tile
+  // (pre), straight from 16-byte loads, kRowBatch rows per round.
+  const int ce = 4 * tid;
+  const bool has_c = ce < E;
+  u32x4_coh v[kRowBatch];
+  auto load_rows = [&](int r0) {
+    const u32x4_coh *src = reinterpret_cast<const u32x4_coh *>(p.tcnt + (size_t)r0 * W + (has_c ? ce : 0));
 #pragma unroll
-    for (int u = 0; u < kSlabLoads; ++u)
-      if (u * kThreads < nchunk) v[u] = src[min(u * kThreads + tid, nchunk - 1)];
+    for (int u = 0; u < kRowBatch; ++u) v[u] = src[(size_t)min(u, NT - 1 - r0) * (W / 4)];
   };
-  auto store_slab = [&](int r0) {
-    const int nchunk = min(R, NT - r0) * W / 4;
-    u32x4_coh *dst = reinterpret_cast<u32x4_coh *>(tab);
-#pragma unroll
-    for (int u = 0; u < kSlabLoads; ++u)
-      if (u * kThreads + tid < nchunk) dst[u * kThreads + tid] = v[u];
-  };
-  load_slab(0);
+  load_rows(0);
   for (int e = tid; e < Ep; e += kThreads) {
     hist[e] = 0u;
     for (int w = 0; w < nmw; ++w) mask[e * nmw + w] = 0u;
@@ -600,64 +593,45 @@ __device__ uint32_t align_group(const MfmaParams &p, int g, const int32_t *own, 
       atomicOr(mask + e * nmw + (tok >> 5), 1u << (tok & 31));
     }
   }
-  // column sums: tot over every tile, pre over the tiles before the
-  // group's; a thread keeps its experts' sums in registers across slabs
-  constexpr int kEPT = (kMaxRouteExperts + kThreads - 1) / kThreads;
-  uint32_t st[kEPT], sq[kEPT];
+  uint32_t tot4[4] = {0u, 0u, 0u, 0u}, pre4[4] = {0u, 0u, 0u, 0u};
+  for (int r0 = 0; r0 < NT; r0 += kRowBatch) {
+    if (r0) load_rows(r0);
 #pragma unroll
-  for (int j = 0; j < kEPT; ++j) st[j] = sq[j] = 0u;
-  for (int r0 = 0; r0 < NT; r0 += R) {
-    if (r0) load_slab(r0);
-    store_slab(r0);
-    __syncthreads();
-    const int nr = min(R, NT - r0);
+    for (int u = 0; u < kRowBatch; ++u)
+      if (r0 + u < NT) {
 #pragma unroll
-    for (int j = 0; j < kEPT; ++j) {
-      const int e = tid + j * kThreads;
-      if (e < E) {
-        const uint32_t *col = tab + e;
-        for (int i0 = 0; i0 < nr; i0 += 16) {  // 16 rows' reads issued before their sums
-          uint32_t w[16];
-#pragma unroll
-          for (int u = 0; u < 16; ++u) w[u] = col[min(i0 + u, nr - 1) * W];
-#pragma unroll
-          for (int u = 0; u < 16; ++u) {
-            const uint32_t c = (i0 + u < nr) ? w[u] : 0u;
-            st[j] += c;
-            sq[j] += (r0 + i0 + u < tile) ? c : 0u;
-          }
+        for (int j = 0; j < 4; ++j) {
+          tot4[j] += v[u][j];
+          pre4[j] += (r0 + u < tile) ? v[u][j] : 0u;
         }
       }
-    }
-    __syncthreads();  // the slab region is rewritten next
   }
-#pragma unroll
-  for (int j = 0; j < kEPT; ++j) {
-    const int e = tid + j * kThreads;
-    if (e < E) {
-      tot[e] = st[j];
-      pre[e] = sq[j];
-    }
-  }
-  if (tid == 0 && Ep > E) tot[E] = (uint32_t)M;  // the shared expert takes every token
-  __syncthreads();
-  // padded offsets: each thread scans a run of q consecutive experts
+  // padded offsets: thread t's run is its own 4 experts; the shared expert
+  // (id E, every token) comes after all routed experts
   const uint32_t amask = (uint32_t)p.A - 1u;
-  constexpr int kRun = (kMaxRouteExperts + 1 + kThreads - 1) / kThreads;
-  const int q = (Ep + kThreads - 1) / kThreads;
-  const int e0 = tid * q;
-  uint32_t P[kRun], run = 0;
+  uint32_t P[4], run = 0;
 #pragma unroll
-  for (int j = 0; j < kRun; ++j) {
-    P[j] = (j < q && e0 + j < Ep) ? (tot[e0 + j] + amask) & ~amask : 0u;
+  for (int j = 0; j < 4; ++j) {
+    P[j] = (has_c && ce + j < E) ? (tot4[j] + amask) & ~amask : 0u;
     run += P[j];
   }
-  uint32_t npp;
-  uint32_t o = block_excl_scan_u32<kThreads>(run, scan_tmp, &npp);
+  uint32_t routed;
+  uint32_t o = block_excl_scan_u32<kThreads>(run, scan_tmp, &routed);
 #pragma unroll
-  for (int j = 0; j < kRun; ++j) {
-    if (j < q && e0 + j < Ep) off[e0 + j] = o;
-    o += P[j];
+  for (int j = 0; j < 4; ++j)
+    if (has_c && ce + j < E) {
+      tot[ce + j] = tot4[j];
+      pre[ce + j] = pre4[j];
+      off[ce + j] = o;
+      o += P[j];
+    }
+  uint32_t npp = routed;
+  if (Ep > E) {
+    npp += ((uint32_t)M + amask) & ~amask;
+    if (tid == 0) {
+      tot[E] = (uint32_t)M;
+      off[E] = routed;
+    }
   }
   __syncthreads();
   for (int i = tid; i < npairs; i += kThreads) {
