@@ -14,11 +14,12 @@
 // Launch shape (one kernel):
 //   grid = ceil(E' / RPB) blocks of 256 threads; block b owns gate rows
 //   [b*RPB, b*RPB + RPB) of the E' = E + shared rows (the shared row is
-//   row E).  Each row is split over 4/RPB waves; a thread streams 16-byte
-//   chunks of its row (coalesced 128-bit non-temporal loads) and of the M
-//   token rows, all issued before any arithmetic, accumulating with
-//   v_dot2_f32_bf16.  Partial sums are reduced with DPP butterflies and across
-//   waves through LDS.
+//   row E), with RPB = 4, 2, 1 for M <= 4, 8, 16.  Thread t streams the
+//   16-byte chunks t, t + 256, ... of the block's gate rows (coalesced
+//   128-bit non-temporal loads) and the same chunks of the M token rows
+//   (each loaded once per block), all issued before any arithmetic, and
+//   accumulates RPB x M sums with v_dot2_f32_bf16.  The 16 sums per thread
+//   are reduced by a halving DPP butterfly and across waves through LDS.
 //
 // Hand-off (no ticket): every block writes, with write-through agent-scope
 //   stores, the 32-bit selection key of each routed logit -- the bf16 order
@@ -63,11 +64,100 @@ __device__ __forceinline__ uint32_t max_of(const uint32_t (&a)[N]) {
   return t[0];
 }
 
-// Tail, part 1: rows m = wave, wave+4, ...  Each lane holds NK keys (experts
+// Tail, part 1, token rows in pairs: wave w takes the token rows w, w+4,
+// w+8, ..., two at a time (w + 8i and w + 8i + 4) so that the two
+// selections interleave.  Each
+// lane holds NK keys per row (experts lane, lane+64, ...); a selection round
+// is a wave-wide maximum of the lanes' sorted heads, and the lane that held
+// it drops its head (keys are unique).
+template <int NK>
+__device__ void route_tail_rows2(const SmallParams &p, int32_t *lds_ids) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = p.E, k = p.k, S = p.S;
+  constexpr int kWaves = kThreads / kWave;
+  // softmax over the chosen k, the shared slot, the stores
+  auto finish = [&](int m, uint32_t mine, unsigned long long sv) {
+    const float r = key_value(mine);
+    const float r0 = readlane_f32(r, 0);
+    const float ex = (lane < k) ? expf(r - r0) : 0.0f;
+    const float den = wave_sum_f32(ex);
+    int32_t id = (int32_t)key_id(mine);
+    float w = ex / den;
+    if (p.has_shared && lane == k) {
+      const float s = __uint_as_float((uint32_t)sv);
+      id = E;
+      w = p.scale / (1.0f + expf(-s));
+    }
+    if (lane < S) {
+      p.ids[(size_t)m * S + lane] = id;
+      p.wts[(size_t)m * S + lane] = w;
+      lds_ids[m * S + lane] = id;
+    }
+  };
+  for (int ma = wave; ma < p.M; ma += 2 * kWaves) {
+    const int mb = ma + kWaves;
+    const bool two = mb < p.M;
+    const int mb_ = two ? mb : ma;
+    uint32_t *kra = p.keys + (size_t)ma * E, *krb = p.keys + (size_t)mb_ * E;
+    uint32_t ka[NK], kb[NK];
+    unsigned long long sa = 0, sb = 0;
+    // poll until every key of the row(s) (and their shared logits) has
+    // arrived; a single row is polled alone
+    for (int it = 0;; ++it) {
+      bool missing = false;
+#pragma unroll
+      for (int i = 0; i < NK; ++i) ka[i] = ld_agent(kra + min(lane + kWave * i, E - 1));
+      if (p.has_shared) sa = ld_agent(p.shared_logit + ma);
+      if (two) {
+#pragma unroll
+        for (int i = 0; i < NK; ++i) kb[i] = ld_agent(krb + min(lane + kWave * i, E - 1));
+        if (p.has_shared) sb = ld_agent(p.shared_logit + mb);
+        missing = p.has_shared && (sb >> 32) == 0;
+#pragma unroll
+        for (int i = 0; i < NK; ++i) missing |= (lane + kWave * i < E) && kb[i] == 0u;
+      }
+      missing |= p.has_shared && (sa >> 32) == 0;
+#pragma unroll
+      for (int i = 0; i < NK; ++i) missing |= (lane + kWave * i < E) && ka[i] == 0u;
+      if (__builtin_amdgcn_ballot_w64(missing) == 0) break;
+      if (it == kPollSpin) {
+        if (lane == 0) st_agent(p.ctr + kCtrError, 1u);
+        break;
+      }
+    }
+    // consume: mask lanes past E, re-zero the slots for the next launch
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      if (lane + kWave * i < E) {
+        st_agent(kra + lane + kWave * i, 0u);
+        if (two) st_agent(krb + lane + kWave * i, 0u);
+      } else {
+        ka[i] = 0u;
+        kb[i] = 0u;
+      }
+    }
+    if (p.has_shared && lane == 0) {
+      st_agent(p.shared_logit + ma, 0ull);
+      if (two) st_agent(p.shared_logit + mb, 0ull);
+    }
+    sort_desc_u32(ka);
+    if (two) {
+      sort_desc_u32(kb);
+      uint32_t mine_a, mine_b;
+      topk_sorted2_u32(ka, kb, k, lane, mine_a, mine_b);  // lane j < k: the j-th chosen key
+      finish(ma, mine_a, sa);
+      finish(mb, mine_b, sb);
+    } else {
+      finish(ma, topk_sorted_u32(ka, k, lane), sa);
+    }
+  }
+}
+
+// Tail, part 1, one token row at a time: rows m = wave, wave+4, ...  Each lane holds NK keys (experts
 // lane, lane+64, ...); a selection round is the lane maximum, a wave-wide
 // maximum, and clearing the one key equal to it (keys are unique).
 template <int NK>
-__device__ void route_tail_rows(const SmallParams &p, int32_t *lds_ids) {
+__device__ void route_tail_rows1(const SmallParams &p, int32_t *lds_ids) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = p.E, k = p.k, S = p.S;
   for (int m = wave; m < p.M; m += kThreads / kWave) {
@@ -218,13 +308,41 @@ __device__ void align_wave64(const SmallParams &p, const int32_t *lds_ids) {
   if (lane == 0) *p.npp = (int32_t)__builtin_amdgcn_readlane(incl, 63);
 }
 
-template <int RPB, int MAXM, int NK>
+// Value held by lane (lane ^ J) of a float (see xor_lane_u32).
+template <int J>
+__device__ __forceinline__ float xor_lane_f32(float v, int lane) {
+  return __uint_as_float(xor_lane_u32<J>(__float_as_uint(v), lane));
+}
+
+// One halving step of the butterfly below: lanes at distance J pair up, the
+// lane with bit J clear keeps the lower half of its N values and the other
+// the upper half, and each adds the partner's matching half to its own.
+template <int N, int J>
+__device__ __forceinline__ void halve(float (&v)[16], int lane) {
+  const bool upper = (lane & J) != 0;
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    const float lo = v[i], hi = v[i + N / 2];
+    const float keep = upper ? hi : lo, send = upper ? lo : hi;
+    v[i] = keep + xor_lane_f32<J>(send, lane);
+  }
+}
+
+// Gate layouts.  SHARED: thread t takes the 16-byte chunks t, t + 256, ...
+// of all RPB gate rows of the block, so each token chunk is loaded once per
+// block (RPB * MAXM = 16 sums per thread, reduced by a halving butterfly).
+// Otherwise each gate row is split over 4 / RPB waves and a thread streams
+// its share of one row against every token row (one sum per token, reduced
+// by wave sums).  Both leave thread tid < RPB * MAXM with the logit of gate
+// row row0 + tid / MAXM and token tid % MAXM (valid for tokens < M).
+template <int RPB, int MAXM, bool SHARED, int NK>
 __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
-  constexpr int WPR = (kThreads / kWave) / RPB;  // waves per gate row
-  __shared__ float red[kThreads / kWave][MAXM];
+  constexpr int V = RPB * MAXM;
+  constexpr int WPR = (kThreads / kWave) / RPB;  // waves per gate row (split layout)
+  static_assert(!SHARED || V == 16, "the butterfly reduces 16 sums per thread");
+  __shared__ float red[kThreads / kWave][SHARED ? 16 : MAXM];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int rloc = wave / WPR, sub = wave % WPR;
-  const int row = blockIdx.x * RPB + rloc;
+  const int row0 = blockIdx.x * RPB;
   const int H = p.H, M = p.M;
   const int nch = H >> 3;  // 16-byte chunks per row
 
@@ -235,76 +353,149 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
       st_agent(p.sorted + i, sentinel);
   }
 
-  // ---- gate: stream this wave's share of one gate row -----------------
-  // Each iteration first issues every load it needs -- the gate-row chunks
-  // (non-temporal: read once) and the same chunks of every token row -- and
-  // only then accumulates, so a thread has all its loads in flight at once.
-  float acc[MAXM];
+  if constexpr (SHARED) {
+    // ---- gate: the block's RPB gate rows against the M token rows ---------
+    // Thread t takes the 16-byte chunks t, t + 256, ... of every row, so each
+    // token chunk is loaded once per block and serves all RPB gate rows.  A
+    // batch issues all its loads (gate chunks non-temporal: read once) before
+    // any arithmetic.  Rows past E' reload row E'-1 and tokens past M reload
+    // token M-1; those sums are dropped.
+    float acc[V];
 #pragma unroll
-  for (int m = 0; m < MAXM; ++m) acc[m] = 0.0f;
-  if (row < p.Ep) {
-    const uint4 *wrow = reinterpret_cast<const uint4 *>(row < p.E ? p.w + (size_t)row * H : p.ws_row);
+    for (int i = 0; i < V; ++i) acc[i] = 0.0f;
+    const uint4 *wr[RPB];
+#pragma unroll
+    for (int r = 0; r < RPB; ++r) {
+      const int e = min(row0 + r, p.Ep - 1);
+      wr[r] = reinterpret_cast<const uint4 *>(e < p.E ? p.w + (size_t)e * H : p.ws_row);
+    }
     const uint4 *xb = reinterpret_cast<const uint4 *>(p.x);
-    constexpr int kChunks = 2 * RPB;             // chunks per thread per iteration (H = 4096: one iteration)
-    constexpr int kStride = WPR * kWave;         // threads sharing the row
-    constexpr int kRowsPerGroup = 16 / kChunks;  // token rows whose chunks are loaded together
-    int c0 = sub * kWave + lane;
-    for (; c0 + (kChunks - 1) * kStride < nch; c0 += kChunks * kStride) {
-      uint4 wv[kChunks];
+    constexpr int UB = (RPB + MAXM <= 8) ? 2 : 1;  // chunk positions per batch
+    for (int c0 = tid; c0 < nch; c0 += UB * kThreads) {
+      uint4 wv[UB][RPB], xv[UB][MAXM];
 #pragma unroll
-      for (int u = 0; u < kChunks; ++u) wv[u] = ld_stream_16(wrow + c0 + u * kStride);
+      for (int u = 0; u < UB; ++u) {
+        const int c = min(c0 + u * kThreads, nch - 1);
 #pragma unroll
-      for (int g = 0; g < MAXM; g += kRowsPerGroup) {
-        if (g < M) {
-          uint4 xv[kRowsPerGroup][kChunks];
+        for (int r = 0; r < RPB; ++r) wv[u][r] = ld_stream_16(wr[r] + c);
 #pragma unroll
-          for (int r = 0; r < kRowsPerGroup; ++r) {
-            const int m = min(g + r, M - 1);  // rows past M reload row M-1; their sums are dropped
+        for (int m = 0; m < MAXM; ++m) xv[u][m] = xb[(size_t)min(m, M - 1) * nch + c];
+      }
+      // branch-free (a selected sum for a chunk past the row), and fenced from
+      // the loads, so that all the batch's loads are issued together
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int u = 0; u < kChunks; ++u) xv[r][u] = xb[(size_t)m * nch + c0 + u * kStride];
+      for (int u = 0; u < UB; ++u) {
+        const bool in = c0 + u * kThreads < nch;
+#pragma unroll
+        for (int r = 0; r < RPB; ++r)
+#pragma unroll
+          for (int m = 0; m < MAXM; ++m) {
+            const float t = dot8_bf16(wv[u][r], xv[u][m], acc[r * MAXM + m]);
+            acc[r * MAXM + m] = in ? t : acc[r * MAXM + m];
           }
-#pragma unroll
-          for (int r = 0; r < kRowsPerGroup; ++r)
-#pragma unroll
-            for (int u = 0; u < kChunks; ++u) acc[g + r] = dot8_bf16(wv[u], xv[r][u], acc[g + r]);
-        }
       }
     }
-    for (; c0 < nch; c0 += kStride) {  // ragged tail: one chunk at a time
-      const uint4 wv = ld_stream_16(wrow + c0);
-#pragma unroll
-      for (int m = 0; m < MAXM; ++m)
-        if (m < M) acc[m] = dot8_bf16(wv, xb[(size_t)m * nch + c0], acc[m]);
+    // Wave totals of the 16 sums: four halving steps leave lane l with one sum
+    // over its 16-lane row (value index bitrev4(l & 15)), two full steps add
+    // the other rows.  A fixed tree: the result does not depend on timing.
+    halve<16, 1>(acc, lane);
+    halve<8, 2>(acc, lane);
+    halve<4, 4>(acc, lane);
+    halve<2, 8>(acc, lane);
+    float tot = acc[0];
+    tot += xor_lane_f32<16>(tot, lane);
+    tot += xor_lane_f32<32>(tot, lane);
+    if (lane < 16) {
+      const int idx = ((lane & 1) << 3) | ((lane & 2) << 1) | ((lane & 4) >> 1) | ((lane & 8) >> 3);
+      red[wave][idx] = tot;
     }
-  }
+    wait_own_stores();  // the pre-fill is complete before any key is published
+    __syncthreads();
+  } else {
+    const int rloc = wave / WPR, sub = wave % WPR;
+    const int row = row0 + rloc;
+    // ---- gate: stream this wave's share of one gate row -----------------
+    // Each iteration first issues every load it needs -- the gate-row chunks
+    // (non-temporal: read once) and the same chunks of every token row -- and
+    // only then accumulates, so a thread has all its loads in flight at once.
+    float acc[MAXM];
 #pragma unroll
-  for (int m = 0; m < MAXM; ++m) {
+    for (int m = 0; m < MAXM; ++m) acc[m] = 0.0f;
+    if (row < p.Ep) {
+      const uint4 *wrow = reinterpret_cast<const uint4 *>(row < p.E ? p.w + (size_t)row * H : p.ws_row);
+      const uint4 *xb = reinterpret_cast<const uint4 *>(p.x);
+      constexpr int kChunks = 2 * RPB;             // chunks per thread per iteration (H = 4096: one iteration)
+      constexpr int kStride = WPR * kWave;         // threads sharing the row
+      constexpr int kRowsPerGroup = 16 / kChunks;  // token rows whose chunks are loaded together
+      int c0 = sub * kWave + lane;
+      for (; c0 + (kChunks - 1) * kStride < nch; c0 += kChunks * kStride) {
+        uint4 wv[kChunks];
+#pragma unroll
+        for (int u = 0; u < kChunks; ++u) wv[u] = ld_stream_16(wrow + c0 + u * kStride);
+#pragma unroll
+        for (int g = 0; g < MAXM; g += kRowsPerGroup) {
+          if (g < M) {
+            uint4 xv[kRowsPerGroup][kChunks];
+#pragma unroll
+            for (int r = 0; r < kRowsPerGroup; ++r) {
+              const int m = min(g + r, M - 1);  // rows past M reload row M-1; their sums are dropped
+#pragma unroll
+              for (int u = 0; u < kChunks; ++u) xv[r][u] = xb[(size_t)m * nch + c0 + u * kStride];
+            }
+#pragma unroll
+            for (int r = 0; r < kRowsPerGroup; ++r)
+#pragma unroll
+              for (int u = 0; u < kChunks; ++u) acc[g + r] = dot8_bf16(wv[u], xv[r][u], acc[g + r]);
+          }
+        }
+      }
+      for (; c0 < nch; c0 += kStride) {  // ragged tail: one chunk at a time
+        const uint4 wv = ld_stream_16(wrow + c0);
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m)
+          if (m < M) acc[m] = dot8_bf16(wv, xb[(size_t)m * nch + c0], acc[m]);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) {
+      if (m < M) {
+        const float v = wave_sum_f32(acc[m]);
+        if (lane == 0) red[wave][m] = v;
+      }
+    }
+    wait_own_stores();  // the pre-fill is complete before any key is published
+    __syncthreads();
+  }
+  if (tid < V) {
+    const int r = tid / MAXM, m = tid % MAXM;
+    const int e = row0 + r;
+    float z;
+    if constexpr (SHARED) {
+      z = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+    } else {
+      z = 0.0f;
+#pragma unroll
+      for (int s = 0; s < WPR; ++s) z += red[r * WPR + s][m];
+    }
     if (m < M) {
-      const float v = wave_sum_f32(acc[m]);
-      if (lane == 0) red[wave][m] = v;
-    }
-  }
-  wait_own_stores();  // the pre-fill is complete before any key is published
-  __syncthreads();
-  if (tid < RPB * M) {
-    const int rl = tid / M, m = tid % M;
-    const int e = blockIdx.x * RPB + rl;
-    float z = 0.0f;
-#pragma unroll
-    for (int s = 0; s < WPR; ++s) z += red[rl * WPR + s][m];
-    if (p.logits_only) {
-      if (e < p.Ep) p.logits_out[(size_t)m * p.Ep + e] = z;
-    } else if (e < p.E) {
-      st_agent(p.keys + (size_t)m * p.E + e, make_key(z, (uint32_t)e));
-    } else if (e == p.E) {
-      st_agent(p.shared_logit + m, (1ull << 32) | __float_as_uint(z));
+      if (p.logits_only) {
+        if (e < p.Ep) p.logits_out[(size_t)m * p.Ep + e] = z;
+      } else if (e < p.E) {
+        st_agent(p.keys + (size_t)m * p.E + e, make_key(z, (uint32_t)e));
+      } else if (e == p.E && p.has_shared) {
+        st_agent(p.shared_logit + m, (1ull << 32) | __float_as_uint(z));
+      }
     }
   }
   if (p.logits_only || blockIdx.x != 0) return;
 
   // ---- block 0: the tail ---------------------------------------------------
   __shared__ int32_t lds_ids[MAXM * (kMaxTopK + 1)];
-  route_tail_rows<NK>(p, lds_ids);
+  // Token rows in pairs for 5 <= M <= 8 (measured faster there; at M <= 4
+  // a wave holds one row, and for M >= 9 one row at a time measured faster).
+  if constexpr (MAXM == 2 * (kThreads / kWave)) route_tail_rows2<NK>(p, lds_ids);
+  else route_tail_rows1<NK>(p, lds_ids);
   if (p.do_align) {
     __shared__ uint32_t bm[kWave * NK];
     __shared__ uint32_t offl[kWave * NK];
@@ -317,32 +508,32 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
   }
 }
 
-template <int RPB, int MAXM>
+template <int RPB, int MAXM, bool SHARED>
 hipError_t launch_nk(const SmallParams &p, hipStream_t stream) {
   const int grid = (p.Ep + RPB - 1) / RPB;
   const int nk = (p.E + kWave - 1) / kWave;
-  if (nk <= 2) route_small_kernel<RPB, MAXM, 2><<<grid, kThreads, 0, stream>>>(p);
-  else if (nk <= 4) route_small_kernel<RPB, MAXM, 4><<<grid, kThreads, 0, stream>>>(p);
-  else if (nk <= 8) route_small_kernel<RPB, MAXM, 8><<<grid, kThreads, 0, stream>>>(p);
-  else route_small_kernel<RPB, MAXM, 16><<<grid, kThreads, 0, stream>>>(p);
+  if (nk <= 2) route_small_kernel<RPB, MAXM, SHARED, 2><<<grid, kThreads, 0, stream>>>(p);
+  else if (nk <= 4) route_small_kernel<RPB, MAXM, SHARED, 4><<<grid, kThreads, 0, stream>>>(p);
+  else if (nk <= 8) route_small_kernel<RPB, MAXM, SHARED, 8><<<grid, kThreads, 0, stream>>>(p);
+  else route_small_kernel<RPB, MAXM, SHARED, 16><<<grid, kThreads, 0, stream>>>(p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 int small_rows_per_block(int Ep, int M) {
-  // Two gate rows per block at M <= 4 (257 blocks for 513 rows: a thread
-  // holds 4 row chunks and 4x4 token chunks); one row per block above that
-  // or for small E' (a thread then holds 2 row chunks and up to 8x2 token
-  // chunks per load group).
+  // Measured per token count at E' = 513, H = 4096: the shared-chunk layout
+  // (2 rows per block) is faster for 5 <= M <= 8; the row-split layout (2
+  // rows per block at M <= 4 and E' > 256, else 1) elsewhere.
+  if (M >= 5 && M <= 8) return 2;
   return (M <= 4 && Ep > 256) ? 2 : 1;
 }
 
 hipError_t launch_route_small(const SmallParams &p, hipStream_t stream) {
-  if (small_rows_per_block(p.Ep, p.M) == 2) return launch_nk<2, 4>(p, stream);
-  if (p.M <= 4) return launch_nk<1, 4>(p, stream);
-  if (p.M <= 8) return launch_nk<1, 8>(p, stream);
-  return launch_nk<1, 16>(p, stream);
+  if (p.M <= 4) return small_rows_per_block(p.Ep, p.M) == 2 ? launch_nk<2, 4, false>(p, stream)
+                                                            : launch_nk<1, 4, false>(p, stream);
+  if (p.M <= 8) return launch_nk<2, 8, true>(p, stream);
+  return launch_nk<1, 16, false>(p, stream);
 }
 
 }  // namespace mr
