@@ -209,6 +209,11 @@ int route_impl(const char *fn, const void *x, const void *gate_w, const void *sh
     int sk = grid / (q.NE * q.NT);
     if (sk < 1) sk = 1;
     if (sk > q.nstages) sk = q.nstages;
+    // at least 4 stages of 64 k per item: a split of one or two stages pays
+    // the item's fixed costs (first loads, partial-tile stores, one more
+    // partial row per token in the top-k phase) for too little work
+    // (measured at M = 17 .. 128; no change at M >= 512)
+    if (sk > q.nstages / 4) sk = q.nstages / 4 > 0 ? q.nstages / 4 : 1;
     q.spp = (q.nstages + sk - 1) / sk;
     q.SK = (q.nstages + q.spp - 1) / q.spp;
     q.items = q.NE * q.NT * q.SK;
