@@ -14,12 +14,14 @@
 // Launch shape (one kernel):
 //   grid = ceil(E' / RPB) blocks of 256 threads; block b owns gate rows
 //   [b*RPB, b*RPB + RPB) of the E' = E + shared rows (the shared row is
-//   row E), with RPB = 4, 2, 1 for M <= 4, 8, 16.  Thread t streams the
-//   16-byte chunks t, t + 256, ... of the block's gate rows (coalesced
-//   128-bit non-temporal loads) and the same chunks of the M token rows
-//   (each loaded once per block), all issued before any arithmetic, and
-//   accumulates RPB x M sums with v_dot2_f32_bf16.  The 16 sums per thread
-//   are reduced by a halving DPP butterfly and across waves through LDS.
+//   row E).  At M <= 4, RPB = 2 (E' > 256) and each row is split over the
+//   block's waves: a thread streams 16-byte chunks of its row (coalesced
+//   128-bit non-temporal loads) and the same chunks of every token row.  At
+//   M >= 5, RPB = 2 and thread t streams the chunks t, t + 256, ... of both
+//   gate rows and of the M token rows (each token chunk loaded once per
+//   block), and its 16 or 32 sums are reduced by a halving DPP butterfly.
+//   Either way all loads of a batch are issued before any arithmetic
+//   (v_dot2_f32_bf16), and partial sums meet across waves in LDS.
 //
 // Hand-off (no ticket): every block writes, with write-through agent-scope
 //   stores, the 32-bit selection key of each routed logit -- the bf16 order
@@ -32,12 +34,13 @@
 //   sentinel pre-fill of sorted_token_ids is issued first in every block and
 //   completed before that block's keys are written, so block 0 never races it.
 //
-// Tail (block 0): one wave per token row selects the top-k as k rounds of a
-//   wave-wide maximum over the packed keys (DPP within rows of 16, then
-//   gfx950's permlane16/32 swaps), then the softmax, shared slot and stores;
-//   then one wave aligns: LDS row bitmaps per expert give counts and stable
-//   ranks, one wave scan gives the padded offsets, each pair is scattered to
-//   offset + rank.
+// Tail (block 0): wave w takes token rows w, w+4, ... (two at a time, the
+//   selections interleaved, when it holds more than one) and selects the
+//   top-k as k rounds of a wave-wide maximum over the packed keys (DPP within
+//   rows of 16, then gfx950's permlane16/32 swaps), then the softmax, shared
+//   slot and stores; then one wave aligns: up to 64 pairs by a wave-wide
+//   bitonic sort in registers, more by LDS row bitmaps per expert (counts
+//   and stable ranks) and one wave scan for the padded offsets.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -317,8 +320,8 @@ __device__ __forceinline__ float xor_lane_f32(float v, int lane) {
 // One halving step of the butterfly below: lanes at distance J pair up, the
 // lane with bit J clear keeps the lower half of its N values and the other
 // the upper half, and each adds the partner's matching half to its own.
-template <int N, int J>
-__device__ __forceinline__ void halve(float (&v)[16], int lane) {
+template <int N, int J, int V>
+__device__ __forceinline__ void halve(float (&v)[V], int lane) {
   const bool upper = (lane & J) != 0;
 #pragma unroll
   for (int i = 0; i < N / 2; ++i) {
@@ -335,12 +338,33 @@ __device__ __forceinline__ void halve(float (&v)[16], int lane) {
 // its share of one row against every token row (one sum per token, reduced
 // by wave sums).  Both leave thread tid < RPB * MAXM with the logit of gate
 // row row0 + tid / MAXM and token tid % MAXM (valid for tokens < M).
+// Wave totals of V = 16 or 32 sums per lane: log2(V) halving steps leave
+// lane l with one sum over V lanes (value index bitrev(l mod V)), full steps
+// add the rest of the wave.  A fixed tree: the result does not depend on
+// timing.  Returns the total and sets idx to its value index.
+template <int V>
+__device__ __forceinline__ float wave_totals(float (&v)[V], int lane, int &idx) {
+  static_assert(V == 16 || V == 32, "16 or 32 sums per lane");
+  halve<V, 1>(v, lane);
+  halve<V / 2, 2>(v, lane);
+  halve<V / 4, 4>(v, lane);
+  halve<V / 8, 8>(v, lane);
+  if constexpr (V == 32) halve<2, 16>(v, lane);
+  float t = v[0];
+  if constexpr (V == 16) t += xor_lane_f32<16>(t, lane);
+  t += xor_lane_f32<32>(t, lane);
+  idx = 0;
+#pragma unroll
+  for (int b = 0; (1 << b) < V; ++b) idx |= ((lane >> b) & 1) << (__builtin_ctz(V) - 1 - b);
+  return t;
+}
+
 template <int RPB, int MAXM, bool SHARED, int NK>
 __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
   constexpr int V = RPB * MAXM;
   constexpr int WPR = (kThreads / kWave) / RPB;  // waves per gate row (split layout)
-  static_assert(!SHARED || V == 16, "the butterfly reduces 16 sums per thread");
-  __shared__ float red[kThreads / kWave][SHARED ? 16 : MAXM];
+  static_assert(!SHARED || V == 16 || V == 32, "the butterfly reduces 16 or 32 sums per thread");
+  __shared__ float red[kThreads / kWave][SHARED ? V : MAXM];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row0 = blockIdx.x * RPB;
   const int H = p.H, M = p.M;
@@ -370,7 +394,7 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
       wr[r] = reinterpret_cast<const uint4 *>(e < p.E ? p.w + (size_t)e * H : p.ws_row);
     }
     const uint4 *xb = reinterpret_cast<const uint4 *>(p.x);
-    constexpr int UB = (RPB + MAXM <= 8) ? 2 : 1;  // chunk positions per batch
+    constexpr int UB = (RPB + MAXM <= 18) ? 2 : 1;  // chunk positions per batch
     for (int c0 = tid; c0 < nch; c0 += UB * kThreads) {
       uint4 wv[UB][RPB], xv[UB][MAXM];
 #pragma unroll
@@ -396,20 +420,9 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
           }
       }
     }
-    // Wave totals of the 16 sums: four halving steps leave lane l with one sum
-    // over its 16-lane row (value index bitrev4(l & 15)), two full steps add
-    // the other rows.  A fixed tree: the result does not depend on timing.
-    halve<16, 1>(acc, lane);
-    halve<8, 2>(acc, lane);
-    halve<4, 4>(acc, lane);
-    halve<2, 8>(acc, lane);
-    float tot = acc[0];
-    tot += xor_lane_f32<16>(tot, lane);
-    tot += xor_lane_f32<32>(tot, lane);
-    if (lane < 16) {
-      const int idx = ((lane & 1) << 3) | ((lane & 2) << 1) | ((lane & 4) >> 1) | ((lane & 8) >> 3);
-      red[wave][idx] = tot;
-    }
+    int idx;
+    const float tot = wave_totals<V>(acc, lane, idx);
+    if (lane < V) red[wave][idx] = tot;
     wait_own_stores();  // the pre-fill is complete before any key is published
     __syncthreads();
   } else {
@@ -492,9 +505,8 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
 
   // ---- block 0: the tail ---------------------------------------------------
   __shared__ int32_t lds_ids[MAXM * (kMaxTopK + 1)];
-  // Token rows in pairs for 5 <= M <= 8 (measured faster there; at M <= 4
-  // a wave holds one row, and for M >= 9 one row at a time measured faster).
-  if constexpr (MAXM == 2 * (kThreads / kWave)) route_tail_rows2<NK>(p, lds_ids);
+  // Token rows in pairs when a wave holds more than one (M >= 5).
+  if constexpr (MAXM > kThreads / kWave) route_tail_rows2<NK>(p, lds_ids);
   else route_tail_rows1<NK>(p, lds_ids);
   if (p.do_align) {
     __shared__ uint32_t bm[kWave * NK];
@@ -523,17 +535,17 @@ hipError_t launch_nk(const SmallParams &p, hipStream_t stream) {
 
 int small_rows_per_block(int Ep, int M) {
   // Measured per token count at E' = 513, H = 4096: the shared-chunk layout
-  // (2 rows per block) is faster for 5 <= M <= 8; the row-split layout (2
-  // rows per block at M <= 4 and E' > 256, else 1) elsewhere.
-  if (M >= 5 && M <= 8) return 2;
-  return (M <= 4 && Ep > 256) ? 2 : 1;
+  // (2 rows per block, 16 or 32 sums per thread) is faster for M >= 5; the
+  // row-split layout (2 rows per block at E' > 256, else 1) for M <= 4.
+  if (M >= 5) return 2;
+  return Ep > 256 ? 2 : 1;
 }
 
 hipError_t launch_route_small(const SmallParams &p, hipStream_t stream) {
   if (p.M <= 4) return small_rows_per_block(p.Ep, p.M) == 2 ? launch_nk<2, 4, false>(p, stream)
                                                             : launch_nk<1, 4, false>(p, stream);
   if (p.M <= 8) return launch_nk<2, 8, true>(p, stream);
-  return launch_nk<1, 16, false>(p, stream);
+  return launch_nk<2, 16, true>(p, stream);
 }
 
 }  // namespace mr
