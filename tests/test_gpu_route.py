@@ -92,6 +92,8 @@ def test_router_sweep_small_m(M):
     (1024, 32, 512, True, 7, 0.5),
     (100, 7, 200, True, 9, 1.0),     # ragged: E and H not multiples of the wave
     (32, 32, 8, False, 3, 1.0),      # k = E: every expert chosen
+    (3, 2, 8, True, 12, 1.0),        # shared-chunk layout with one chunk per row, odd E'
+    (32, 32, 24, False, 6, 1.0),     # shared-chunk layout, k = E, H not a multiple of 64
 ])
 def test_router_shapes(E, k, H, shared, M, scale):
     _say("shape", E, k, H, shared, M, scale)
