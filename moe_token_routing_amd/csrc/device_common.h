@@ -77,8 +77,6 @@ constexpr int kRowMirror = 0x140;     // lane i <- lane 15-i within 16
 constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
 constexpr int kQuadRev = 0x1B;        // quad_perm [3,2,1,0]
 constexpr int kRowRor8 = 0x128;       // lane i <- lane (i + 8) mod 16 within 16: i ^ 8
-constexpr int kWaveShl1 = 0x130;      // lane i <- lane i + 1 (lane 63: `old`)
-constexpr int kWaveShr1 = 0x138;      // lane i <- lane i - 1 (lane 0: `old`)
 
 // Max over the 64 lanes; every lane must be active.  Returns a wave-uniform
 // value.
@@ -128,35 +126,6 @@ __device__ __forceinline__ uint32_t xor_lane_u32(uint32_t v, int lane) {
     const auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);
     return (lane & 32) ? a[0] : a[1];
   }
-}
-
-// One value per lane sorted ascending across the 64 lanes: Batcher's bitonic
-// network (merge stages K = 2 .. 64, each with half-cleaner steps J = K/2 ..
-// 1; 21 compare-exchanges).  Every lane must be active.
-template <int K, int J>
-__device__ __forceinline__ uint32_t bitonic_merge_u32(uint32_t v, int lane) {
-  const uint32_t q = xor_lane_u32<J>(v, lane);
-  const bool up = (lane & K) == 0, lower = (lane & J) == 0;
-  v = (lower == up) ? min(v, q) : max(v, q);
-  if constexpr (J > 1) return bitonic_merge_u32<K, J / 2>(v, lane);
-  else return v;
-}
-__device__ __forceinline__ uint32_t wave_sort_asc_u32(uint32_t v, int lane) {
-  v = bitonic_merge_u32<2, 1>(v, lane);
-  v = bitonic_merge_u32<4, 2>(v, lane);
-  v = bitonic_merge_u32<8, 4>(v, lane);
-  v = bitonic_merge_u32<16, 8>(v, lane);
-  v = bitonic_merge_u32<32, 16>(v, lane);
-  return bitonic_merge_u32<64, 32>(v, lane);
-}
-
-// Lane i receives lane i - 1 (shr) or lane i + 1 (shl); the end lane gets
-// `fill`.
-__device__ __forceinline__ uint32_t wave_shr1_u32(uint32_t v, uint32_t fill) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)fill, (int)v, kWaveShr1, 0xF, 0xF, false);
-}
-__device__ __forceinline__ uint32_t wave_shl1_u32(uint32_t v, uint32_t fill) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)fill, (int)v, kWaveShl1, 0xF, 0xF, false);
 }
 
 // Sorts N (a power of two) keys held in registers into descending order
@@ -324,25 +293,6 @@ __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v, int lane) {
   const uint32_t r2 = __builtin_amdgcn_readlane(v, 47);
   const int row = lane >> 4;
   v += (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
-  return v;
-}
-
-// Inclusive prefix maximum over the 64 lanes (signed); every lane active.
-__device__ __forceinline__ int32_t wave_incl_max_i32(int32_t v, int lane) {
-  auto shr = [](int32_t x, auto ctrl) {
-    return __builtin_amdgcn_update_dpp((int)0x80000000, x, decltype(ctrl)::value, 0xF, 0xF, false);
-  };
-  v = max(v, shr(v, std::integral_constant<int, kRowShr1>{}));
-  v = max(v, shr(v, std::integral_constant<int, kRowShr2>{}));
-  v = max(v, shr(v, std::integral_constant<int, kRowShr4>{}));
-  v = max(v, shr(v, std::integral_constant<int, kRowShr8>{}));
-  const int32_t r0 = __builtin_amdgcn_readlane(v, 15);
-  const int32_t r1 = __builtin_amdgcn_readlane(v, 31);
-  const int32_t r2 = __builtin_amdgcn_readlane(v, 47);
-  const int row = lane >> 4;
-  if (row >= 1) v = max(v, r0);
-  if (row >= 2) v = max(v, r1);
-  if (row >= 3) v = max(v, r2);
   return v;
 }
 

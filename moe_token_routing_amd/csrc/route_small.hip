@@ -38,9 +38,10 @@
 //   selections interleaved, when it holds more than one) and selects the
 //   top-k as k rounds of a wave-wide maximum over the packed keys (DPP within
 //   rows of 16, then gfx950's permlane16/32 swaps), then the softmax, shared
-//   slot and stores; then one wave aligns: up to 64 pairs by a wave-wide
-//   bitonic sort in registers, more by LDS row bitmaps per expert (counts
-//   and stable ranks) and one wave scan for the padded offsets.
+//   slot and stores; then one wave aligns: with M <= 16 <= A every touched
+//   expert takes exactly one block, so a bitmap of touched experts (block
+//   index = rank among them, one wave scan) and one of token rows per expert
+//   (slot in the block) place every pair.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -50,9 +51,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kPollSpin = 1 << 21;  // bound on block 0's polls (each is one memory round trip)
-// Most blocks an align of M <= 16 rows can produce: every pair alone in its
-// expert's block, at the smallest alignment (16).
-constexpr int kMaxSmallBlocks = kSmallMaxTokens * (kMaxTopK + 1);
+static_assert(kSmallMaxTokens <= 16, "the small-M align puts each expert's pairs (one per row) in one block of A >= 16 slots");
 
 // Max of N keys held in registers (a balanced tree, depth log2 N).
 template <int N>
@@ -209,106 +208,53 @@ __device__ void route_tail_rows1(const SmallParams &p, int32_t *lds_ids) {
   }
 }
 
-// Tail, part 2: align over the n = M*S pairs whose ids are in lds_ids, by
-// ONE wave (no block barriers; a wave's LDS operations complete in order, and
-// wave_lds_sync orders them for the compiler).  Every id in a row is distinct
-// (top-k ids plus the shared id E), so a 32-bit bitmap of rows per routed
-// expert gives both its count and each pair's stable rank.  Lane l owns the
-// NK consecutive routed experts [NK*l, NK*l + NK): a local prefix over them
-// plus one wave scan gives every padded offset in expert order.  The shared
-// expert (id E, the largest) holds every row once: its segment is rows
-// 0..M-1 in order, after all routed experts.
-template <int NK>
-__device__ void align_wave(const SmallParams &p, const int32_t *lds_ids, uint32_t *bm, uint32_t *offl,
-                           int32_t *mark) {
+// Tail, part 2: align of the n = M*S pairs in lds_ids by ONE wave (no
+// block barriers; wave_lds_sync orders the wave's LDS accesses for the
+// compiler).  Here M <= 16 <= A, and a token row holds an expert at most
+// once, so an expert's pairs always fit one block of A slots: every touched
+// expert pads to exactly A.  Its block index is its rank among the touched
+// experts (a bitmap over expert ids and one wave scan of the word
+// popcounts), and a pair's slot in the block is the number of earlier token
+// rows that chose the same expert (a bitmap of rows per expert), which keeps
+// ascending flat index inside the expert.  The shared expert (id E, every
+// row) is handled like the others and comes last.  Only the bitmap entries
+// the pairs touch are cleared first; the sentinel pre-fill already holds
+// every slot the pairs do not.
+__device__ void align_small(const SmallParams &p, const int32_t *lds_ids, uint32_t *rowbm, uint32_t *touched,
+                            uint32_t *pre) {
   const int lane = threadIdx.x & 63;
-  const int E = p.E, S = p.S, M = p.M, sh = p.log2A;
-  const uint32_t amask = (1u << sh) - 1u;
-  const int n = M * S;
-  const int e0 = NK * lane;
-#pragma unroll
-  for (int j = 0; j < NK; ++j) bm[e0 + j] = 0u;
-  wave_lds_sync();
+  const int n = p.M * p.S, Ep = p.Ep, sh = p.log2A;
+  const int words = (Ep + 31) >> 5;  // <= 33 for E' <= 1025: one wave scan covers them
+  for (int w = lane; w < words; w += kWave) touched[w] = 0u;
   for (int i = lane; i < n; i += kWave) {
     const int e = lds_ids[i];
-    if (e >= 0 && e < E) atomicOr(&bm[e], 1u << __umulhi((uint32_t)i, p.S_magic));
-  }
-  wave_lds_sync();
-  uint32_t P[NK], pre[NK], lane_total = 0;
-#pragma unroll
-  for (int j = 0; j < NK; ++j) {
-    P[j] = (__builtin_popcount(bm[e0 + j]) + amask) & ~amask;
-    pre[j] = lane_total;
-    lane_total += P[j];
-  }
-  const uint32_t incl = wave_incl_scan_u32(lane_total, lane);
-  const uint32_t base = incl - lane_total;
-  const uint32_t routed = __builtin_amdgcn_readlane(incl, 63);
-  const uint32_t P_sh = p.has_shared ? (((uint32_t)M + amask) & ~amask) : 0u;
-  const uint32_t total = routed + P_sh;
-  const uint32_t nblocks = min((uint64_t)(total >> sh), (uint64_t)p.expert_cap);
-  // expert_ids: expert ids grow with the block index, so block b's expert is
-  // the running maximum of the segment-start marks at or before b
-  for (uint32_t b = lane; b < nblocks; b += kWave) mark[b] = -1;
-  wave_lds_sync();
-#pragma unroll
-  for (int j = 0; j < NK; ++j) {
-    const uint32_t off = base + pre[j];
-    offl[e0 + j] = off;
-    if (P[j] != 0u) mark[off >> sh] = e0 + j;
-  }
-  if (p.has_shared && lane == 0 && P_sh != 0u) mark[routed >> sh] = E;
-  wave_lds_sync();
-  int32_t carry = -1;
-  for (uint32_t b0 = 0; b0 < nblocks; b0 += kWave) {
-    const uint32_t b = b0 + lane;
-    const int32_t v = wave_incl_max_i32(max(carry, b < nblocks ? mark[b] : -1), lane);
-    if (b < nblocks) p.expert_ids[b] = v;
-    carry = __builtin_amdgcn_readlane(v, 63);
+    if (e >= 0 && e < Ep) rowbm[e] = 0u;
   }
   wave_lds_sync();
   for (int i = lane; i < n; i += kWave) {
     const int e = lds_ids[i];
+    if (e >= 0 && e < Ep) {
+      atomicOr(&rowbm[e], 1u << __umulhi((uint32_t)i, p.S_magic));
+      atomicOr(&touched[e >> 5], 1u << (e & 31));
+    }
+  }
+  wave_lds_sync();
+  const uint32_t pc = lane < words ? __builtin_popcount(touched[lane]) : 0u;
+  const uint32_t incl = wave_incl_scan_u32(pc, lane);
+  if (lane < words) pre[lane] = incl - pc;
+  const uint32_t touched_experts = __builtin_amdgcn_readlane(incl, 63);
+  wave_lds_sync();
+  for (int i = lane; i < n; i += kWave) {
+    const int e = lds_ids[i];
+    if (e < 0 || e >= Ep) continue;
     const uint32_t m = __umulhi((uint32_t)i, p.S_magic);
-    uint32_t pos;
-    if (e >= 0 && e < E) pos = offl[e] + __builtin_popcount(bm[e] & ((1u << m) - 1u));
-    else if (p.has_shared && e == E) pos = routed + m;
-    else continue;
+    const uint32_t blk = pre[e >> 5] + __builtin_popcount(touched[e >> 5] & ((1u << (e & 31)) - 1u));
+    const uint32_t rank = __builtin_popcount(rowbm[e] & ((1u << m) - 1u));
+    const uint64_t pos = ((uint64_t)blk << sh) + rank;
     if (pos < (uint64_t)p.sorted_cap) p.sorted[pos] = i;
+    if (rank == 0 && blk < (uint64_t)p.expert_cap) p.expert_ids[blk] = e;
   }
-  if (lane == 0) *p.npp = (int32_t)total;
-}
-
-// Align of at most 64 pairs by one wave, in registers: lane i holds pair i
-// as the key (expert << 16 | i) and a bitonic sort across the wave puts the
-// pairs in expert order, ascending flat index inside an expert.  Each
-// expert's pairs are then a run of lanes: the rank is the distance to the
-// run's first lane (a prefix maximum), the run's last lane knows the count
-// and adds the padded size to a prefix sum that gives every run its offset.
-// sorted_token_ids already holds the sentinel everywhere (pre-fill), so only
-// the pairs, the blocks' experts and npp are written.
-__device__ void align_wave64(const SmallParams &p, const int32_t *lds_ids) {
-  const int lane = threadIdx.x & 63;
-  const int n = p.M * p.S, sh = p.log2A;
-  const uint32_t amask = (1u << sh) - 1u, none = 0xFFFFFFFFu;
-  uint32_t key = none;
-  if (lane < n) {
-    const int32_t e = lds_ids[lane];
-    if (e >= 0 && e < p.Ep) key = ((uint32_t)e << 16) | (uint32_t)lane;
-  }
-  key = wave_sort_asc_u32(key, lane);
-  const bool valid = key != none;
-  const uint32_t e = key >> 16;  // 0xFFFF for the empty lanes at the end
-  const bool head = valid && (wave_shr1_u32(key, none) >> 16) != e;
-  const bool last = valid && (wave_shl1_u32(key, none) >> 16) != e;
-  const uint32_t rank = (uint32_t)(lane - wave_incl_max_i32(head ? lane : 0, lane));
-  const uint32_t P = last ? ((rank + 1u + amask) & ~amask) : 0u;
-  const uint32_t incl = wave_incl_scan_u32(P, lane);
-  const uint32_t off = incl - P;  // sum of the padded sizes of the earlier runs
-  if (valid && off + rank < (uint64_t)p.sorted_cap) p.sorted[off + rank] = (int32_t)(key & 0xFFFFu);
-  if (last)
-    for (uint32_t b = off >> sh; b < ((off + P) >> sh) && b < (uint64_t)p.expert_cap; ++b) p.expert_ids[b] = (int32_t)e;
-  if (lane == 0) *p.npp = (int32_t)__builtin_amdgcn_readlane(incl, 63);
+  if (lane == 0) *p.npp = (int32_t)(touched_experts << sh);
 }
 
 // Value held by lane (lane ^ J) of a float (see xor_lane_u32).
@@ -509,14 +455,10 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
   if constexpr (MAXM > kThreads / kWave) route_tail_rows2<NK>(p, lds_ids);
   else route_tail_rows1<NK>(p, lds_ids);
   if (p.do_align) {
-    __shared__ uint32_t bm[kWave * NK];
-    __shared__ uint32_t offl[kWave * NK];
-    __shared__ int32_t mark[kMaxSmallBlocks];
+    __shared__ uint32_t rowbm[kWave * NK + 1];  // E' <= 64 NK + 1
+    __shared__ uint32_t touched[kMaxRouteExperts / 32 + 1], pre[kMaxRouteExperts / 32 + 1];
     __syncthreads();
-    if (wave == 0) {
-      if (p.M * p.S <= kWave) align_wave64(p, lds_ids);
-      else align_wave<NK>(p, lds_ids, bm, offl, mark);
-    }
+    if (wave == 0) align_small(p, lds_ids, rowbm, touched, pre);
   }
 }
 
