@@ -28,6 +28,8 @@ METRIC = "route+align µs/layer at M=4 (E=512,k=10); rows/s at M=2048; % HBM/MFM
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 ROTATE_BYTES = 512 << 20        # inputs rotated per replay
+FLUSH_BYTES = 512 << 20         # the fill before each call in the memset method
+SWEEP_M = (1, 2, 3, 4, 8, 9, 16, 40, 512, 2048)
 
 
 def parse():
@@ -35,7 +37,19 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=8192)
     ap.add_argument("--warmup", type=int, default=512)
-    ap.add_argument("--workload", default="m4", choices=["m4", "m2048", "c3", "c4"])
+    ap.add_argument("--workload", default="m4", choices=[f"m{m}" for m in SWEEP_M] + ["c3", "c4"],
+                    help="m<M>: E=512+1, H=4096, k=10 at M tokens (m4 is the headline); c3: E=128, H=2048, "
+                         "k=8, M=128; c4: the same at M=2048 with Zipf-skewed gate rows")
+    ap.add_argument("--align", type=int, default=None, choices=[64, 128],
+                    help="force the alignment A (default: the M-aware tier)")
+    ap.add_argument("--method", default="rotate", choices=["rotate", "memset"],
+                    help="rotate: graph replay over rotated inputs (default); memset: a 512 MB fill before "
+                         "each call, per-call time = (fills + calls) - (fills alone)")
+    ap.add_argument("--stream-read", action="store_true",
+                    help="time only the plain streaming-read kernel at 4 MiB and 512 MiB")
+    ap.add_argument("--cpu-only", action="store_true", help="time only the CPU oracle on the workload")
+    ap.add_argument("--cpu-threads", type=int, default=None,
+                    help="oracle threads (default: every host core, capped by OMP_NUM_THREADS)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall time spent timing the CPU oracle (0 disables)")
     ap.add_argument("--secondary-steps", type=int, default=1024,
@@ -48,8 +62,11 @@ def parse():
 def workload(name):
     from moe_token_routing_amd import workloads as W
 
-    return {"m4": W.ROUTER_E512_M4, "m2048": W.sweep_workload(2048), "c3": W.PREFILL_E128_M128,
-            "c4": W.PREFILL_E128_M2048_ZIPF}[name]
+    if name == "m4":
+        return W.ROUTER_E512_M4
+    if name.startswith("m"):
+        return W.sweep_workload(int(name[1:]))
+    return {"c3": W.PREFILL_E128_M128, "c4": W.PREFILL_E128_M2048_ZIPF}[name]
 
 
 def make_copies(wl, R, device):
@@ -88,28 +105,36 @@ def algorithmic_bytes(wl, npp, A):
     return read + write
 
 
-def cpu_baseline(d, wl, seconds):
+def cpu_baseline(d, wl, seconds, threads=None, A=None):
+    """The oracle as it stands, timed on the host: full route+align calls on
+    the workload's seeded input until `seconds` have passed (at least one);
+    the value is the median call."""
     import oracle
 
-    threads = os.cpu_count() or 1
-    if os.environ.get("OMP_NUM_THREADS", "").isdigit():
-        threads = max(1, min(threads, int(os.environ["OMP_NUM_THREADS"])))
-    n = 0
+    if threads is None:
+        threads = os.cpu_count() or 1
+        if os.environ.get("OMP_NUM_THREADS", "").isdigit():
+            threads = max(1, min(threads, int(os.environ["OMP_NUM_THREADS"])))
+    if A is None:
+        A = oracle.select_alignment(wl.M, wl.k, wl.E)
+    times = []
     t0 = time.perf_counter()
     while True:
+        t1 = time.perf_counter()
         r = oracle.route(d["x"], d["w"], d["ws"], wl.k, wl.scale, nthreads=threads)
-        oracle.align(r["ids"], wl.num_experts, oracle.select_alignment(wl.M, wl.k, wl.E))
-        n += 1
+        oracle.align(r["ids"], wl.num_experts, A)
+        times.append(time.perf_counter() - t1)
         if time.perf_counter() - t0 >= seconds:
             break
     dt = time.perf_counter() - t0
-    per = dt / n
+    per = sorted(times)[len(times) // 2]
     if wl.M >= 512:
         value, unit = wl.M / per, "rows/s"
     else:
         value, unit = per * 1e6, "us/layer"
-    return {"value": value, "unit": unit, "cores": threads, "kind": "oracle",
-            "sample": f"{n} full oracle route+align calls on the {wl.name} input (seed 0), {dt:.1f} s"}
+    return {"value": value, "unit": unit, "cores": threads, "kind": "oracle", "us_per_call": round(per * 1e6, 1),
+            "sample": f"median of {len(times)} full oracle route+align calls on the {wl.name} input (seed 0), "
+                      f"{dt:.1f} s"}
 
 
 def calibrate_copy():
@@ -158,7 +183,147 @@ def profiled_traffic(kernel, wl_name):
     return int(float(fields["hbm_bytes_per_launch"]))
 
 
-def measure(wl, steps, warmup):
+def result_fields(wl, A, ms_per_step, mean_npp, npps, steps, warmup, timing):
+    """The bench line's fields for one timed workload."""
+    for n in npps:
+        assert n % A == 0 and n > 0
+    nbytes = algorithmic_bytes(wl, mean_npp, A)
+    launch_s = ms_per_step * 1e-3
+    achieved_gbs = nbytes / launch_s / 1e9
+    flops = 2.0 * wl.M * (wl.E + int(wl.shared)) * wl.H
+    mfma_tflops = flops / launch_s / 1e12
+
+    if wl.M >= 512:
+        value, unit, hib = wl.M / launch_s, "rows/s", True
+    else:
+        value, unit, hib = ms_per_step * 1e3, "us/layer", False
+    hbm = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": None}
+    mfma = {"bound": "mfma", "achieved": round(mfma_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(mfma_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+    if wl.M >= 512 and flops / nbytes > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        roof = dict(mfma, hbm_frac=hbm["frac"])
+    else:
+        roof = dict(hbm, mfma_frac=mfma["frac"]) if wl.M >= 512 else hbm
+    roof["kernel"] = "route_small_kernel" if wl.M <= 16 else "route_mfma_kernel"
+    roof["traffic"] = profiled_traffic(roof["kernel"], wl.name)
+    roof["bytes_per_launch"] = int(nbytes)
+    roof["flops_per_launch"] = int(flops)
+    return {
+        "value": round(value, 3) if unit == "us/layer" else round(value, 1),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": hib,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "M": wl.M, "E": wl.E, "shared": wl.shared, "H": wl.H, "k": wl.k,
+                   "A": A, "timing": timing},
+        "roofline": roof,
+    }
+
+
+def measure_memset(wl, calls, reps, A=None):
+    """The pages' method: a 512 MB fill before every call evicts the L2s and
+    the memory-side cache, so each call reads its inputs from HBM.  Per call
+    = (replay of fill+call pairs - replay of the fills alone) / calls, the
+    medians over `reps` replays of each."""
+    import torch
+
+    import moe_token_routing_amd as mr
+
+    device = "cuda:0"
+    d, copies = make_copies(wl, 1, device)
+    x, w, s = copies[0]
+    if A is None:
+        A = mr.mr_select_alignment(wl.M, wl.k, wl.E)
+    ws = mr.new_workspace(wl.M, wl.E, wl.k, wl.shared, device=device)
+    o = mr.mr_route_align(x, w, s, wl.k, wl.scale, A, workspace=ws)
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device=device)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream(device=device)
+
+    def capture(with_call):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(calls):
+                flush.zero_()
+                if with_call:
+                    mr.mr_route_align(x, w, s, wl.k, wl.scale, A, workspace=ws, topk_ids=o["topk_ids"],
+                                      topk_weights=o["topk_weights"], sorted_token_ids=o["sorted_token_ids"],
+                                      expert_ids=o["expert_ids"], npp=o["npp"])
+        return g
+
+    graphs = {True: capture(True), False: capture(False)}
+    cur = torch.cuda.current_stream(device)
+    for g in graphs.values():
+        g.replay()
+    torch.cuda.synchronize()
+    times = {True: [], False: []}
+    for _ in range(reps):
+        for key, g in graphs.items():
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(cur)
+            g.replay()
+            e1.record(cur)
+            torch.cuda.synchronize()
+            times[key].append(e0.elapsed_time(e1))
+    med = {key: sorted(t)[len(t) // 2] for key, t in times.items()}
+    ms_per_call = (med[True] - med[False]) / calls
+    npp = int(o["npp"].item())
+    timing = (f"pages' method: a {FLUSH_BYTES >> 20} MiB fill before each call; per call = (graph of fill+call "
+              f"- graph of fills) / {calls}, medians of {reps} replays each")
+    result = result_fields(wl, A, ms_per_call, npp, [npp], calls * reps, calls, timing)
+    result["config"]["fill_ms_per_call"] = round(med[False] / calls, 4)
+    return d, result
+
+
+def stream_read(reps=20):
+    """One plain streaming-read launch at 4 MiB and at 512 MiB: the 4 MiB
+    launches rotate over a 512 MiB buffer (each reads from HBM), as the route
+    launches do; graph replay, HIP events on the launch stream."""
+    import torch
+
+    import moe_token_routing_amd as mr
+
+    device = "cuda:0"
+    words = ROTATE_BYTES // 4
+    buf = torch.arange(words, dtype=torch.int32, device=device)
+    out = torch.zeros(mr.MR_STREAM_READ_OUT_WORDS, dtype=torch.int32, device=device)
+    stream = torch.cuda.Stream(device=device)
+    cur = torch.cuda.current_stream(device)
+    rows = []
+    for size in (4 << 20, 512 << 20):
+        R = ROTATE_BYTES // size
+        n = max(R, 8)
+        views = [buf[(i % R) * (size // 4):((i % R) + 1) * (size // 4)] for i in range(n)]
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for v in views:
+                mr.mr_debug_stream_read(v, out)
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(cur)
+        for _ in range(reps):
+            g.replay()
+        e1.record(cur)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * n)
+        gbs = size / (us * 1e-6) / 1e9
+        rows.append({"bytes": size, "launches": reps * n, "us_per_launch": round(us, 3), "GB/s": round(gbs, 1),
+                     "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)})
+    return {"stream_read": rows, "timing": "HIP graph replay, HIP events on the launch stream"}
+
+
+def measure(wl, steps, warmup, A=None):
     """Times `steps` route+align launches on workload `wl`; returns the seeded
     input and the result fields."""
     import torch
@@ -169,7 +334,8 @@ def measure(wl, steps, warmup):
     per_copy = (wl.E + int(wl.shared)) * wl.H * 2 + wl.M * wl.H * 2
     R = max(8, math.ceil(ROTATE_BYTES / per_copy))
     d, copies = make_copies(wl, R, device)
-    A = mr.mr_select_alignment(wl.M, wl.k, wl.E)
+    if A is None:
+        A = mr.mr_select_alignment(wl.M, wl.k, wl.E)
     ws = mr.new_workspace(wl.M, wl.E, wl.k, wl.shared, device=device)
     outs = []
     for (x, w, s) in copies:
@@ -215,47 +381,9 @@ def measure(wl, steps, warmup):
     ms_per_step = total_ms / steps
 
     npps = [int(o["npp"].item()) for o in outs]
-    mean_npp = sum(npps) / len(npps)
-    for n in npps:
-        assert n % A == 0 and n > 0
-    nbytes = algorithmic_bytes(wl, mean_npp, A)
-    launch_s = ms_per_step * 1e-3
-    achieved_gbs = nbytes / launch_s / 1e9
-    flops = 2.0 * wl.M * (wl.E + int(wl.shared)) * wl.H
-
-    if wl.M >= 512:
-        value, unit, hib = wl.M / launch_s, "rows/s", True
-    else:
-        value, unit, hib = ms_per_step * 1e3, "us/layer", False
-    mfma_tflops = flops / launch_s / 1e12
-    if wl.M >= 512 and flops / nbytes > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
-        roof = {"bound": "mfma", "achieved": round(mfma_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(mfma_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
-    else:
-        roof = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": None}
-    roof["kernel"] = "route_small_kernel" if wl.M <= 16 else "route_mfma_kernel"
-    roof["traffic"] = profiled_traffic(roof["kernel"], wl.name)
-    roof["bytes_per_launch"] = int(nbytes)
-    roof["flops_per_launch"] = int(flops)
-
-    result = {
-        "value": round(value, 3) if unit == "us/layer" else round(value, 1),
-        "unit": unit,
-        "n_gpus": 1,
-        "steps": steps,
-        "warmup": warmup,
-        "ms_per_step": round(ms_per_step, 6),
-        "higher_is_better": hib,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": wl.name, "M": wl.M, "E": wl.E, "shared": wl.shared, "H": wl.H, "k": wl.k,
-                   "A": A, "rotation_copies": R, "rotation_bytes": R * per_copy,
-                   "timing": "HIP graph of launches over rotated inputs; HIP events on the launch stream"},
-        "roofline": roof,
-    }
+    timing = "HIP graph of launches over rotated inputs; HIP events on the launch stream"
+    result = result_fields(wl, A, ms_per_step, sum(npps) / len(npps), npps, steps, warmup, timing)
+    result["config"].update({"rotation_copies": R, "rotation_bytes": R * per_copy})
     return d, result
 
 
@@ -270,18 +398,31 @@ def main():
     if args.calibrate_copy:
         calibrate_copy()
         return
+    wl = workload(args.workload)
+    if args.cpu_only:
+        from moe_token_routing_amd import workloads as W
+
+        d = W.workload_inputs(wl)
+        base = cpu_baseline(d, wl, args.cpu_seconds if args.cpu_seconds > 0 else 10.0, args.cpu_threads, args.align)
+        print(json.dumps({"workload": wl.name, "cpu_baseline": base}), flush=True)
+        return
     import moe_token_routing_amd as mr
 
     mr._binding.lib()
     torch.cuda.set_device(0)
-    wl = workload(args.workload)
-    d, result = measure(wl, args.steps, args.warmup)
+    if args.stream_read:
+        print(json.dumps(stream_read()), flush=True)
+        return
+    if args.method == "memset":
+        d, result = measure_memset(wl, 64, max(3, min(args.steps // 64, 15)), args.align)
+    else:
+        d, result = measure(wl, args.steps, args.warmup, args.align)
     result = {"metric": METRIC, **result}
-    if args.secondary_steps > 0 and args.workload == "m4":
+    if args.secondary_steps > 0 and args.workload == "m4" and args.method == "rotate" and args.align is None:
         _, sec = measure(workload("m2048"), args.secondary_steps, min(args.warmup, 256))
         result["secondary"] = {kk: sec[kk] for kk in ["value", "unit", "ms_per_step", "steps", "config", "roofline"]}
     if args.cpu_seconds > 0:
-        result["cpu_baseline"] = cpu_baseline(d, wl, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(d, wl, args.cpu_seconds, args.cpu_threads, args.align)
     print(json.dumps(result), flush=True)
 
 

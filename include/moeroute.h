@@ -155,6 +155,20 @@ int mr_debug_gate_logits(const void *x, const void *gate_w, const void *shared_w
                          int32_t M, int32_t H, int32_t E, float *logits,
                          void *ws, size_t ws_bytes, void *stream);
 
+/* Measurement hook, not part of the routing API: one launch of a plain
+ * streaming-read kernel over nbytes bytes at src (device memory, 16-byte
+ * aligned, nbytes a multiple of 16), as a yardstick for what a single launch
+ * of the simplest bandwidth kernel achieves at a given size.  out is a
+ * caller-owned device array of MR_STREAM_READ_OUT_WORDS 32-bit words: block
+ * b of the launch stores the XOR of the words it read in out[b] and leaves
+ * the other entries alone, so with out zeroed first, the XOR of all entries
+ * is the XOR of every word read (checkable, independent of the read order).
+ * Returns MR_EINVAL for a NULL pointer, MR_EUNSUPPORTED for a misaligned src
+ * or out or nbytes % 16 != 0, MR_ELAUNCH if the launch fails; nbytes == 0
+ * launches nothing. */
+#define MR_STREAM_READ_OUT_WORDS 4096
+int mr_debug_stream_read(const void *src, size_t nbytes, uint32_t *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

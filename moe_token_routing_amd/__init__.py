@@ -7,6 +7,7 @@ from ._binding import (  # noqa: F401
     MR_ELAUNCH,
     MR_EUNSUPPORTED,
     MR_OK,
+    MR_STREAM_READ_OUT_WORDS,
     SIGNATURES,
     MoeRouteError,
     library_path,
@@ -14,6 +15,7 @@ from ._binding import (  # noqa: F401
     mr_align,
     mr_align_capacity,
     mr_debug_gate_logits,
+    mr_debug_stream_read,
     mr_expert_ids_capacity,
     mr_last_error,
     mr_route,

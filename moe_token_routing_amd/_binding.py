@@ -17,6 +17,7 @@ MR_EINVAL = -1
 MR_EUNSUPPORTED = -2
 MR_ECAPACITY = -3
 MR_ELAUNCH = -4
+MR_STREAM_READ_OUT_WORDS = 4096
 
 # Every symbol include/moeroute.h declares, with (restype, argtypes).
 _P = ctypes.c_void_p
@@ -37,6 +38,7 @@ SIGNATURES = {
     "mr_route_align": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _F32, _I32, _P, _P, _P, _I64,
                                       _P, _I64, _P, _P, _SZ, _P]),
     "mr_debug_gate_logits": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _P, _P, _SZ, _P]),
+    "mr_debug_stream_read": (ctypes.c_int, [_P, _SZ, _P, _P]),
 }
 
 
@@ -231,3 +233,15 @@ def mr_debug_gate_logits(x, gate_w, shared_w, *, workspace, logits=None, stream=
     _check(lib().mr_debug_gate_logits(_ptr(x), _ptr(gate_w), _ptr(shared_w), M, H, E, _ptr(logits),
                                       _ptr(workspace), workspace.numel(), _stream(stream, x.device)))
     return logits
+
+
+def mr_debug_stream_read(src, out, nbytes=None, stream=None):
+    """Measurement hook: one plain streaming-read launch over the first
+    nbytes of src (default: all of it).  out: MR_STREAM_READ_OUT_WORDS int32
+    words on the device; block b stores the XOR of what it read in out[b]."""
+    if not src.is_contiguous():
+        raise ValueError("src must be contiguous")
+    if out.numel() * out.element_size() < 4 * MR_STREAM_READ_OUT_WORDS:
+        raise ValueError(f"out must hold {MR_STREAM_READ_OUT_WORDS} 32-bit words")
+    n = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    _check(lib().mr_debug_stream_read(_ptr(src), n, _ptr(out), _stream(stream, src.device)))

@@ -336,6 +336,20 @@ int mr_debug_gate_logits(const void *x, const void *gate_w, const void *shared_w
                     nullptr, 0, nullptr, 0, nullptr, logits, ws, ws_bytes, stream, false);
 }
 
+static_assert(MR_STREAM_READ_OUT_WORDS == mr::kStreamReadMaxBlocks, "stream-read output size");
+
+int mr_debug_stream_read(const void *src, size_t nbytes, uint32_t *out, void *stream) {
+  Checks ck;
+  if (!src) ck.fail(MR_EINVAL, "src is NULL");
+  else if (!aligned16(src)) ck.fail(MR_EUNSUPPORTED, "src is not 16-byte aligned");
+  if (!out) ck.fail(MR_EINVAL, "out is NULL");
+  else if (reinterpret_cast<uintptr_t>(out) % 4 != 0) ck.fail(MR_EUNSUPPORTED, "out is not 4-byte aligned");
+  if (nbytes % 16 != 0) ck.fail(MR_EUNSUPPORTED, "nbytes=%zu is not a multiple of 16", nbytes);
+  if (ck.code() != MR_OK) return ck.finish("mr_debug_stream_read");
+  return launch_result(mr::launch_stream_read(src, nbytes, out, reinterpret_cast<hipStream_t>(stream)),
+                       "mr_debug_stream_read");
+}
+
 int mr_align(const int32_t *topk_ids, int32_t M, int32_t S, int32_t num_experts, int32_t A,
              int32_t *sorted_token_ids, int64_t sorted_cap, int32_t *expert_ids, int64_t expert_cap, int32_t *npp,
              void *ws, size_t ws_bytes, void *stream) {

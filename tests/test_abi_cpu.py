@@ -123,6 +123,21 @@ def test_align_refusals(lib):
     assert rc == mr.MR_EUNSUPPORTED and "num_experts=5000 > 4096" in _err(lib)
 
 
+def test_stream_read_refusals(lib):
+    rc = lib.mr_debug_stream_read(None, 16, None, None)
+    assert rc == mr.MR_EINVAL
+    msg = _err(lib)
+    assert "src is NULL" in msg and "out is NULL" in msg, msg
+    rc = lib.mr_debug_stream_read(ctypes.c_void_p((1 << 20) + 8), 24, ctypes.c_void_p((1 << 20) + 2), None)
+    assert rc == mr.MR_EUNSUPPORTED
+    msg = _err(lib)
+    for needle in ["src is not 16-byte aligned", "out is not 4-byte aligned", "nbytes=24 is not a multiple of 16"]:
+        assert needle in msg, (needle, msg)
+    with open(os.path.join(ROOT, "include", "moeroute.h")) as f:
+        words = re.search(r"#define MR_STREAM_READ_OUT_WORDS (\d+)", f.read())
+    assert words and int(words.group(1)) == mr.MR_STREAM_READ_OUT_WORDS
+
+
 def test_error_cleared_after_success_path(lib):
     lib.mr_route(None, None, None, -1, 7, 0, 0, 1.0, None, None, None, 0, None)
     assert _err(lib)
