@@ -16,6 +16,7 @@
 
 #include "kernels.h"
 #include "moeroute.h"
+#include "stream_read.h"
 
 static_assert(MR_MAX_ROUTED_EXPERTS == mr::kMaxRouteExperts, "route expert limit");
 static_assert(MR_MAX_ALIGN_EXPERTS == mr::kMaxAlignExperts, "align expert limit");

@@ -129,11 +129,4 @@ hipError_t launch_align(const AlignParams &p, hipStream_t stream);
 hipError_t launch_zero_words(uint32_t *p, size_t n, hipStream_t stream);
 hipError_t launch_store_zero(int32_t *p, hipStream_t stream);
 
-// Plain streaming read of nbytes (a multiple of 16, 16-byte aligned): block b
-// of at most kStreamReadMaxBlocks stores the XOR of the words it read in
-// out[b]; the XOR of out[0 .. kStreamReadMaxBlocks) is the XOR of every word
-// when out starts zeroed.
-constexpr int kStreamReadMaxBlocks = 4096;
-hipError_t launch_stream_read(const void *src, size_t nbytes, uint32_t *out, hipStream_t stream);
-
 }  // namespace mr

@@ -8,7 +8,7 @@
 // Block b stores the XOR of everything it read in out[b] (a plain store: one
 // shared word taking an atomic per wave would serialise at the memory).
 #include "device_common.h"
-#include "kernels.h"
+#include "stream_read.h"
 
 namespace mr {
 
