@@ -38,10 +38,11 @@
 //   selections interleaved, when it holds more than one) and selects the
 //   top-k as k rounds of a wave-wide maximum over the packed keys (DPP within
 //   rows of 16, then gfx950's permlane16/32 swaps), then the softmax, shared
-//   slot and stores; then one wave aligns: with M <= 16 <= A every touched
-//   expert takes exactly one block, so a bitmap of touched experts (block
-//   index = rank among them, one wave scan) and one of token rows per expert
-//   (slot in the block) place every pair.
+//   slot and stores, marking each pair in two LDS bitmaps; then the align:
+//   with M <= 16 <= A every touched expert takes exactly one block, so the
+//   bitmap of touched experts (block index = rank among them, one wave scan)
+//   and the one of token rows per expert (slot in the block) place every
+//   pair, one pair per thread.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -66,6 +67,18 @@ __device__ __forceinline__ uint32_t max_of(const uint32_t (&a)[N]) {
   return t[0];
 }
 
+// Align bitmaps (block 0's LDS, zeroed at the block's start): bit m of
+// rowbm[e] marks that token row m chose expert e, bit e & 31 of
+// touched[e >> 5] that some row did.  The tail marks each pair as it stores
+// it; ids outside [0, E') are skipped.
+__device__ __forceinline__ void mark_pair(const SmallParams &p, int32_t id, int m, uint32_t *rowbm,
+                                          uint32_t *touched) {
+  if ((uint32_t)id < (uint32_t)p.Ep) {
+    atomicOr(&rowbm[id], 1u << m);
+    atomicOr(&touched[id >> 5], 1u << (id & 31));
+  }
+}
+
 // Tail, part 1, token rows in pairs: wave w takes the token rows w, w+4,
 // w+8, ..., two at a time (w + 8i and w + 8i + 4) so that the two
 // selections interleave.  Each
@@ -73,7 +86,7 @@ __device__ __forceinline__ uint32_t max_of(const uint32_t (&a)[N]) {
 // is a wave-wide maximum of the lanes' sorted heads, and the lane that held
 // it drops its head (keys are unique).
 template <int NK>
-__device__ void route_tail_rows2(const SmallParams &p, int32_t *lds_ids) {
+__device__ void route_tail_rows2(const SmallParams &p, int32_t *lds_ids, uint32_t *rowbm, uint32_t *touched) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = p.E, k = p.k, S = p.S;
   constexpr int kWaves = kThreads / kWave;
@@ -94,6 +107,7 @@ __device__ void route_tail_rows2(const SmallParams &p, int32_t *lds_ids) {
       p.ids[(size_t)m * S + lane] = id;
       p.wts[(size_t)m * S + lane] = w;
       lds_ids[m * S + lane] = id;
+      if (p.do_align) mark_pair(p, id, m, rowbm, touched);
     }
   };
   for (int ma = wave; ma < p.M; ma += 2 * kWaves) {
@@ -159,7 +173,7 @@ __device__ void route_tail_rows2(const SmallParams &p, int32_t *lds_ids) {
 // lane, lane+64, ...); a selection round is the lane maximum, a wave-wide
 // maximum, and clearing the one key equal to it (keys are unique).
 template <int NK>
-__device__ void route_tail_rows1(const SmallParams &p, int32_t *lds_ids) {
+__device__ void route_tail_rows1(const SmallParams &p, int32_t *lds_ids, uint32_t *rowbm, uint32_t *touched) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = p.E, k = p.k, S = p.S;
   for (int m = wave; m < p.M; m += kThreads / kWave) {
@@ -204,57 +218,47 @@ __device__ void route_tail_rows1(const SmallParams &p, int32_t *lds_ids) {
       p.ids[(size_t)m * S + lane] = id;
       p.wts[(size_t)m * S + lane] = w;
       lds_ids[m * S + lane] = id;
+      if (p.do_align) mark_pair(p, id, m, rowbm, touched);
     }
   }
 }
 
-// Tail, part 2: align of the n = M*S pairs in lds_ids by ONE wave (no
-// block barriers; wave_lds_sync orders the wave's LDS accesses for the
-// compiler).  Here M <= 16 <= A, and a token row holds an expert at most
-// once, so an expert's pairs always fit one block of A slots: every touched
-// expert pads to exactly A.  Its block index is its rank among the touched
-// experts (a bitmap over expert ids and one wave scan of the word
-// popcounts), and a pair's slot in the block is the number of earlier token
-// rows that chose the same expert (a bitmap of rows per expert), which keeps
-// ascending flat index inside the expert.  The shared expert (id E, every
-// row) is handled like the others and comes last.  Only the bitmap entries
-// the pairs touch are cleared first; the sentinel pre-fill already holds
-// every slot the pairs do not.
-__device__ void align_small(const SmallParams &p, const int32_t *lds_ids, uint32_t *rowbm, uint32_t *touched,
-                            uint32_t *pre) {
-  const int lane = threadIdx.x & 63;
+// Tail, part 2: align of the n = M*S pairs in lds_ids.  Here M <= 16 <= A,
+// and a token row holds an expert at most once, so an expert's pairs always
+// fit one block of A slots: every touched expert pads to exactly A.  Its
+// block index is its rank among the touched experts -- the touched-bitmap
+// words' popcounts, scanned by each wave that holds pairs (at most 33 words,
+// one wave scan; the base of word e >> 5 fetched with ds_bpermute) -- and a
+// pair's slot in the block is the number of earlier token rows that chose
+// the same expert, which keeps ascending flat index inside the expert.  The
+// shared expert (id E, every row) is handled like the others and comes last.
+// The sentinel pre-fill already holds every slot the pairs do not.  Every
+// thread of the block calls this after the block barrier that follows the
+// tail's marks.
+__device__ void align_small(const SmallParams &p, const int32_t *lds_ids, const uint32_t *rowbm,
+                            const uint32_t *touched) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = p.M * p.S, Ep = p.Ep, sh = p.log2A;
   const int words = (Ep + 31) >> 5;  // <= 33 for E' <= 1025: one wave scan covers them
-  for (int w = lane; w < words; w += kWave) touched[w] = 0u;
-  for (int i = lane; i < n; i += kWave) {
-    const int e = lds_ids[i];
-    if (e >= 0 && e < Ep) rowbm[e] = 0u;
-  }
-  wave_lds_sync();
-  for (int i = lane; i < n; i += kWave) {
-    const int e = lds_ids[i];
-    if (e >= 0 && e < Ep) {
-      atomicOr(&rowbm[e], 1u << __umulhi((uint32_t)i, p.S_magic));
-      atomicOr(&touched[e >> 5], 1u << (e & 31));
-    }
-  }
-  wave_lds_sync();
+  if (wave * kWave >= n) return;  // wave-uniform: this wave holds no pairs (wave 0 always does)
   const uint32_t pc = lane < words ? __builtin_popcount(touched[lane]) : 0u;
   const uint32_t incl = wave_incl_scan_u32(pc, lane);
-  if (lane < words) pre[lane] = incl - pc;
-  const uint32_t touched_experts = __builtin_amdgcn_readlane(incl, 63);
-  wave_lds_sync();
-  for (int i = lane; i < n; i += kWave) {
-    const int e = lds_ids[i];
-    if (e < 0 || e >= Ep) continue;
+  const uint32_t excl = incl - pc;  // touched experts in the words before lane's
+  if (tid == 0) *p.npp = (int32_t)(__builtin_amdgcn_readlane(incl, 63) << sh);
+  for (int i0 = wave * kWave; i0 < n; i0 += kThreads) {  // wave-uniform trip count: every lane active
+    const int i = i0 + lane;
+    const int e = lds_ids[min(i, n - 1)];
+    const bool valid = i < n && e >= 0 && e < Ep;
+    const int ew = valid ? e >> 5 : 0;
+    const uint32_t base = (uint32_t)__builtin_amdgcn_ds_bpermute(ew << 2, (int)excl);
+    if (!valid) continue;
     const uint32_t m = __umulhi((uint32_t)i, p.S_magic);
-    const uint32_t blk = pre[e >> 5] + __builtin_popcount(touched[e >> 5] & ((1u << (e & 31)) - 1u));
+    const uint32_t blk = base + __builtin_popcount(touched[ew] & ((1u << (e & 31)) - 1u));
     const uint32_t rank = __builtin_popcount(rowbm[e] & ((1u << m) - 1u));
     const uint64_t pos = ((uint64_t)blk << sh) + rank;
     if (pos < (uint64_t)p.sorted_cap) p.sorted[pos] = i;
     if (rank == 0 && blk < (uint64_t)p.expert_cap) p.expert_ids[blk] = e;
   }
-  if (lane == 0) *p.npp = (int32_t)(touched_experts << sh);
 }
 
 // Value held by lane (lane ^ J) of a float (see xor_lane_u32).
@@ -315,6 +319,15 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
   const int row0 = blockIdx.x * RPB;
   const int H = p.H, M = p.M;
   const int nch = H >> 3;  // 16-byte chunks per row
+
+  // align bitmaps of block 0's tail: zeroed now, off the tail's path (the
+  // gate's block barrier orders these stores before the tail's marks)
+  __shared__ uint32_t rowbm[kWave * NK + 1];  // E' <= 64 NK + 1
+  __shared__ uint32_t touched[kMaxRouteExperts / 32 + 1];
+  if (blockIdx.x == 0 && p.do_align && !p.logits_only) {
+    for (int e = tid; e < p.Ep; e += kThreads) rowbm[e] = 0u;
+    for (int w = tid; w < ((p.Ep + 31) >> 5); w += kThreads) touched[w] = 0u;
+  }
 
   // ---- sentinel pre-fill of this block's slice of sorted_token_ids ------
   if (p.do_align) {
@@ -452,13 +465,11 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
   // ---- block 0: the tail ---------------------------------------------------
   __shared__ int32_t lds_ids[MAXM * (kMaxTopK + 1)];
   // Token rows in pairs when a wave holds more than one (M >= 5).
-  if constexpr (MAXM > kThreads / kWave) route_tail_rows2<NK>(p, lds_ids);
-  else route_tail_rows1<NK>(p, lds_ids);
+  if constexpr (MAXM > kThreads / kWave) route_tail_rows2<NK>(p, lds_ids, rowbm, touched);
+  else route_tail_rows1<NK>(p, lds_ids, rowbm, touched);
   if (p.do_align) {
-    __shared__ uint32_t rowbm[kWave * NK + 1];  // E' <= 64 NK + 1
-    __shared__ uint32_t touched[kMaxRouteExperts / 32 + 1], pre[kMaxRouteExperts / 32 + 1];
-    __syncthreads();
-    if (wave == 0) align_small(p, lds_ids, rowbm, touched, pre);
+    __syncthreads();  // every pair is marked and in lds_ids
+    align_small(p, lds_ids, rowbm, touched);
   }
 }
 
