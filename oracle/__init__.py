@@ -62,6 +62,8 @@ def _load():
     lib.or_round_bf16_array.restype = None
     lib.or_bf16_value_array.argtypes = [P, P, i64]
     lib.or_bf16_value_array.restype = None
+    lib.or_argmax_rows.argtypes = [P, i64, i64, i64, P, i32]
+    lib.or_argmax_rows.restype = i32
     _lib = lib
     return lib
 
@@ -179,6 +181,19 @@ def align(topk_ids, num_experts: int, A: int, sorted_cap: int | None = None,
         raise ValueError(f"or_align failed ({rc})")
     n = int(npp[0])
     return srt[:n].copy(), eids[: n // A].copy(), n
+
+
+def argmax_rows(x, nthreads: int = 0) -> np.ndarray:
+    """Row-wise argmax of a 2-D float32 array with PyTorch's semantics (NaN
+    first, lowest index on ties, -0 == +0); int64 [R]."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.ndim != 2 or x.shape[1] < 1:
+        raise ValueError("x must be [R, N] with N >= 1")
+    out = np.empty(x.shape[0], dtype=np.int64)
+    rc = _load().or_argmax_rows(_ptr(x), x.shape[0], x.shape[1], x.shape[1], _ptr(out), nthreads)
+    if rc != 0:
+        raise ValueError(f"or_argmax_rows failed ({rc})")
+    return out
 
 
 class use_library:

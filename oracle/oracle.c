@@ -16,6 +16,8 @@
  *        sections Motivation, Modifications, Accuracy Tests.
  *   [A]  "W4A16 MoE prefill: M-aware moe_align block size" (ROCm vLLM),
  *        sections Purpose, Scope and safety.
+ *   [N]  "Open-Source ROCm Kernels for AMD MI350X" (Netra Kernel blog),
+ *        section "Sampling: make small batches large enough".
  *
  * What each function computes, in the order the route takes:
  *   or_gate            z[m][e] = sum_h x[m][h] * W[e][h] in double, summed
@@ -37,6 +39,10 @@
  *                      expert, each touched expert padded to a multiple of A;
  *                      npp = sum over touched experts of ceil(c_e/A)*A ([A]
  *                      Purpose).
+ *   or_argmax_rows     row-wise argmax of an fp32 matrix with PyTorch's
+ *                      semantics as [N] Sampling states them: a NaN beats
+ *                      every number and the first NaN beats later ones; among
+ *                      equal numbers the lowest index wins; -0 equals +0.
  *
  * Readings where the pages are silent (each is listed in the design notes):
  *   - rounding mode of the logit rounding: nearest, ties to even;
@@ -376,3 +382,36 @@ void or_bf16_value_array(const uint16_t *bits, double *out, int64_t n)
     for (int64_t i = 0; i < n; ++i)
         out[i] = or_bf16_value(bits[i]);
 }
+
+/* -------------------------------------------------------------- argmax -- */
+
+/* out[r] = index of the winner of row r of x [R, N] (row stride ld floats),
+ * scanning the row left to right and replacing the current winner only when
+ * the new value beats it ([N] Sampling): a NaN beats any number, a NaN never
+ * loses its place to a later NaN, and a number beats another only when it is
+ * strictly greater (so equal numbers, including -0 and +0, keep the lowest
+ * index).  Returns OR_EINVAL for R < 0, N < 1 or ld < N. */
+int or_argmax_rows(const float *x, int64_t R, int64_t N, int64_t ld, int64_t *out, int nthreads)
+{
+    if (R < 0 || N < 1 || ld < N)
+        return OR_EINVAL;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(static) if (nthreads != 1)
+#endif
+    for (int64_t r = 0; r < R; ++r) {
+        const float *row = x + r * ld;
+        int64_t best = 0;
+        for (int64_t j = 1; j < N; ++j) {
+            const float b = row[best], v = row[j];
+            if (isnan(b))
+                break; /* the first NaN has won the row */
+            if (isnan(v) || v > b)
+                best = j;
+        }
+        out[r] = best;
+    }
+    return OR_OK;
+}
+

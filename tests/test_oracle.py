@@ -462,3 +462,59 @@ def test_route_exact_inputs_consistency():
     for m in range(3):
         assert out["ids"][m, :3].tolist() == _brute_topk(rb[m], 3)
         assert out["ids"][m, 3] == 12
+
+
+# ---------------------------------------------------------------- argmax --
+# [N] Sampling: a NaN beats every number, the first NaN beats later NaNs,
+# equal numbers go to the lowest index, -0 equals +0 (PyTorch's argmax).
+
+def test_argmax_hand_cases(golden_dir):
+    with open(os.path.join(golden_dir, "argmax_cases.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        row = np.array([float(v) for v in c["row"]], dtype=np.float32)
+        got = int(oracle.argmax_rows(row[None, :])[0])
+        assert got == c["want"], (c, got)
+
+
+def test_argmax_brute_force_tiny():
+    # every row of length 4 over seven special values, against the rule
+    # stated as a set: the first NaN if there is one, else the first index
+    # whose value equals the maximum
+    vals = [float("nan"), float("-inf"), -1.0, -0.0, 0.0, 1.0, float("inf")]
+    rows = np.array(list(itertools.product(vals, repeat=4)), dtype=np.float32)
+    got = oracle.argmax_rows(rows)
+    for r, g in zip(rows, got):
+        nans = [i for i, v in enumerate(r) if math.isnan(v)]
+        if nans:
+            want = nans[0]
+        else:
+            mx = max(float(v) for v in r)
+            want = min(i for i, v in enumerate(r) if float(v) == mx)
+        assert g == want, (r, g, want)
+
+
+def test_argmax_matches_torch_and_numpy():
+    import torch
+
+    rng = np.random.default_rng(7)
+    R, N = 24, 3001
+    x = rng.standard_normal((R, N)).astype(np.float32)
+    pool = np.array([np.nan, np.inf, -np.inf, 0.0, -0.0, 1.5, -1.5, 4.0], dtype=np.float32)
+    for r in range(R):
+        kind = r % 6
+        if kind == 1:  # a few NaNs
+            x[r, rng.choice(N, 3, replace=False)] = np.nan
+        elif kind == 2:  # many ties at the maximum
+            x[r, rng.choice(N, 50, replace=False)] = 9.0
+        elif kind == 3:  # only signed zeros and -inf
+            x[r] = rng.choice(np.array([0.0, -0.0, -np.inf], dtype=np.float32), N)
+        elif kind == 4:  # special values everywhere
+            x[r] = rng.choice(pool, N)
+        elif kind == 5:  # integer-valued, heavy ties
+            x[r] = rng.integers(-3, 4, N).astype(np.float32)
+    got = oracle.argmax_rows(x)
+    assert np.array_equal(got, torch.from_numpy(x).argmax(dim=1).numpy())
+    assert np.array_equal(got, np.argmax(x, axis=1))
+    # thread count does not change the result
+    assert np.array_equal(got, oracle.argmax_rows(x, nthreads=1))

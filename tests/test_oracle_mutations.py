@@ -34,6 +34,10 @@ MUTATIONS = {
                              "for (int64_t b = off[e] / A + 1; b <= (off[e] + padded) / A && b < expert_cap; ++b)"),
     "tier_strict": ("((int64_t)M * k >= (int64_t)128 * E)", "((int64_t)M * k > (int64_t)128 * E)"),
     "tier_uses_slots": ("((int64_t)M * k >= (int64_t)128 * E)", "((int64_t)M * (k + 1) >= (int64_t)128 * E)"),
+    "argmax_ties_last": ("if (isnan(v) || v > b)", "if (isnan(v) || v >= b)"),
+    "argmax_last_nan": ("            if (isnan(b))\n                break; /* the first NaN has won the row */\n", ""),
+    "argmax_nan_loses": ("if (isnan(v) || v > b)", "if (v > b)"),
+    "argmax_positive_zero_wins": ("if (isnan(v) || v > b)", "if (isnan(v) || v > b || (v == b && signbit(b) && !signbit(v)))"),
     "capacity_tight_wrong": ("int64_t touched = loose ? Eprime : (Eprime < n ? Eprime : n);",
                              "int64_t touched = loose ? Eprime - 1 : (Eprime < n ? Eprime : n);"),
 }
