@@ -155,6 +155,28 @@ int mr_debug_gate_logits(const void *x, const void *gate_w, const void *shared_w
                          int32_t M, int32_t H, int32_t E, float *logits,
                          void *ws, size_t ws_bytes, void *stream);
 
+/* Row-wise argmax of an fp32 matrix, one launch: out[r] = the index of the
+ * winner of row r of x, with the semantics "Open-Source ROCm Kernels for AMD
+ * MI350X" (Netra Kernel blog), section "Sampling: make small batches large
+ * enough", requires (PyTorch's argmax): a NaN beats every number and the
+ * first NaN beats later NaNs; among equal numbers the lowest index wins; -0
+ * and +0 compare equal.
+ *   x    device, [R, ld] fp32 row-major (row r at x + r * ld), 16-byte
+ *        aligned, ld % 4 == 0, ld >= N; only the first N values of a row
+ *        are read.
+ *   out  device, [R] int64, caller-owned.
+ *   ws   device workspace of at least mr_argmax_workspace_bytes(R, N) bytes,
+ *        16-byte aligned, zeroed once by the caller; every launch leaves it
+ *        zeroed again (row tickets), so calls are graph-capturable.  One
+ *        workspace per concurrently running stream.
+ * Returns MR_OK; MR_EINVAL for NULL pointers, R < 0, N < 1 or ld < N;
+ * MR_EUNSUPPORTED for a misaligned x or ws, ld % 4 != 0 or N >= 2^31;
+ * MR_ECAPACITY for a short workspace; MR_ELAUNCH if the launch fails.
+ * R == 0 launches nothing. */
+size_t mr_argmax_workspace_bytes(int32_t R, int64_t N);
+int mr_argmax_rows_f32(const float *x, int32_t R, int64_t N, int64_t ld, int64_t *out,
+                       void *ws, size_t ws_bytes, void *stream);
+
 /* Measurement hook, not part of the routing API: one launch of a plain
  * streaming-read kernel over nbytes bytes at src (device memory, 16-byte
  * aligned, nbytes a multiple of 16), as a yardstick for what a single launch

@@ -39,6 +39,8 @@ SIGNATURES = {
                                       _P, _I64, _P, _P, _SZ, _P]),
     "mr_debug_gate_logits": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _P, _P, _SZ, _P]),
     "mr_debug_stream_read": (ctypes.c_int, [_P, _SZ, _P, _P]),
+    "mr_argmax_workspace_bytes": (_SZ, [_I32, _I64]),
+    "mr_argmax_rows_f32": (ctypes.c_int, [_P, _I32, _I64, _I64, _P, _P, _SZ, _P]),
 }
 
 
@@ -245,3 +247,33 @@ def mr_debug_stream_read(src, out, nbytes=None, stream=None):
         raise ValueError(f"out must hold {MR_STREAM_READ_OUT_WORDS} 32-bit words")
     n = src.numel() * src.element_size() if nbytes is None else int(nbytes)
     _check(lib().mr_debug_stream_read(_ptr(src), n, _ptr(out), _stream(stream, src.device)))
+
+
+def mr_argmax_workspace_bytes(R: int, N: int) -> int:
+    return int(lib().mr_argmax_workspace_bytes(R, N))
+
+
+def new_argmax_workspace(R: int, N: int, device="cuda"):
+    """A zeroed workspace for mr_argmax_rows_f32 on R rows of N values."""
+    import torch
+
+    return torch.zeros(max(mr_argmax_workspace_bytes(R, N), 16), dtype=torch.uint8, device=device)
+
+
+def mr_argmax_rows_f32(x, *, workspace, out=None, n=None, stream=None):
+    """Row-wise argmax (PyTorch semantics) of a 2-D float32 CUDA tensor whose
+    rows are contiguous; reads the first n (default: all) values of each row.
+    Returns int64 [R]."""
+    import torch
+
+    if x.dtype != torch.float32 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D float32 tensor with contiguous rows")
+    R, N = x.shape
+    N = N if n is None else int(n)
+    if out is None:
+        out = torch.empty(R, dtype=torch.int64, device=x.device)
+    # a single row's stride is never used: pass N rounded up to 4
+    ld = x.stride(0) if R > 1 else N + (-N) % 4
+    _check(lib().mr_argmax_rows_f32(_ptr(x), R, N, ld, _ptr(out), _ptr(workspace), workspace.numel(),
+                                    _stream(stream, x.device)))
+    return out

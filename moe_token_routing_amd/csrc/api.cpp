@@ -17,6 +17,7 @@
 #include "kernels.h"
 #include "moeroute.h"
 #include "stream_read.h"
+#include "argmax.h"
 
 static_assert(MR_MAX_ROUTED_EXPERTS == mr::kMaxRouteExperts, "route expert limit");
 static_assert(MR_MAX_ALIGN_EXPERTS == mr::kMaxAlignExperts, "align expert limit");
@@ -275,6 +276,9 @@ int route_impl(const char *fn, const void *x, const void *gate_w, const void *sh
 
 }  // namespace
 
+// Argmax workspace: row tickets (own 256-byte region), then the [R, C] block keys.
+static size_t argmax_ticket_bytes(int64_t R) { return ((size_t)R * 4 + 255) / 256 * 256; }
+
 extern "C" {
 
 int mr_abi_version(void) { return MR_ABI_VERSION; }
@@ -335,6 +339,50 @@ int mr_debug_gate_logits(const void *x, const void *gate_w, const void *shared_w
   }
   return route_impl("mr_debug_gate_logits", x, gate_w, shared_w, M, H, E, 1, 1.0f, 64, nullptr, nullptr,
                     nullptr, 0, nullptr, 0, nullptr, logits, ws, ws_bytes, stream, false);
+}
+
+size_t mr_argmax_workspace_bytes(int32_t R, int64_t N) {
+  if (R < 0 || N < 1) return 0;
+  const int64_t C = mr::argmax_chunks(N);
+  return argmax_ticket_bytes(R) + (size_t)R * (size_t)C * 8;
+}
+
+int mr_argmax_rows_f32(const float *x, int32_t R, int64_t N, int64_t ld, int64_t *out, void *ws, size_t ws_bytes,
+                       void *stream) {
+  Checks ck;
+  if (R < 0) ck.fail(MR_EINVAL, "R=%d < 0", R);
+  if (N < 1) ck.fail(MR_EINVAL, "N=%lld < 1", (long long)N);
+  if (N >= ((int64_t)1 << 31)) ck.fail(MR_EUNSUPPORTED, "N=%lld >= 2^31", (long long)N);
+  if (ld < N) ck.fail(MR_EINVAL, "ld=%lld < N=%lld", (long long)ld, (long long)N);
+  if (ld % 4 != 0) ck.fail(MR_EUNSUPPORTED, "ld=%lld is not a multiple of 4", (long long)ld);
+  if (R > 0) {
+    if (!x) ck.fail(MR_EINVAL, "x is NULL");
+    else if (!aligned16(x)) ck.fail(MR_EUNSUPPORTED, "x is not 16-byte aligned");
+    if (!out) ck.fail(MR_EINVAL, "out is NULL");
+    if (!ws) ck.fail(MR_EINVAL, "ws is NULL");
+    else if (!aligned16(ws)) ck.fail(MR_EUNSUPPORTED, "ws is not 16-byte aligned");
+    if (N >= 1 && N < ((int64_t)1 << 31) && (int64_t)R * mr::argmax_chunks(N) > (int64_t)0x7FFFFFFF)
+      ck.fail(MR_EUNSUPPORTED, "R * chunks = %lld blocks > 2^31 - 1", (long long)((int64_t)R * mr::argmax_chunks(N)));
+    if (R >= 0 && N >= 1) {
+      const size_t need = mr_argmax_workspace_bytes(R, N);
+      if (ws_bytes < need) ck.fail(MR_ECAPACITY, "ws_bytes=%zu < %zu", ws_bytes, need);
+    }
+  }
+  if (ck.code() != MR_OK) return ck.finish("mr_argmax_rows_f32");
+  if (R == 0) {
+    g_last_error.clear();
+    return MR_OK;
+  }
+  mr::ArgmaxParams p;
+  p.x = x;
+  p.R = R;
+  p.N = N;
+  p.ld = ld;
+  p.C = mr::argmax_chunks(N);
+  p.out = out;
+  p.ticket = static_cast<uint32_t *>(ws);
+  p.part = reinterpret_cast<unsigned long long *>(static_cast<char *>(ws) + argmax_ticket_bytes(R));
+  return launch_result(mr::launch_argmax(p, reinterpret_cast<hipStream_t>(stream)), "mr_argmax_rows_f32");
 }
 
 static_assert(MR_STREAM_READ_OUT_WORDS == mr::kStreamReadMaxBlocks, "stream-read output size");

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared_symbols():
     with open(os.path.join(ROOT, "include", "moeroute.h")) as f:
         text = f.read()
-    return sorted(set(re.findall(r"\b(mr_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(mr_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -136,6 +136,28 @@ def test_stream_read_refusals(lib):
     with open(os.path.join(ROOT, "include", "moeroute.h")) as f:
         words = re.search(r"#define MR_STREAM_READ_OUT_WORDS (\d+)", f.read())
     assert words and int(words.group(1)) == mr.MR_STREAM_READ_OUT_WORDS
+
+
+def test_argmax_refusals(lib):
+    p = ctypes.c_void_p(1 << 20)
+    rc = lib.mr_argmax_rows_f32(None, 2, 0, 2, None, None, 0, None)
+    assert rc == mr.MR_EINVAL
+    msg = _err(lib)
+    for needle in ["N=0 < 1", "x is NULL", "out is NULL", "ws is NULL", "ld=2 is not a multiple of 4"]:
+        assert needle in msg, (needle, msg)
+    rc = lib.mr_argmax_rows_f32(ctypes.c_void_p((1 << 20) + 4), 2, 10, 8, p, p, 16, None)
+    assert rc == mr.MR_EINVAL
+    msg = _err(lib)
+    for needle in ["ld=8 < N=10", "x is not 16-byte aligned"]:
+        assert needle in msg, (needle, msg)
+    need = lib.mr_argmax_workspace_bytes(16, 248320)
+    assert need == 256 + 16 * 31 * 8
+    rc = lib.mr_argmax_rows_f32(p, 16, 248320, 248320, p, p, need - 8, None)
+    assert rc == mr.MR_ECAPACITY and f"< {need}" in _err(lib)
+    rc = lib.mr_argmax_rows_f32(p, 1, 1 << 31, 1 << 31, p, p, 1 << 40, None)
+    assert rc == mr.MR_EUNSUPPORTED and ">= 2^31" in _err(lib)
+    assert lib.mr_argmax_rows_f32(None, 0, 5, 8, None, None, 0, None) == mr.MR_OK  # R == 0: nothing to do
+    assert lib.mr_argmax_workspace_bytes(-1, 5) == 0 and lib.mr_argmax_workspace_bytes(3, 0) == 0
 
 
 def test_error_cleared_after_success_path(lib):
