@@ -37,9 +37,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=8192)
     ap.add_argument("--warmup", type=int, default=512)
-    ap.add_argument("--workload", default="m4", choices=[f"m{m}" for m in SWEEP_M] + ["c3", "c4"],
+    ap.add_argument("--workload", default="m4", choices=[f"m{m}" for m in SWEEP_M] + ["c3", "c4", "argmax"],
                     help="m<M>: E=512+1, H=4096, k=10 at M tokens (m4 is the headline); c3: E=128, H=2048, "
-                         "k=8, M=128; c4: the same at M=2048 with Zipf-skewed gate rows")
+                         "k=8, M=128; c4: the same at M=2048 with Zipf-skewed gate rows; argmax: row-wise fp32 "
+                         "argmax of [16, 248320] (the sampling shape)")
     ap.add_argument("--align", type=int, default=None, choices=[64, 128],
                     help="force the alignment A (default: the M-aware tier)")
     ap.add_argument("--method", default="rotate", choices=["rotate", "memset"],
@@ -156,9 +157,11 @@ def source_digest(kernel):
     import hashlib
 
     csrc = os.path.join(ROOT, "moe_token_routing_amd", "csrc")
-    main = {"route_small_kernel": "route_small.hip", "route_mfma_kernel": "route_mfma.hip"}[kernel]
+    files = {"route_small_kernel": ["route_small.hip", "device_common.h", "kernels.h"],
+             "route_mfma_kernel": ["route_mfma.hip", "device_common.h", "kernels.h"],
+             "argmax_kernel": ["argmax.hip", "argmax.h", "device_common.h"]}[kernel]
     h = hashlib.sha256()
-    for f in [main, "device_common.h", "kernels.h"]:
+    for f in files:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -323,6 +326,116 @@ def stream_read(reps=20):
     return {"stream_read": rows, "timing": "HIP graph replay, HIP events on the launch stream"}
 
 
+ARGMAX_R, ARGMAX_N = 16, 248320
+
+
+def argmax_input(seed=0):
+    """[16, 248320] fp32 logits ~ N(0, 1) with a few planted NaNs, ties and
+    signed zeros (seeded)."""
+    import numpy as np
+
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((ARGMAX_R, ARGMAX_N)).astype(np.float32)
+    x[1, rng.choice(ARGMAX_N, 3, replace=False)] = np.nan
+    x[2, rng.choice(ARGMAX_N, 40, replace=False)] = 8.0
+    x[3] = rng.choice(np.array([0.0, -0.0, -1.0], dtype=np.float32), ARGMAX_N)
+    return x
+
+
+def measure_argmax(steps, warmup, cpu_seconds):
+    """Times mr_argmax_rows_f32 on [16, 248320] fp32: graph replay over R
+    rotated copies totalling >= 512 MiB (cold: every launch reads HBM) and
+    over one copy (hot: the 15.9 MB input stays in the memory-side cache);
+    torch.argmax(dim=1) in the same harness for context."""
+    import numpy as np
+    import torch
+
+    import moe_token_routing_amd as mr
+    import oracle
+
+    device = "cuda:0"
+    nbytes = ARGMAX_R * ARGMAX_N * 4
+    R = max(8, math.ceil(ROTATE_BYTES / nbytes))
+    x0 = argmax_input()
+    g = torch.Generator(device=device)
+    g.manual_seed(99)
+    copies = [torch.from_numpy(x0).to(device)] + [torch.randn(ARGMAX_R, ARGMAX_N, generator=g, device=device)
+                                                  for _ in range(R - 1)]
+    ws = mr.new_argmax_workspace(ARGMAX_R, ARGMAX_N, device=device)
+    out = torch.empty(ARGMAX_R, dtype=torch.int64, device=device)
+    got = mr.mr_argmax_rows_f32(copies[0], workspace=ws, out=out).cpu().numpy()
+    assert np.array_equal(got, oracle.argmax_rows(x0)), "argmax differs from the oracle"
+    stream = torch.cuda.Stream(device=device)
+    cur = torch.cuda.current_stream(device)
+
+    def timed(fn, n_rot):
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(n_rot):
+                fn(copies[i % R])
+        reps = max(1, steps // n_rot)
+        for _ in range(max(1, warmup // n_rot)):
+            graph.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(cur)
+        for _ in range(reps):
+            graph.replay()
+        e1.record(cur)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * n_rot), reps * n_rot
+
+    ours = lambda x: mr.mr_argmax_rows_f32(x, workspace=ws, out=out)  # noqa: E731
+    theirs = lambda x: torch.argmax(x, dim=1)  # noqa: E731
+    ms_cold, n_cold = timed(ours, R)
+    ms_hot, _ = timed(lambda x: ours(copies[0]), R)
+    ms_torch_cold, _ = timed(theirs, R)
+    ms_torch_hot, _ = timed(lambda x: theirs(copies[0]), R)
+    alg = nbytes + ARGMAX_R * 8
+    gbs = alg / (ms_cold * 1e-3) / 1e9
+    result = {
+        "metric": "row-wise fp32 argmax (PyTorch semantics) us/call at [16, 248320]",
+        "value": round(ms_cold * 1e3, 3),
+        "unit": "us/call",
+        "n_gpus": 1,
+        "steps": n_cold,
+        "warmup": warmup,
+        "ms_per_step": round(ms_cold, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "argmax_f32_r16_n248320", "R": ARGMAX_R, "N": ARGMAX_N, "rotation_copies": R,
+                   "timing": "HIP graph of launches over rotated inputs; HIP events on the launch stream"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": profiled_traffic("argmax_kernel", "argmax_f32_r16_n248320"), "kernel": "argmax_kernel",
+                     "bytes_per_launch": alg},
+        "hot_us": round(ms_hot * 1e3, 3),
+        "torch_argmax_us": {"cold": round(ms_torch_cold * 1e3, 3), "hot": round(ms_torch_hot * 1e3, 3)},
+    }
+    if cpu_seconds > 0:
+        threads = os.cpu_count() or 1
+        if os.environ.get("OMP_NUM_THREADS", "").isdigit():
+            threads = max(1, min(threads, int(os.environ["OMP_NUM_THREADS"])))
+        times = []
+        t0 = time.perf_counter()
+        while True:
+            t1 = time.perf_counter()
+            oracle.argmax_rows(x0, nthreads=threads)
+            times.append(time.perf_counter() - t1)
+            if time.perf_counter() - t0 >= cpu_seconds:
+                break
+        per = sorted(times)[len(times) // 2]
+        result["cpu_baseline"] = {"value": round(per * 1e6, 1), "unit": "us/call", "cores": threads, "kind": "oracle",
+                                  "sample": f"median of {len(times)} oracle argmax calls on the seeded "
+                                            f"[16, 248320] input, {time.perf_counter() - t0:.1f} s"}
+    return result
+
+
 def measure(wl, steps, warmup, A=None):
     """Times `steps` route+align launches on workload `wl`; returns the seeded
     input and the result fields."""
@@ -397,6 +510,13 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.workload == "argmax":
+        import moe_token_routing_amd as mr
+
+        mr._binding.lib()
+        torch.cuda.set_device(0)
+        print(json.dumps(measure_argmax(args.steps, args.warmup, args.cpu_seconds)), flush=True)
         return
     wl = workload(args.workload)
     if args.cpu_only:

@@ -276,8 +276,9 @@ int route_impl(const char *fn, const void *x, const void *gate_w, const void *sh
 
 }  // namespace
 
-// Argmax workspace: row tickets (own 256-byte region), then the [R, C] block keys.
-static size_t argmax_ticket_bytes(int64_t R) { return ((size_t)R * 4 + 255) / 256 * 256; }
+// Argmax workspace: one 256-byte slot per row ticket (tickets of different rows
+// in one line would serialise every block's atomic), then the [R, C] block keys.
+static size_t argmax_ticket_bytes(int64_t R) { return (size_t)R * mr::kArgmaxTicketStride * 4; }
 
 extern "C" {
 

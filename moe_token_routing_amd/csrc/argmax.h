@@ -8,14 +8,15 @@
 
 namespace mr {
 
-constexpr int kArgmaxU = 8;  // 16-byte loads per thread: a chunk is 256 * 8 * 4 = 8192 values
+constexpr int kArgmaxU = 4;  // 16-byte loads per thread: a chunk is 256 * 4 * 4 = 4096 values
+constexpr int kArgmaxTicketStride = 64;  // words between row tickets (256 bytes)
 
 struct ArgmaxParams {
   const float *x;  // [R, ld] fp32, 16-byte aligned, ld % 4 == 0
   int64_t R, N, ld;
   int64_t C;                 // chunks per row (argmax_chunks(N))
   int64_t *out;              // [R] indices
-  uint32_t *ticket;          // [R] zero between launches
+  uint32_t *ticket;          // [R] at stride kArgmaxTicketStride words, zero between launches
   unsigned long long *part;  // [R, C] block keys
 };
 

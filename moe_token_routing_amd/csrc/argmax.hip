@@ -4,9 +4,9 @@
 // (PyTorch's argmax): a NaN beats every number and the first NaN beats later
 // ones; among equal numbers the lowest index wins; -0 and +0 are equal.
 //
-// Launch shape: row r is cut into C chunks of 8192 values and block
+// Launch shape: row r is cut into C chunks of 4096 values and block
 // r * C + c scans chunk c, so a few long rows still fill the chip (the page's
-// point: [16, 248320] is 16 rows but 496 blocks here).  Every thread issues
+// point: [16, 248320] is 16 rows but 976 blocks here).  Every thread issues
 // its kArgmaxU 16-byte non-temporal loads at once, then keeps, in index order, the
 // first value that beats its current winner (plain float compares give -0 ==
 // +0 for free; a NaN is taken only when the winner is not one already).  The
@@ -17,10 +17,12 @@
 // LDS.
 //
 // Hand-off: with C > 1 each block writes its key with a write-through store,
-// waits for it, and takes a ticket on its row; in the block taking the row's
-// last ticket, the first wave reads the C keys with coherent loads (one per
-// lane), writes the index, and re-zeroes the ticket, so the workspace is
-// clean again for the next launch.
+// waits for it, and takes a ticket on its row (each row's ticket in its own
+// 256-byte slot: tickets sharing a line serialise every block's atomic, which
+// cost 5 us at [16, 248320]); in the block taking the row's last ticket, the
+// first wave reads the C keys with coherent loads (one per lane), writes the
+// index, and re-zeroes the ticket, so the workspace is clean again for the
+// next launch.
 #include "argmax.h"
 #include "device_common.h"
 
@@ -116,7 +118,7 @@ __global__ __launch_bounds__(kThreads) void argmax_kernel(ArgmaxParams p) {
   if (lane == 0) {
     st_agent(p.part + row * p.C + chunk, ((unsigned long long)hi << 32) | lo);
     wait_own_stores();
-    t = __hip_atomic_fetch_add(p.ticket + row, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    t = __hip_atomic_fetch_add(p.ticket + row * kArgmaxTicketStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   t = __builtin_amdgcn_readfirstlane(t);
   if (t != (uint32_t)p.C - 1u) return;
@@ -129,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void argmax_kernel(ArgmaxParams p) {
   wave_key_max(hi, lo, lane);
   if (lane == 0) {
     p.out[row] = (int64_t)(0xFFFFFFFFu - lo);
-    st_agent(p.ticket + row, 0u);
+    st_agent(p.ticket + row * kArgmaxTicketStride, 0u);
   }
 }
 

@@ -151,7 +151,7 @@ def test_argmax_refusals(lib):
     for needle in ["ld=8 < N=10", "x is not 16-byte aligned"]:
         assert needle in msg, (needle, msg)
     need = lib.mr_argmax_workspace_bytes(16, 248320)
-    assert need == 256 + 16 * 31 * 8
+    assert need == 16 * 256 + 16 * 61 * 8
     rc = lib.mr_argmax_rows_f32(p, 16, 248320, 248320, p, p, need - 8, None)
     assert rc == mr.MR_ECAPACITY and f"< {need}" in _err(lib)
     rc = lib.mr_argmax_rows_f32(p, 1, 1 << 31, 1 << 31, p, p, 1 << 40, None)

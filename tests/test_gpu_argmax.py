@@ -11,7 +11,7 @@ import oracle
 
 pytestmark = pytest.mark.gpu
 
-CHUNK = 8192  # values per block of the kernel
+CHUNK = 4096  # values per block of the kernel
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -123,7 +123,7 @@ def test_argmax_full_size_and_relaunch():
         assert np.array_equal(got, oracle.argmax_rows(x))
     import torch
 
-    tickets = ws[: 4 * R].view(torch.int32)  # the block keys may stay; the tickets must be zero
+    tickets = ws[: 256 * R].view(torch.int32)  # the block keys may stay; the ticket slots must be zero
     assert int(tickets.abs().sum().item()) == 0
 
 
