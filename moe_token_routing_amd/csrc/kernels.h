@@ -35,7 +35,14 @@ enum CounterIndex : int {
 constexpr int kTicketLanes = 16;
 constexpr int kTicketLaneStride = 64;  // words (256 bytes); set s of lane r at word 64 + 64 r + 32 s
 constexpr int kReleaseWord = 8;        // words after a lane counter: its barrier release word
-constexpr size_t kCounterBytes = 256 + (size_t)kTicketLanes * kTicketLaneStride * 4;
+// Then the prefill route's tile-ready counters: set s of token tile t at word
+// kReadyBase + (2 t + s) * kReadyStride, each in its own 128-byte slot (items
+// of different tiles arriving on one line would serialise).  Launches with
+// more than kMaxReadyTiles token tiles use a grid barrier instead.
+constexpr int kMaxReadyTiles = 256;
+constexpr int kReadyStride = 32;  // words
+constexpr int kReadyBase = 64 + kTicketLanes * kTicketLaneStride;
+constexpr size_t kCounterBytes = (size_t)(kReadyBase + 2 * kMaxReadyTiles * kReadyStride) * 4;
 
 // Small-M fused route (+ align).
 struct SmallParams {
@@ -106,6 +113,7 @@ struct MfmaParams {
   int tcnt_row;         // words per tcnt row: Ep rounded up to 4
   const uint4 *zero16;  // 16 zero bytes (stands in for k past H): kCtrZero16 of the counters
   uint32_t *ctr;        // counter words
+  int tile_wait;        // top-k groups wait for their own tile's items only (2 <= NT <= kMaxReadyTiles, with align)
   int tpb, ngroups;     // tokens per top-k group (power of two <= 128) and groups
   int do_align, A, log2A;
   int32_t *sorted;

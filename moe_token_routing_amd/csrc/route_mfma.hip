@@ -187,6 +187,35 @@ __device__ __forceinline__ void grid_barrier(uint32_t *ctr, uint32_t set, uint32
   grid_wait(ctr, set, gen, grid);
 }
 
+// Tile-ready counter of token tile t in counter set `set` (zero at launch
+// start): every gate item of the tile takes one after its partial tile and
+// its share of the tile's counter-row clear have completed.
+__device__ __forceinline__ uint32_t *tile_ready(uint32_t *ctr, uint32_t set, int t) {
+  return ctr + kReadyBase + (size_t)(2 * t + (int)set) * kReadyStride;
+}
+__device__ __forceinline__ void tile_arrive(uint32_t *ctr, uint32_t set, int t) {
+  wait_own_stores();
+  __syncthreads();
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(tile_ready(ctr, set, t), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Waits until all `count` items of token tile t have arrived (bounded, like
+// grid_wait).  Every thread of the block must call it.
+__device__ __forceinline__ void tile_wait(uint32_t *ctr, uint32_t set, int t, uint32_t count) {
+  if (threadIdx.x == 0) {
+    uint32_t *r = tile_ready(ctr, set, t);
+    int it = 0;
+    while (__hip_atomic_load(r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < count) {
+      if (++it == kBarrierSpin) {
+        __hip_atomic_store(ctr + kCtrError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  __syncthreads();
+}
+
 // ------------------------------------------------------------- phase G ---
 
 __device__ void gate_item(const MfmaParams &p, uint8_t *smem, int et, int tt, int sp) {
@@ -697,29 +726,45 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(MfmaParams p) {
   // first barrier arrival, and block 0 advances it only after the last
   // barrier, so all blocks agree on the set.
   uint32_t set = 0;
-  if (threadIdx.x == 0 || (b == 0 && threadIdx.x <= kTicketLanes)) set = ld_agent(p.ctr + kCtrEpoch) & 1u;
-  if (b == 0 && threadIdx.x < kTicketLanes + 1) {
+  if (threadIdx.x == 0 || b == 0) set = ld_agent(p.ctr + kCtrEpoch) & 1u;
+  if (b == 0) {
     if (threadIdx.x < kTicketLanes) {
       __hip_atomic_store(barrier_lane(p.ctr, set ^ 1u, threadIdx.x), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(barrier_release(p.ctr, set ^ 1u, threadIdx.x), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
+    } else if (threadIdx.x == kTicketLanes) {
       __hip_atomic_store(barrier_top(p.ctr, set ^ 1u), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    for (int t = threadIdx.x; t < kMaxReadyTiles; t += kThreads)
+      __hip_atomic_store(tile_ready(p.ctr, set ^ 1u, t), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // ---- G: gate partials -------------------------------------------------
-  // the tile counters start from zero in every launch (the workspace layout
-  // moves with M, so nothing else may be assumed about this region)
-  if (p.do_align && !p.logits_only)
+  // The tile counters start from zero in every launch (the workspace layout
+  // moves with M, so nothing else may be assumed about this region).  With
+  // tile waits, the items of a token tile clear that tile's counter row
+  // (each its share) before they arrive; otherwise every block clears a
+  // slice and the grid barrier orders the clear before the top-k phase.
+  const bool clear_tcnt = p.do_align && !p.logits_only;
+  if (clear_tcnt && !p.tile_wait)
     for (int i = b * kThreads + threadIdx.x; i < p.NT * p.tcnt_row; i += (int)grid * kThreads)
       __hip_atomic_fetch_and(p.tcnt + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int per_xcd = p.xcd_map ? (int)grid / 8 : 0;
   const int lmap = p.xcd_map ? (b % 8) * per_xcd + b / 8 : b;
+  const int tile_items = p.NE * p.SK;
   for (int it = 0;; ++it) {
     const int L = it * (int)grid + lmap;
     if (L >= p.items) break;
     const int et = L % p.NE, sp = (L / p.NE) % p.SK, tt = L / (p.NE * p.SK);
     gate_item(p, smem, et, tt, sp);
+    if (p.tile_wait) {
+      if (clear_tcnt) {
+        const int share = (p.tcnt_row + tile_items - 1) / tile_items, q = sp * p.NE + et;
+        const int i1 = min(p.tcnt_row, (q + 1) * share);
+        for (int i = q * share + threadIdx.x; i < i1; i += kThreads)
+          __hip_atomic_fetch_and(p.tcnt + (size_t)tt * p.tcnt_row + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      tile_arrive(p.ctr, set, tt);
+    }
   }
   // phases T and A: block b takes token group lmap (+ grid, ...), so a
   // group's partial rows were written by blocks of its own XCD
@@ -744,11 +789,11 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(MfmaParams p) {
       touch = ld_agent(a);
     }
   }
-  grid_arrive(p.ctr, set, 1, grid);
   // The shared logits of the block's first token group need only x and the
-  // shared gate row: they are computed while the other blocks arrive.
+  // shared gate row: they are computed while the other blocks' items finish.
+  if (!p.tile_wait) grid_arrive(p.ctr, set, 1, grid);
   if (p.has_shared && gb < p.ngroups) shared_logits(p, gb * p.tpb, min(p.M, gb * p.tpb + p.tpb), sh_first);
-  grid_wait(p.ctr, set, 1, grid);
+  if (!p.tile_wait) grid_wait(p.ctr, set, 1, grid);
   if (touch == 0xFFFFFFFFu && threadIdx.x == 1000) p.npp[0] = 0;  // never true
 
   // ---- T: logits, top-k, weights ----------------------------------------
@@ -759,9 +804,13 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(MfmaParams p) {
   // A block owns more than one group only for M > 128 * grid; then `own`
   // holds one group at a time and is reloaded in phase A.
   const bool multi = (int)grid < p.ngroups;
-  for (int g = gb; g < p.ngroups; g += grid) topk_group<NKP>(p, own, g, (p.has_shared && g == gb) ? sh_first : nullptr);
+  for (int g = gb; g < p.ngroups; g += grid) {
+    // with tile waits, a group starts once its own token tile's items are in
+    if (p.tile_wait) tile_wait(p.ctr, set, (g * p.tpb) >> 7, (uint32_t)tile_items);
+    topk_group<NKP>(p, own, g, (p.has_shared && g == gb) ? sh_first : nullptr);
+  }
   if (align) {
-    grid_barrier(p.ctr, set, 2, grid);
+    grid_barrier(p.ctr, set, p.tile_wait ? 1 : 2, grid);
     uint32_t npp = 0;
     if (!multi) {
       npp = align_group(p, gb, own, smem, scan_tmp);
