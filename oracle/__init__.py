@@ -62,6 +62,8 @@ def _load():
     lib.or_round_bf16_array.restype = None
     lib.or_bf16_value_array.argtypes = [P, P, i64]
     lib.or_bf16_value_array.restype = None
+    lib.or_align_local.argtypes = [P, i32, i32, i32, P, i32, i32, P, i64, P, i64, P]
+    lib.or_align_local.restype = i32
     lib.or_argmax_rows.argtypes = [P, i64, i64, i64, P, i32]
     lib.or_argmax_rows.restype = i32
     _lib = lib
@@ -179,6 +181,27 @@ def align(topk_ids, num_experts: int, A: int, sorted_cap: int | None = None,
                           _ptr(eids), expert_cap, _ptr(npp))
     if rc != 0:
         raise ValueError(f"or_align failed ({rc})")
+    n = int(npp[0])
+    return srt[:n].copy(), eids[: n // A].copy(), n
+
+
+def align_local(topk_ids, expert_map, num_local: int, A: int):
+    """Align of one expert-parallel rank: expert_map [E'] gives each global
+    expert's local id or -1; returns (sorted_token_ids[:npp],
+    expert_ids[:npp // A] as local ids, npp)."""
+    ids = np.ascontiguousarray(topk_ids, dtype=np.int32)
+    if ids.ndim == 1:
+        ids = ids.reshape(-1, 1)
+    emap = np.ascontiguousarray(expert_map, dtype=np.int32)
+    M, S = ids.shape
+    cap = align_capacity(M, S, num_local, A)
+    srt = np.full(max(1, cap), -7, dtype=np.int32)
+    eids = np.full(max(1, cap // A), -7, dtype=np.int32)
+    npp = np.zeros(1, dtype=np.int32)
+    rc = _load().or_align_local(_ptr(ids), M, S, emap.size, _ptr(emap), num_local, A, _ptr(srt), cap,
+                                _ptr(eids), max(1, cap // A), _ptr(npp))
+    if rc != 0:
+        raise ValueError(f"or_align_local failed ({rc})")
     n = int(npp[0])
     return srt[:n].copy(), eids[: n // A].copy(), n
 

@@ -39,6 +39,14 @@
  *                      expert, each touched expert padded to a multiple of A;
  *                      npp = sum over touched experts of ceil(c_e/A)*A ([A]
  *                      Purpose).
+ *   or_align_local     the align of one expert-parallel rank: each pair's
+ *                      global expert id goes through the rank's expert map
+ *                      (its local id, or -1 for an expert another rank
+ *                      owns) and the pairs of local experts are aligned by
+ *                      local id as or_align does; non-local pairs are
+ *                      skipped.  (The design the scope table's EP row
+ *                      describes; the pages themselves run the router
+ *                      replicated, [R] Motivation.)
  *   or_argmax_rows     row-wise argmax of an fp32 matrix with PyTorch's
  *                      semantics as [N] Sampling states them: a NaN beats
  *                      every number and the first NaN beats later ones; among
@@ -366,6 +374,29 @@ int or_align(const int32_t *ids, int M, int S, int Eprime, int A,
     free(cnt);
     free(off);
     return OR_OK;
+}
+
+/* Align of one expert-parallel rank (see the header): map, then or_align
+ * over the local experts.  Global ids outside [0, Eglobal) and map entries
+ * outside [0, Elocal) are not local. */
+int or_align_local(const int32_t *ids, int M, int S, int Eglobal, const int32_t *map, int Elocal,
+                   int A, int32_t *sorted, int64_t sorted_cap, int32_t *expert_ids,
+                   int64_t expert_cap, int32_t *npp_out)
+{
+    if (M < 0 || S < 1 || Eglobal < 1 || Elocal < 1)
+        return OR_EINVAL;
+    const int64_t n = (int64_t)M * S;
+    int32_t *loc = (int32_t *)malloc((size_t)(n > 0 ? n : 1) * sizeof(int32_t));
+    if (!loc)
+        return OR_EINVAL;
+    for (int64_t i = 0; i < n; ++i) {
+        const int32_t e = ids[i];
+        const int32_t l = (e >= 0 && e < Eglobal) ? map[e] : -1;
+        loc[i] = (l >= 0 && l < Elocal) ? l : -1;
+    }
+    const int rc = or_align(loc, M, S, Elocal, A, sorted, sorted_cap, expert_ids, expert_cap, npp_out);
+    free(loc);
+    return rc;
 }
 
 /* ------------------------------------------------------- array helpers -- */

@@ -518,3 +518,53 @@ def test_argmax_matches_torch_and_numpy():
     assert np.array_equal(got, np.argmax(x, axis=1))
     # thread count does not change the result
     assert np.array_equal(got, oracle.argmax_rows(x, nthreads=1))
+
+
+# ------------------------------------------------------- EP-local align --
+
+def test_align_local_identity_map_is_align():
+    # every expert local under its own id: the plain align, already pinned
+    rng = np.random.default_rng(11)
+    for (M, S, E, A) in [(37, 9, 65, 16), (300, 11, 257, 64), (5, 3, 4, 128)]:
+        ids = rng.integers(0, E, size=(M, S)).astype(np.int32)
+        got = oracle.align_local(ids, np.arange(E, dtype=np.int32), E, A)
+        want = oracle.align(ids, E, A)
+        assert got[2] == want[2] and np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
+
+
+def test_align_local_hand_case():
+    # 8 global experts, this rank owns 2 -> 0 and 5 -> 1; flat pairs
+    # i = 0..5 carry experts 2, 5, 5, 7, 0, 2
+    ids = np.array([[2, 5], [5, 7], [0, 2]], np.int32)
+    emap = np.full(8, -1, np.int32)
+    emap[2], emap[5] = 0, 1
+    srt, eids, npp = oracle.align_local(ids, emap, 2, 16)
+    assert npp == 32 and eids.tolist() == [0, 1]
+    assert srt[:2].tolist() == [0, 5] and set(srt[2:16].tolist()) == {6}
+    assert srt[16:18].tolist() == [1, 2] and set(srt[18:].tolist()) == {6}
+
+
+def test_align_local_nothing_local():
+    ids = np.arange(12, dtype=np.int32).reshape(4, 3) % 7
+    srt, eids, npp = oracle.align_local(ids, np.full(7, -1, np.int32), 3, 64)
+    assert npp == 0 and srt.size == 0 and eids.size == 0
+
+
+def test_align_local_partition_covers_every_pair():
+    # split E' experts over 4 ranks: every flat index lands on exactly one
+    # rank, and each rank's npp is its own closed form
+    rng = np.random.default_rng(3)
+    M, S, E, A, ranks = 64, 9, 33, 16, 4
+    ids = rng.integers(0, E, size=(M, S)).astype(np.int32)
+    owner = rng.integers(0, ranks, size=E)
+    seen = []
+    for r in range(ranks):
+        local = np.flatnonzero(owner == r)
+        emap = np.full(E, -1, np.int32)
+        emap[local] = np.arange(local.size, dtype=np.int32)
+        srt, eids, npp = oracle.align_local(ids, emap, max(1, local.size), A)
+        counts = [int((ids == e).sum()) for e in local]
+        assert npp == sum(-(-c // A) * A for c in counts if c)
+        seen += [int(v) for v in srt if v != M * S]
+        assert all(owner[ids.reshape(-1)[v]] == r for v in srt if v != M * S)
+    assert sorted(seen) == list(range(M * S))

@@ -34,6 +34,8 @@ MUTATIONS = {
                              "for (int64_t b = off[e] / A + 1; b <= (off[e] + padded) / A && b < expert_cap; ++b)"),
     "tier_strict": ("((int64_t)M * k >= (int64_t)128 * E)", "((int64_t)M * k > (int64_t)128 * E)"),
     "tier_uses_slots": ("((int64_t)M * k >= (int64_t)128 * E)", "((int64_t)M * (k + 1) >= (int64_t)128 * E)"),
+    "align_local_ignores_map": ("const int32_t l = (e >= 0 && e < Eglobal) ? map[e] : -1;", "const int32_t l = (e >= 0 && e < Eglobal) ? e : -1;"),
+    "align_local_map_off_by_one": ("const int32_t l = (e >= 0 && e < Eglobal) ? map[e] : -1;", "const int32_t l = (e >= 1 && e < Eglobal) ? map[e - 1] : -1;"),
     "argmax_ties_last": ("if (isnan(v) || v > b)", "if (isnan(v) || v >= b)"),
     "argmax_last_nan": ("            if (isnan(b))\n                break; /* the first NaN has won the row */\n", ""),
     "argmax_nan_loses": ("if (isnan(v) || v > b)", "if (v > b)"),
