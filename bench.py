@@ -37,10 +37,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=8192)
     ap.add_argument("--warmup", type=int, default=512)
-    ap.add_argument("--workload", default="m4", choices=[f"m{m}" for m in SWEEP_M] + ["c3", "c4", "argmax"],
+    ap.add_argument("--workload", default="m4", choices=[f"m{m}" for m in SWEEP_M] + ["c3", "c4", "argmax", "align_ep"],
                     help="m<M>: E=512+1, H=4096, k=10 at M tokens (m4 is the headline); c3: E=128, H=2048, "
                          "k=8, M=128; c4: the same at M=2048 with Zipf-skewed gate rows; argmax: row-wise fp32 "
-                         "argmax of [16, 248320] (the sampling shape)")
+                         "argmax of [16, 248320] (the sampling shape); align_ep: mr_align over all 513 experts vs "
+                         "mr_align_local for one of 8 expert-parallel ranks, on M=2048 routing ids")
     ap.add_argument("--align", type=int, default=None, choices=[64, 128],
                     help="force the alignment A (default: the M-aware tier)")
     ap.add_argument("--method", default="rotate", choices=["rotate", "memset"],
@@ -436,6 +437,83 @@ def measure_argmax(steps, warmup, cpu_seconds):
     return result
 
 
+def measure_align_ep(steps, warmup):
+    """Times the align alone on M=2048 tokens x (10 routed + 1 shared) ids
+    over E' = 513 experts (seeded: distinct routed experts per token, the
+    shared expert id 512 in the last column): mr_align over every expert,
+    and mr_align_local for rank 0 of 8 (routed experts e with e % 8 == 0,
+    the shared expert replicated).  Graph replay, HIP events."""
+    import numpy as np
+    import torch
+
+    import moe_token_routing_amd as mr
+    import oracle
+
+    device = "cuda:0"
+    M, k, E, ranks = 2048, 10, 512, 8
+    rng = np.random.default_rng(0)
+    ids = np.empty((M, k + 1), np.int32)
+    for m in range(M):
+        ids[m, :k] = rng.choice(E, k, replace=False)
+    ids[:, k] = E
+    emap = np.full(E + 1, -1, np.int32)
+    own = np.arange(0, E, ranks)
+    emap[own] = np.arange(own.size, dtype=np.int32)
+    emap[E] = own.size
+    A = mr.mr_select_alignment(M, k, E)
+    t_ids = torch.from_numpy(ids).to(device)
+    t_map = torch.from_numpy(emap).to(device)
+    ws_full = mr.new_workspace(M, E + 1, k + 1, False, device=device)
+    ws_loc = mr.new_workspace(M, own.size + 1, k + 1, False, device=device)
+    full = mr.mr_align(t_ids, E + 1, A, workspace=ws_full)
+    loc = mr.mr_align_local(t_ids, t_map, own.size + 1, A, workspace=ws_loc)
+    torch.cuda.synchronize()
+    for (srt, eids, npp), want in ((full, oracle.align(ids, E + 1, A)), (loc, oracle.align_local(ids, emap, own.size + 1, A))):
+        n = int(npp.item())
+        assert n == want[2] and np.array_equal(srt[:n].cpu().numpy(), want[0]), "align differs from the oracle"
+    stream = torch.cuda.Stream(device=device)
+    cur = torch.cuda.current_stream(device)
+
+    def timed(fn):
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(32):
+                fn()
+        for _ in range(max(1, warmup // 32)):
+            g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, steps // 32)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(cur)
+        for _ in range(reps):
+            g.replay()
+        e1.record(cur)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * 32) * 1e3
+
+    us_full = timed(lambda: mr.mr_align(t_ids, E + 1, A, workspace=ws_full, sorted_token_ids=full[0],
+                                        expert_ids=full[1], npp=full[2]))
+    us_loc = timed(lambda: mr.mr_align_local(t_ids, t_map, own.size + 1, A, workspace=ws_loc,
+                                             sorted_token_ids=loc[0], expert_ids=loc[1], npp=loc[2]))
+    npp_full, npp_loc = int(full[2].item()), int(loc[2].item())
+    nbytes = M * (k + 1) * 4 + 4 * npp_full + 4 * (npp_full // A) + 4
+    gbs = nbytes / (us_full * 1e-6) / 1e9
+    return {
+        "metric": "standalone align us/call at M=2048, E'=513, S=11 (all experts / one of 8 EP ranks)",
+        "value": round(us_full, 3), "unit": "us/call", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(us_full * 1e-3, 6), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int32", "data": "synthetic",
+        "config": {"workload": "align_m2048_e513_s11", "A": A, "npp": npp_full, "local_rank_npp": npp_loc,
+                   "timing": "HIP graph of 32 launches, HIP events on the launch stream"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "align_kernel",
+                     "bytes_per_launch": nbytes},
+        "local_rank_us": round(us_loc, 3),
+    }
+
+
 def measure(wl, steps, warmup, A=None):
     """Times `steps` route+align launches on workload `wl`; returns the seeded
     input and the result fields."""
@@ -517,6 +595,13 @@ def main():
         mr._binding.lib()
         torch.cuda.set_device(0)
         print(json.dumps(measure_argmax(args.steps, args.warmup, args.cpu_seconds)), flush=True)
+        return
+    if args.workload == "align_ep":
+        import moe_token_routing_amd as mr
+
+        mr._binding.lib()
+        torch.cuda.set_device(0)
+        print(json.dumps(measure_align_ep(args.steps, args.warmup)), flush=True)
         return
     wl = workload(args.workload)
     if args.cpu_only:

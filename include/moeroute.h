@@ -137,6 +137,23 @@ int mr_align(const int32_t *topk_ids, int32_t M, int32_t S, int32_t num_experts,
              int32_t *expert_ids, int64_t expert_cap, int32_t *npp,
              void *ws, size_t ws_bytes, void *stream);
 
+/* The align of one expert-parallel rank: as mr_align, but each pair's global
+ * expert id e (0 <= e < num_experts_global) is first replaced by
+ * expert_map[e], the rank's local id of that expert, or -1 when another rank
+ * owns it; pairs with -1 (or any map entry outside [0, num_local_experts),
+ * or a global id outside [0, num_experts_global)) are skipped, and the pairs
+ * of local experts are grouped and padded by local id exactly as mr_align
+ * does (expert_ids hold local ids, padding holds M*S).  This is the
+ * single-GPU part of expert-parallel routing: each rank aligns only the
+ * pairs its experts serve.  expert_map: device, [num_experts_global] int32,
+ * caller-owned.  Capacities and the workspace are those of mr_align with
+ * num_experts = num_local_experts.  Errors as mr_align, plus MR_EINVAL for a
+ * NULL expert_map or num_experts_global < 1. */
+int mr_align_local(const int32_t *topk_ids, int32_t M, int32_t S, int32_t num_experts_global,
+                   const int32_t *expert_map, int32_t num_local_experts, int32_t A,
+                   int32_t *sorted_token_ids, int64_t sorted_cap, int32_t *expert_ids,
+                   int64_t expert_cap, int32_t *npp, void *ws, size_t ws_bytes, void *stream);
+
 /* Route followed by align, in ONE launch: the arguments of mr_route plus
  * the alignment A (pass mr_select_alignment(M, k, E) for the M-aware tier)
  * and the align outputs.  num_experts is E + (shared_w != NULL). */

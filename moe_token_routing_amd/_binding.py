@@ -35,6 +35,8 @@ SIGNATURES = {
     "mr_workspace_reset": (ctypes.c_int, [_P, _SZ, _P]),
     "mr_route": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _F32, _P, _P, _P, _SZ, _P]),
     "mr_align": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _P, _I64, _P, _I64, _P, _P, _SZ, _P]),
+    "mr_align_local": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _I32, _I32, _P, _I64, _P, _I64, _P, _P, _SZ,
+                                      _P]),
     "mr_route_align": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _F32, _I32, _P, _P, _P, _I64,
                                       _P, _I64, _P, _P, _SZ, _P]),
     "mr_debug_gate_logits": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _P, _P, _SZ, _P]),
@@ -189,6 +191,30 @@ def mr_align(topk_ids, num_experts: int, A: int, *, workspace, sorted_token_ids=
     _check(lib().mr_align(_ptr(topk_ids), M, S, num_experts, A, _ptr(sorted_token_ids),
                           sorted_token_ids.numel(), _ptr(expert_ids), expert_ids.numel(), _ptr(npp),
                           _ptr(workspace), workspace.numel(), _stream(stream, topk_ids.device)))
+    return sorted_token_ids, expert_ids, npp
+
+
+def mr_align_local(topk_ids, expert_map, num_local_experts: int, A: int, *, workspace, sorted_token_ids=None,
+                   expert_ids=None, npp=None, stream=None):
+    """The align of one expert-parallel rank: expert_map (int32 device tensor
+    [E'], local id or -1 per global expert) selects and renumbers the pairs.
+    Returns (sorted_token_ids, expert_ids, npp) as device tensors; entries at
+    or past npp are unspecified."""
+    import torch
+
+    if topk_ids.dtype != torch.int32 or not topk_ids.is_contiguous():
+        raise ValueError("topk_ids must be a contiguous int32 tensor")
+    if expert_map.dtype != torch.int32 or not expert_map.is_contiguous():
+        raise ValueError("expert_map must be a contiguous int32 tensor")
+    ids2 = topk_ids.view(topk_ids.shape[0], -1) if topk_ids.dim() >= 1 and topk_ids.numel() else topk_ids
+    M = topk_ids.shape[0] if topk_ids.dim() else 0
+    S = ids2.shape[1] if ids2.dim() == 2 else 1
+    sorted_token_ids, expert_ids, npp = _align_outputs(M, S, num_local_experts, A, topk_ids.device,
+                                                       sorted_token_ids, expert_ids, npp)
+    _check(lib().mr_align_local(_ptr(topk_ids), M, S, expert_map.numel(), _ptr(expert_map), num_local_experts, A,
+                                _ptr(sorted_token_ids), sorted_token_ids.numel(), _ptr(expert_ids),
+                                expert_ids.numel(), _ptr(npp), _ptr(workspace), workspace.numel(),
+                                _stream(stream, topk_ids.device)))
     return sorted_token_ids, expert_ids, npp
 
 

@@ -5,6 +5,8 @@
 // expert, each touched expert padded to a multiple of A, so that
 // num_tokens_post_padded = sum over touched experts of ceil(c_e / A) * A.
 // Inside an expert, pairs keep ascending flat index; padding holds M*S.
+// With an expert map (one expert-parallel rank), each pair's expert is its
+// local id and pairs of other ranks' experts are skipped.
 //
 // Launch shape: one block of 256 threads per chunk of 64*W pairs.
 //   Phase one (every block): per-expert bitmaps of the chunk's pairs in LDS
@@ -28,6 +30,14 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Expert of pair i as the align sees it: its id, or with an expert map its
+// local id (-1 for an expert another rank owns or an id outside the map).
+__device__ __forceinline__ int32_t pair_expert(const AlignParams &p, int64_t i) {
+  const int32_t e = p.ids[i];
+  if (!p.map) return e;
+  return (uint32_t)e < (uint32_t)p.Eg ? p.map[e] : -1;
+}
+
 __global__ __launch_bounds__(kThreads) void align_kernel(AlignParams p) {
   extern __shared__ uint64_t smem[];
   __shared__ uint32_t flag, slot;
@@ -48,7 +58,7 @@ __global__ __launch_bounds__(kThreads) void align_kernel(AlignParams p) {
     for (int j = tid; j < Ep * W; j += kThreads) bm[j] = 0ull;
     __syncthreads();
     for (int64_t i = lo + tid; i < hi; i += kThreads) {
-      const int32_t e = p.ids[i];
+      const int32_t e = pair_expert(p, i);
       if (e >= 0 && e < Ep) {
         const int li = (int)(i - lo);
         atomicOr(reinterpret_cast<unsigned long long *>(&bm[(size_t)e * W + (li >> 6)]), 1ull << (li & 63));
@@ -61,11 +71,11 @@ __global__ __launch_bounds__(kThreads) void align_kernel(AlignParams p) {
         pre[(size_t)e * W + w] = (uint16_t)run;
         run += __popcll(bm[(size_t)e * W + w]);
       }
-      st_agent(p.counts + (size_t)c * Ep + e, (int32_t)run);
+      st_agent(p.counts + (size_t)c * p.cstride + e, (int32_t)run);
     }
     __syncthreads();
     for (int64_t i = lo + tid; i < hi; i += kThreads) {
-      const int32_t e = p.ids[i];
+      const int32_t e = pair_expert(p, i);
       if (e >= 0 && e < Ep) {
         const int li = (int)(i - lo);
         const size_t j = (size_t)e * W + (li >> 6);
@@ -81,30 +91,67 @@ __global__ __launch_bounds__(kThreads) void align_kernel(AlignParams p) {
   const bool winner = last_block_ticket(&ctr[kCtrDone], gridDim.x, &flag);
   bool help = winner;
   if (winner) {
-    const int nch = p.nchunks;
-    const int per = (Ep + kThreads - 1) / kThreads;
-    const int e0 = tid * per;
-    uint32_t local = 0;
-    for (int e = e0; e < e0 + per && e < Ep; ++e) {
-      uint32_t tot = 0;
-      for (int c = 0; c < nch; ++c) tot += (uint32_t)ld_agent(p.counts + (size_t)c * Ep + e);
-      local += (tot + A - 1) / A * A;
-    }
-    uint32_t total;
-    uint32_t base = block_excl_scan_u32<kThreads>(local, scan_tmp, &total);
-    for (int e = e0; e < e0 + per && e < Ep; ++e) {
-      uint32_t run = base;
-      for (int c = 0; c < nch; ++c) {
-        const uint32_t t = (uint32_t)ld_agent(p.counts + (size_t)c * Ep + e);
-        st_agent(p.counts + (size_t)c * Ep + e, (int32_t)run);
-        run += t;
+    // Thread t owns the 4-expert column group g = t (+ 256, ...) of the
+    // [nchunks, cstride] count table and reads it with 16-byte coherent
+    // loads, 16 chunk rows per batch: the padded totals, one block scan for
+    // the expert offsets (carried across column rounds), expert_ids, then a
+    // second batched pass that turns each chunk's counts into its bases.
+    const int nch = p.nchunks, cs = p.cstride, ncol = cs / 4;
+    uint32_t carry = 0;
+    for (int g0 = 0; g0 < ncol; g0 += kThreads) {  // block-uniform
+      const int g = g0 + tid;
+      const bool has = g < ncol;
+      const u32x4_coh *col = reinterpret_cast<const u32x4_coh *>(p.counts) + (has ? g : 0);
+      uint32_t tot[4] = {0u, 0u, 0u, 0u};
+      for (int c0 = 0; c0 < nch; c0 += 16) {
+        const u32x4_coh *a[16];
+        u32x4_coh v[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) a[j] = col + (size_t)min(c0 + j, nch - 1) * ncol;
+        ld_coherent16(v, a);
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (c0 + j < nch)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tot[i] += v[j][i];
       }
-      const uint32_t P = (run - base + A - 1) / A * A;
-      for (uint32_t b = base / A; b < (base + P) / A; ++b)
-        if (b < (uint64_t)p.expert_cap) p.expert_ids[b] = e;
-      base += P;
+      uint32_t P[4], run = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        P[i] = (has && 4 * g + i < Ep) ? (tot[i] + A - 1) / A * A : 0u;
+        run += P[i];
+      }
+      uint32_t total;
+      uint32_t base = carry + block_excl_scan_u32<kThreads>(run, scan_tmp, &total);
+      carry += total;
+      uint32_t b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        b[i] = base;
+        if (P[i] > 0u)
+          for (uint32_t blk = base / A; blk < (base + P[i]) / A; ++blk)
+            if (blk < (uint64_t)p.expert_cap) p.expert_ids[blk] = 4 * g + i;
+        base += P[i];
+      }
+      if (has)
+        for (int c0 = 0; c0 < nch; c0 += 16) {
+          const u32x4_coh *a[16];
+          u32x4_coh v[16];
+#pragma unroll
+          for (int j = 0; j < 16; ++j) a[j] = col + (size_t)min(c0 + j, nch - 1) * ncol;
+          ld_coherent16(v, a);
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            if (c0 + j < nch)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (4 * g + i < Ep) {
+                  st_agent(p.counts + (size_t)(c0 + j) * cs + 4 * g + i, (int32_t)b[i]);
+                  b[i] += v[j][i];
+                }
+        }
     }
-    if (tid == 0) *p.npp = (int32_t)total;
+    if (tid == 0) *p.npp = (int32_t)carry;
     publish(&ctr[kCtrPublished]);
   } else {
     help = join_after_publish(&ctr[kCtrStarted], gridDim.x, &ctr[kCtrPublished], &flag);
@@ -117,11 +164,28 @@ __global__ __launch_bounds__(kThreads) void align_kernel(AlignParams p) {
       if (c >= (uint32_t)p.nchunks) break;
       const int64_t lo = c * CH;
       const int64_t hi = min(p.n, lo + CH);
-      for (int64_t i = lo + tid; i < hi; i += kThreads) {
-        const int32_t e = p.ids[i];
-        if (e < 0 || e >= Ep) continue;
-        const int64_t pos = (int64_t)ld_agent(p.counts + (size_t)c * Ep + e) + ld_agent(p.ranks + i);
-        if (pos < p.sorted_cap) p.sorted[pos] = (int32_t)i;
+      // four pairs per thread per round: their base and rank loads (eight
+      // coherent loads) are in flight together
+      for (int64_t i0 = lo + tid; i0 < hi; i0 += 4 * kThreads) {
+        int32_t ev[4];
+        const uint32_t *a[8];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int64_t i = i0 + (int64_t)u * kThreads;
+          const int32_t e = i < hi ? pair_expert(p, i) : -1;
+          const bool ok = e >= 0 && e < Ep;
+          ev[u] = ok ? e : -1;
+          a[2 * u] = reinterpret_cast<const uint32_t *>(p.counts) + (ok ? (size_t)c * p.cstride + e : 0);
+          a[2 * u + 1] = reinterpret_cast<const uint32_t *>(p.ranks) + (ok ? i : 0);
+        }
+        uint32_t v[8];
+        ld_coherent8(v, a);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (ev[u] < 0) continue;
+          const int64_t pos = (int64_t)v[2 * u] + v[2 * u + 1];
+          if (pos < p.sorted_cap) p.sorted[pos] = (int32_t)(i0 + (int64_t)u * kThreads);
+        }
       }
     }
   }

@@ -86,7 +86,7 @@ Layout layout_for(int64_t M, int64_t E, int64_t k, int64_t sh) {
   L.shared = take(o, (size_t)mr::kSmallMaxTokens * 8);
   const int W = mr::align_words_per_expert((int)(Ep > 0 ? Ep : 1));
   const int64_t nch = (n + 64 * W - 1) / (64 * W);
-  L.counts = take(o, (size_t)(nch * Ep) * 4);
+  L.counts = take(o, (size_t)(nch * ((Ep + 3) / 4 * 4)) * 4);
   L.ranks = take(o, (size_t)n * 4);
   // split-K partials: for any M' <= M, splits * M' <= max(M, (grid / NE) * min(M, 128))
   const int64_t Epad = (E + 3) / 4 * 4;
@@ -407,10 +407,12 @@ int mr_debug_stream_read(const void *src, size_t nbytes, uint32_t *out, void *st
                        "mr_debug_stream_read");
 }
 
-int mr_align(const int32_t *topk_ids, int32_t M, int32_t S, int32_t num_experts, int32_t A,
-             int32_t *sorted_token_ids, int64_t sorted_cap, int32_t *expert_ids, int64_t expert_cap, int32_t *npp,
-             void *ws, size_t ws_bytes, void *stream) {
-  Checks ck;
+// Shared implementation of mr_align and mr_align_local: num_experts is the
+// number of experts the align groups by (local experts with a map).
+static int align_impl(const char *fn, const int32_t *topk_ids, int32_t M, int32_t S, const int32_t *expert_map,
+                      int32_t num_global, int32_t num_experts, int32_t A, int32_t *sorted_token_ids,
+                      int64_t sorted_cap, int32_t *expert_ids, int64_t expert_cap, int32_t *npp, void *ws,
+                      size_t ws_bytes, void *stream, Checks &ck) {
   if (!topk_ids && M > 0) ck.fail(MR_EINVAL, "topk_ids is NULL");
   if (M < 0) ck.fail(MR_EINVAL, "M=%d < 0", M);
   if (M > MR_MAX_TOKENS) ck.fail(MR_EUNSUPPORTED, "M=%d > %d", M, MR_MAX_TOKENS);
@@ -425,13 +427,15 @@ int mr_align(const int32_t *topk_ids, int32_t M, int32_t S, int32_t num_experts,
   // the align regions of a route workspace with E = Ep and k = S
   const Layout L = layout_for(M > 0 ? M : 0, Ep, S > 0 ? S : 1, 0);
   check_workspace(ck, ws, ws_bytes, L.total);
-  if (ck.code() != MR_OK) return ck.finish("mr_align");
+  if (ck.code() != MR_OK) return ck.finish(fn);
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (n == 0) return launch_result(mr::launch_store_zero(npp, s), "mr_align");
+  if (n == 0) return launch_result(mr::launch_store_zero(npp, s), fn);
   char *wsb = static_cast<char *>(ws);
   mr::AlignParams p{};
   p.ids = topk_ids;
+  p.map = expert_map;
+  p.Eg = num_global;
   p.n = n;
   p.S = S;
   p.Ep = Ep;
@@ -447,8 +451,28 @@ int mr_align(const int32_t *topk_ids, int32_t M, int32_t S, int32_t num_experts,
   p.nchunks = (int)((n + 64 * p.W - 1) / (64 * p.W));
   p.ctr = reinterpret_cast<uint32_t *>(wsb + L.counters);
   p.counts = reinterpret_cast<int32_t *>(wsb + L.counts);
+  p.cstride = (Ep + 3) / 4 * 4;
   p.ranks = reinterpret_cast<int32_t *>(wsb + L.ranks);
-  return launch_result(mr::launch_align(p, s), "mr_align");
+  return launch_result(mr::launch_align(p, s), fn);
+}
+
+int mr_align(const int32_t *topk_ids, int32_t M, int32_t S, int32_t num_experts, int32_t A,
+             int32_t *sorted_token_ids, int64_t sorted_cap, int32_t *expert_ids, int64_t expert_cap, int32_t *npp,
+             void *ws, size_t ws_bytes, void *stream) {
+  Checks ck;
+  return align_impl("mr_align", topk_ids, M, S, nullptr, 0, num_experts, A, sorted_token_ids, sorted_cap, expert_ids,
+                    expert_cap, npp, ws, ws_bytes, stream, ck);
+}
+
+int mr_align_local(const int32_t *topk_ids, int32_t M, int32_t S, int32_t num_experts_global,
+                   const int32_t *expert_map, int32_t num_local_experts, int32_t A, int32_t *sorted_token_ids,
+                   int64_t sorted_cap, int32_t *expert_ids, int64_t expert_cap, int32_t *npp, void *ws,
+                   size_t ws_bytes, void *stream) {
+  Checks ck;
+  if (!expert_map) ck.fail(MR_EINVAL, "expert_map is NULL");
+  if (num_experts_global < 1) ck.fail(MR_EINVAL, "num_experts_global=%d < 1", num_experts_global);
+  return align_impl("mr_align_local", topk_ids, M, S, expert_map, num_experts_global, num_local_experts, A,
+                    sorted_token_ids, sorted_cap, expert_ids, expert_cap, npp, ws, ws_bytes, stream, ck);
 }
 
 }  // extern "C"

@@ -74,6 +74,8 @@ struct SmallParams {
 // Standalone align.
 struct AlignParams {
   const int32_t *ids;  // [n]
+  const int32_t *map;  // null, or [Eg]: each global expert's local id (-1: another rank's)
+  int Eg;              // global experts (with map)
   int64_t n;
   int S, Ep, A;
   int32_t *sorted;
@@ -85,7 +87,8 @@ struct AlignParams {
   int W;        // bitmap words per expert; a chunk is 64 * W pairs
   int nchunks;
   uint32_t *ctr;    // counter words
-  int32_t *counts;  // [nchunks, Ep]: per-chunk counts, then per-chunk bases
+  int32_t *counts;  // [nchunks, cstride]: per-chunk counts, then per-chunk bases
+  int cstride;      // Ep rounded up to 4 (16-byte rows)
   int32_t *ranks;   // [n] rank of each pair inside its chunk
 };
 

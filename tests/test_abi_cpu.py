@@ -160,6 +160,16 @@ def test_argmax_refusals(lib):
     assert lib.mr_argmax_workspace_bytes(-1, 5) == 0 and lib.mr_argmax_workspace_bytes(3, 0) == 0
 
 
+def test_align_local_refusals(lib):
+    p = ctypes.c_void_p(1 << 20)
+    rc = lib.mr_align_local(p, 4, 2, 0, None, 3, 64, p, 1 << 20, p, 1 << 20, p, p, 1 << 30, None)
+    assert rc == mr.MR_EINVAL
+    msg = _err(lib)
+    assert "expert_map is NULL" in msg and "num_experts_global=0 < 1" in msg, msg
+    rc = lib.mr_align_local(p, 4, 2, 8, p, 0, 64, p, 1 << 20, p, 1 << 20, p, p, 1 << 30, None)
+    assert rc == mr.MR_EINVAL and "num_experts=0 < 1" in _err(lib)
+
+
 def test_error_cleared_after_success_path(lib):
     lib.mr_route(None, None, None, -1, 7, 0, 0, 1.0, None, None, None, 0, None)
     assert _err(lib)
