@@ -64,6 +64,8 @@ def _load():
     lib.or_bf16_value_array.restype = None
     lib.or_align_local.argtypes = [P, i32, i32, i32, P, i32, i32, P, i64, P, i64, P]
     lib.or_align_local.restype = i32
+    lib.or_grouped_gemm.argtypes = [P, i32, i32, P, i32, i32, i32, P, P, i64, i32, P, i32]
+    lib.or_grouped_gemm.restype = i32
     lib.or_argmax_rows.argtypes = [P, i64, i64, i64, P, i32]
     lib.or_argmax_rows.restype = i32
     _lib = lib
@@ -204,6 +206,26 @@ def align_local(topk_ids, expert_map, num_local: int, A: int):
         raise ValueError(f"or_align_local failed ({rc})")
     n = int(npp[0])
     return srt[:n].copy(), eids[: n // A].copy(), n
+
+
+def grouped_gemm(x_bits, w_bits, sorted_ids, expert_ids, npp: int, S: int, A: int, nthreads: int = 0):
+    """Consumer of the align output: x bf16 bits [M, H], w bf16 bits
+    [E', N, H]; returns y [M*S, N] float64 with NaN in the rows of pairs that
+    no slot below npp holds."""
+    x = _bits(x_bits)
+    w = np.ascontiguousarray(w_bits, dtype=np.uint16)
+    Ep, N, H = w.shape
+    M = x.shape[0]
+    srt = np.ascontiguousarray(sorted_ids, dtype=np.int32)
+    eids = np.ascontiguousarray(expert_ids, dtype=np.int32)
+    if srt.size < npp or eids.size < npp // A:
+        raise ValueError("sorted_ids / expert_ids shorter than npp")
+    y = np.full((M * S, N), np.nan)
+    rc = _load().or_grouped_gemm(_ptr(x), M, H, _ptr(w), Ep, N, S, _ptr(srt), _ptr(eids), npp, A, _ptr(y),
+                                 nthreads)
+    if rc != 0:
+        raise ValueError(f"or_grouped_gemm failed ({rc})")
+    return y
 
 
 def argmax_rows(x, nthreads: int = 0) -> np.ndarray:

@@ -47,6 +47,12 @@
  *                      skipped.  (The design the scope table's EP row
  *                      describes; the pages themselves run the router
  *                      replicated, [R] Motivation.)
+ *   or_grouped_gemm    the consumer of the align output that [A] Purpose
+ *                      describes: block b of A slots (launched while
+ *                      b*A < npp) multiplies its rows by the weights of
+ *                      expert expert_ids[b]; a slot holding pair p < M*S
+ *                      produces y[p][n] = sum_h x[p / S][h] * W[e][n][h]
+ *                      (double, sequential in h); padding produces nothing.
  *   or_argmax_rows     row-wise argmax of an fp32 matrix with PyTorch's
  *                      semantics as [N] Sampling states them: a NaN beats
  *                      every number and the first NaN beats later ones; among
@@ -397,6 +403,37 @@ int or_align_local(const int32_t *ids, int M, int S, int Eglobal, const int32_t 
     const int rc = or_align(loc, M, S, Elocal, A, sorted, sorted_cap, expert_ids, expert_cap, npp_out);
     free(loc);
     return rc;
+}
+
+/* Grouped expert GEMM over the align output (see the header).  y [M*S, N]
+ * is written only for the pairs that appear in sorted[0, npp). */
+int or_grouped_gemm(const uint16_t *x, int M, int H, const uint16_t *W, int Ep, int N, int S,
+                    const int32_t *sorted, const int32_t *expert_ids, int64_t npp, int A, double *y,
+                    int nthreads)
+{
+    if (M < 0 || H < 1 || Ep < 1 || N < 1 || S < 1 || A < 1 || npp < 0 || npp % A != 0)
+        return OR_EINVAL;
+    const int64_t n = (int64_t)M * S;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 16) if (nthreads != 1)
+#endif
+    for (int64_t j = 0; j < npp; ++j) {
+        const int32_t p = sorted[j];
+        const int32_t e = expert_ids[j / A];
+        if (p < 0 || p >= n || e < 0 || e >= Ep)
+            continue; /* padding slot */
+        const uint16_t *xr = x + (size_t)(p / S) * H;
+        for (int c = 0; c < N; ++c) {
+            const uint16_t *wr = W + ((size_t)e * N + c) * H;
+            double acc = 0.0;
+            for (int h = 0; h < H; ++h)
+                acc += or_bf16_value(xr[h]) * or_bf16_value(wr[h]);
+            y[(size_t)p * N + c] = acc;
+        }
+    }
+    return OR_OK;
 }
 
 /* ------------------------------------------------------- array helpers -- */

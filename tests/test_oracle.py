@@ -568,3 +568,49 @@ def test_align_local_partition_covers_every_pair():
         seen += [int(v) for v in srt if v != M * S]
         assert all(owner[ids.reshape(-1)[v]] == r for v in srt if v != M * S)
     assert sorted(seen) == list(range(M * S))
+
+
+# ------------------------------------------- grouped GEMM over the align --
+# [A] Purpose: the consumer multiplies each block of A slots by its expert's
+# weights; alignment only regroups rows, so every pair's output is its own
+# row times its own expert, whatever A is.
+
+def _consumer_case(M=37, S=3, E=9, N=8, H=24, seed=4):
+    rng = np.random.default_rng(seed)
+    x = oracle.round_bf16(rng.standard_normal((M, H)))
+    w = oracle.round_bf16(rng.standard_normal((E, N, H)) * 0.1)
+    ids = np.stack([rng.choice(E, S, replace=False) for _ in range(M)]).astype(np.int32)
+    return x, w, ids
+
+
+def test_grouped_gemm_is_the_direct_product():
+    x, w, ids = _consumer_case()
+    M, S = ids.shape
+    xv, wv = oracle.bf16_value(x), oracle.bf16_value(w)
+    want = np.einsum("ph,pnh->pn", np.repeat(xv, S, axis=0), wv[ids.reshape(-1)])  # library product, float64
+    for A in (16, 64, 128):
+        srt, eids, npp = oracle.align(ids, w.shape[0], A)
+        y = oracle.grouped_gemm(x, w, srt, eids, npp, S, A)
+        assert not np.isnan(y).any()
+        np.testing.assert_allclose(y, want, rtol=1e-12, atol=1e-12)
+
+
+def test_grouped_gemm_bit_identical_across_alignment():
+    x, w, ids = _consumer_case(M=200, S=5, E=17, seed=9)
+    ys = []
+    for A in (16, 64, 128):
+        srt, eids, npp = oracle.align(ids, w.shape[0], A)
+        ys.append(oracle.grouped_gemm(x, w, srt, eids, npp, ids.shape[1], A))
+    assert all(np.array_equal(ys[0], y) for y in ys[1:])
+
+
+def test_grouped_gemm_skips_padding_and_foreign_pairs():
+    # ids outside [0, E') take no slot, so their rows stay unwritten
+    x, w, ids = _consumer_case(M=10, S=2, E=5, seed=1)
+    ids[3, 1] = 7
+    ids[6, 0] = -1
+    srt, eids, npp = oracle.align(ids, 5, 16)
+    y = oracle.grouped_gemm(x, w, srt, eids, npp, 2, 16)
+    flat = ids.reshape(-1)
+    assert np.isnan(y[flat >= 5]).all() and np.isnan(y[flat < 0]).all()
+    assert not np.isnan(y[(flat >= 0) & (flat < 5)]).any()

@@ -36,6 +36,9 @@ MUTATIONS = {
     "tier_uses_slots": ("((int64_t)M * k >= (int64_t)128 * E)", "((int64_t)M * (k + 1) >= (int64_t)128 * E)"),
     "align_local_ignores_map": ("const int32_t l = (e >= 0 && e < Eglobal) ? map[e] : -1;", "const int32_t l = (e >= 0 && e < Eglobal) ? e : -1;"),
     "align_local_map_off_by_one": ("const int32_t l = (e >= 0 && e < Eglobal) ? map[e] : -1;", "const int32_t l = (e >= 1 && e < Eglobal) ? map[e - 1] : -1;"),
+    "gemm_token_of_pair": ("const uint16_t *xr = x + (size_t)(p / S) * H;", "const uint16_t *xr = x + (size_t)(p % M) * H;"),
+    "gemm_expert_of_next_block": ("const int32_t e = expert_ids[j / A];", "const int32_t e = expert_ids[(j + 1) / A];"),
+    "gemm_weight_transposed": ("const uint16_t *wr = W + ((size_t)e * N + c) * H;", "const uint16_t *wr = W + ((size_t)c * Ep + e) * H;"),
     "argmax_ties_last": ("if (isnan(v) || v > b)", "if (isnan(v) || v >= b)"),
     "argmax_last_nan": ("            if (isnan(b))\n                break; /* the first NaN has won the row */\n", ""),
     "argmax_nan_loses": ("if (isnan(v) || v > b)", "if (v > b)"),
