@@ -194,6 +194,32 @@ size_t mr_argmax_workspace_bytes(int32_t R, int64_t N);
 int mr_argmax_rows_f32(const float *x, int32_t R, int64_t N, int64_t ld, int64_t *out,
                        void *ws, size_t ws_bytes, void *stream);
 
+/* A minimal bf16 grouped-expert GEMM that consumes the align output, the
+ * consumer "W4A16 MoE prefill: M-aware moe_align block size" (ROCm vLLM),
+ * Purpose, describes, for measuring what the alignment costs downstream:
+ * block b of A slots runs only while b * A < *npp (its one early exit) and
+ * multiplies the x rows of its slots by expert expert_ids[b]'s weights; for
+ * every slot holding a pair index p < M*S it writes
+ *   y[p][n] = sum_h x[p / S][h] * w_experts[e][n][h]   (fp32 accumulation),
+ * while a padding slot inside npp still takes part in the contraction and
+ * only skips its store (so the work follows npp).  The output does not
+ * depend on A.
+ *   x          device, [M, H] bf16 row-major, 16-byte aligned.
+ *   w_experts  device, [num_experts, N, H] bf16 row-major, 16-byte aligned.
+ *   sorted_token_ids [sorted_cap], expert_ids, npp: device, as mr_align
+ *              writes them (npp and expert_ids are read on the device).
+ *   y          device, [M*S, N] fp32, 16-byte aligned; rows of pairs not
+ *              placed below npp are left untouched.
+ * A must be 64 or 128, H and N multiples of 64.  Returns MR_OK; MR_EINVAL
+ * for NULL pointers or M < 0, S < 1, num_experts < 1; MR_EUNSUPPORTED for
+ * the shape and alignment limits above; MR_ELAUNCH if the launch fails.
+ * M == 0 or sorted_cap < A launches nothing. */
+int mr_grouped_gemm_bf16(const void *x, int32_t M, int32_t H, const void *w_experts,
+                         int32_t num_experts, int32_t N, int32_t S,
+                         const int32_t *sorted_token_ids, int64_t sorted_cap,
+                         const int32_t *expert_ids, const int32_t *npp, int32_t A, float *y,
+                         void *stream);
+
 /* Measurement hook, not part of the routing API: one launch of a plain
  * streaming-read kernel over nbytes bytes at src (device memory, 16-byte
  * aligned, nbytes a multiple of 16), as a yardstick for what a single launch

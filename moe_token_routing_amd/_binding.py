@@ -42,6 +42,7 @@ SIGNATURES = {
     "mr_debug_gate_logits": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _P, _P, _SZ, _P]),
     "mr_debug_stream_read": (ctypes.c_int, [_P, _SZ, _P, _P]),
     "mr_argmax_workspace_bytes": (_SZ, [_I32, _I64]),
+    "mr_grouped_gemm_bf16": (ctypes.c_int, [_P, _I32, _I32, _P, _I32, _I32, _I32, _P, _I64, _P, _P, _I32, _P, _P]),
     "mr_argmax_rows_f32": (ctypes.c_int, [_P, _I32, _I64, _I64, _P, _P, _SZ, _P]),
 }
 
@@ -303,3 +304,24 @@ def mr_argmax_rows_f32(x, *, workspace, out=None, n=None, stream=None):
     _check(lib().mr_argmax_rows_f32(_ptr(x), R, N, ld, _ptr(out), _ptr(workspace), workspace.numel(),
                                     _stream(stream, x.device)))
     return out
+
+
+def mr_grouped_gemm_bf16(x, w_experts, S: int, sorted_token_ids, expert_ids, npp, A: int, *, y=None, stream=None):
+    """Grouped-expert GEMM over the align output: x bf16 [M, H], w_experts
+    bf16 [E', N, H]; returns y fp32 [M*S, N] (rows of pairs not placed below
+    npp keep y's previous contents; a new y starts as NaN)."""
+    import torch
+
+    _bf16_2d(x, "x")
+    if w_experts.dtype != torch.bfloat16 or w_experts.dim() != 3 or not w_experts.is_contiguous():
+        raise ValueError("w_experts must be a contiguous bf16 tensor [E', N, H]")
+    M, H = x.shape
+    Ep, N, H2 = w_experts.shape
+    if H2 != H:
+        raise ValueError("w_experts hidden size differs from x")
+    if y is None:
+        y = torch.full((M * S, N), float("nan"), dtype=torch.float32, device=x.device)
+    _check(lib().mr_grouped_gemm_bf16(_ptr(x), M, H, _ptr(w_experts), Ep, N, S, _ptr(sorted_token_ids),
+                                      sorted_token_ids.numel(), _ptr(expert_ids), _ptr(npp), A, _ptr(y),
+                                      _stream(stream, x.device)))
+    return y

@@ -18,6 +18,7 @@
 #include "moeroute.h"
 #include "stream_read.h"
 #include "argmax.h"
+#include "grouped_gemm.h"
 
 static_assert(MR_MAX_ROUTED_EXPERTS == mr::kMaxRouteExperts, "route expert limit");
 static_assert(MR_MAX_ALIGN_EXPERTS == mr::kMaxAlignExperts, "align expert limit");
@@ -391,6 +392,52 @@ int mr_argmax_rows_f32(const float *x, int32_t R, int64_t N, int64_t ld, int64_t
   p.ticket = static_cast<uint32_t *>(ws);
   p.part = reinterpret_cast<unsigned long long *>(static_cast<char *>(ws) + argmax_ticket_bytes(R));
   return launch_result(mr::launch_argmax(p, reinterpret_cast<hipStream_t>(stream)), "mr_argmax_rows_f32");
+}
+
+int mr_grouped_gemm_bf16(const void *x, int32_t M, int32_t H, const void *w_experts, int32_t num_experts, int32_t N,
+                         int32_t S, const int32_t *sorted_token_ids, int64_t sorted_cap, const int32_t *expert_ids,
+                         const int32_t *npp, int32_t A, float *y, void *stream) {
+  Checks ck;
+  if (M < 0) ck.fail(MR_EINVAL, "M=%d < 0", M);
+  if (S < 1) ck.fail(MR_EINVAL, "S=%d < 1", S);
+  if (num_experts < 1) ck.fail(MR_EINVAL, "num_experts=%d < 1", num_experts);
+  if (H < 64 || H % 64 != 0) ck.fail(MR_EUNSUPPORTED, "H=%d is not a positive multiple of 64", H);
+  if (N < 64 || N % 64 != 0) ck.fail(MR_EUNSUPPORTED, "N=%d is not a positive multiple of 64", N);
+  if (A != 64 && A != 128) ck.fail(MR_EUNSUPPORTED, "A=%d is not 64 or 128", A);
+  if (sorted_cap < 0) ck.fail(MR_EINVAL, "sorted_cap=%lld < 0", (long long)sorted_cap);
+  if (N >= 64 && (int64_t)num_experts * N > ((int64_t)1 << 31) / (H > 0 ? H : 1))
+    ck.fail(MR_EUNSUPPORTED, "num_experts * N * H >= 2^31 elements");
+  if (M > 0) {
+    if (!x) ck.fail(MR_EINVAL, "x is NULL");
+    else if (!aligned16(x)) ck.fail(MR_EUNSUPPORTED, "x is not 16-byte aligned");
+    if (!w_experts) ck.fail(MR_EINVAL, "w_experts is NULL");
+    else if (!aligned16(w_experts)) ck.fail(MR_EUNSUPPORTED, "w_experts is not 16-byte aligned");
+    if (!sorted_token_ids) ck.fail(MR_EINVAL, "sorted_token_ids is NULL");
+    if (!expert_ids) ck.fail(MR_EINVAL, "expert_ids is NULL");
+    if (!npp) ck.fail(MR_EINVAL, "npp is NULL");
+    if (!y) ck.fail(MR_EINVAL, "y is NULL");
+    else if (!aligned16(y)) ck.fail(MR_EUNSUPPORTED, "y is not 16-byte aligned");
+  }
+  if (ck.code() != MR_OK) return ck.finish("mr_grouped_gemm_bf16");
+  if (M == 0 || sorted_cap < A) {
+    g_last_error.clear();
+    return MR_OK;
+  }
+  mr::GemmParams p;
+  p.x = static_cast<const uint16_t *>(x);
+  p.M = M;
+  p.H = H;
+  p.w = static_cast<const uint16_t *>(w_experts);
+  p.Ep = num_experts;
+  p.N = N;
+  p.S = S;
+  p.A = A;
+  p.sorted = sorted_token_ids;
+  p.sorted_cap = sorted_cap;
+  p.expert_ids = expert_ids;
+  p.npp = npp;
+  p.y = y;
+  return launch_result(mr::launch_grouped_gemm(p, reinterpret_cast<hipStream_t>(stream)), "mr_grouped_gemm_bf16");
 }
 
 static_assert(MR_STREAM_READ_OUT_WORDS == mr::kStreamReadMaxBlocks, "stream-read output size");
