@@ -37,11 +37,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=8192)
     ap.add_argument("--warmup", type=int, default=512)
-    ap.add_argument("--workload", default="m4", choices=[f"m{m}" for m in SWEEP_M] + ["c3", "c4", "argmax", "align_ep"],
+    ap.add_argument("--workload", default="m4", choices=[f"m{m}" for m in SWEEP_M] + ["c3", "c4", "argmax", "align_ep", "consumer"],
                     help="m<M>: E=512+1, H=4096, k=10 at M tokens (m4 is the headline); c3: E=128, H=2048, "
                          "k=8, M=128; c4: the same at M=2048 with Zipf-skewed gate rows; argmax: row-wise fp32 "
                          "argmax of [16, 248320] (the sampling shape); align_ep: mr_align over all 513 experts vs "
-                         "mr_align_local for one of 8 expert-parallel ranks, on M=2048 routing ids")
+                         "mr_align_local for one of 8 expert-parallel ranks, on M=2048 routing ids; consumer: the "
+                         "padding study (align + grouped-expert GEMM at A = 64 and 128 over a token sweep)")
     ap.add_argument("--align", type=int, default=None, choices=[64, 128],
                     help="force the alignment A (default: the M-aware tier)")
     ap.add_argument("--method", default="rotate", choices=["rotate", "memset"],
@@ -514,6 +515,82 @@ def measure_align_ep(steps, warmup):
     }
 
 
+CONSUMER_E, CONSUMER_K, CONSUMER_H, CONSUMER_N = 128, 8, 2048, 512
+CONSUMER_M = (6, 128, 512, 1024, 2048)
+
+
+def zipf_routing(M, E, k, seed=0):
+    """Top-k ids [M, k]: k distinct experts per token drawn with
+    probabilities proportional to Zipf(1.1) over a seeded permutation of the
+    experts (the skew of routing captured from real prefills)."""
+    import numpy as np
+
+    rng = np.random.default_rng(seed)
+    rank = rng.permutation(E) + 1
+    p = rank ** -1.1
+    p = p / p.sum()
+    return np.stack([rng.choice(E, k, replace=False, p=p) for _ in range(M)]).astype(np.int32)
+
+
+def measure_consumer(steps, warmup):
+    """The padding study: for each token count, align the Zipf routing at
+    A = 64 and 128 and time the grouped-expert GEMM (E=128, k=8, H=2048,
+    N=512 synthetic bf16 weights) over each; the outputs must be
+    bit-identical across A."""
+    import numpy as np
+    import torch
+
+    import moe_token_routing_amd as mr
+
+    device = "cuda:0"
+    E, k, H, N = CONSUMER_E, CONSUMER_K, CONSUMER_H, CONSUMER_N
+    g = torch.Generator(device=device)
+    g.manual_seed(5)
+    w = (torch.randn(E, N, H, generator=g, device=device) * 0.02).to(torch.bfloat16)
+    stream = torch.cuda.Stream(device=device)
+    cur = torch.cuda.current_stream(device)
+    rows = []
+    for M in CONSUMER_M:
+        ids = zipf_routing(M, E, k, seed=M)
+        x = torch.randn(M, H, generator=g, device=device).to(torch.bfloat16)
+        t_ids = torch.from_numpy(ids).to(device)
+        row = {"M": M, "routed_rows": M * k, "tier_A": mr.mr_select_alignment(M, k, E)}
+        ys = {}
+        for A in (64, 128):
+            ws = mr.new_workspace(M, E, k, False, device=device)
+            srt, eids, npp = mr.mr_align(t_ids, E, A, workspace=ws)
+            y = mr.mr_grouped_gemm_bf16(x, w, k, srt, eids, npp, A)
+            torch.cuda.synchronize()
+            ys[A] = y
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=stream):
+                for _ in range(8):
+                    mr.mr_grouped_gemm_bf16(x, w, k, srt, eids, npp, A, y=y)
+            for _ in range(max(1, warmup // 64)):
+                gr.replay()
+            torch.cuda.synchronize()
+            reps = max(2, steps // 64)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(cur)
+            for _ in range(reps):
+                gr.replay()
+            e1.record(cur)
+            torch.cuda.synchronize()
+            n = int(npp.item())
+            us = e0.elapsed_time(e1) / (reps * 8) * 1e3
+            row[f"npp_A{A}"] = n
+            row[f"padding_ratio_A{A}"] = round(n / (M * k), 2)
+            row[f"gemm_us_A{A}"] = round(us, 2)
+            row[f"gemm_tflops_A{A}"] = round(2.0 * n * N * H / (us * 1e-6) / 1e12, 1)
+        row["bit_identical"] = bool(torch.equal(ys[64].view(torch.int32), ys[128].view(torch.int32)))
+        rows.append(row)
+    return {"metric": "padding study: grouped-expert GEMM us over the align output at A=64 vs 128 (E=128, k=8, "
+                      "H=2048, N=512, Zipf routing)", "rows": rows,
+            "timing": "HIP graph of 8 launches, HIP events on the launch stream; tflops counts npp rows (padding "
+                      "included, as the consumer computes them)"}
+
+
 def measure(wl, steps, warmup, A=None):
     """Times `steps` route+align launches on workload `wl`; returns the seeded
     input and the result fields."""
@@ -595,6 +672,13 @@ def main():
         mr._binding.lib()
         torch.cuda.set_device(0)
         print(json.dumps(measure_argmax(args.steps, args.warmup, args.cpu_seconds)), flush=True)
+        return
+    if args.workload == "consumer":
+        import moe_token_routing_amd as mr
+
+        mr._binding.lib()
+        torch.cuda.set_device(0)
+        print(json.dumps(measure_consumer(args.steps, args.warmup)), flush=True)
         return
     if args.workload == "align_ep":
         import moe_token_routing_amd as mr
