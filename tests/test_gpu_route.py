@@ -94,6 +94,9 @@ def test_router_sweep_small_m(M):
     (32, 32, 8, False, 3, 1.0),      # k = E: every expert chosen
     (3, 2, 8, True, 12, 1.0),        # shared-chunk layout with one chunk per row, odd E'
     (32, 32, 24, False, 6, 1.0),     # shared-chunk layout, k = E, H not a multiple of 64
+    (512, 10, 4096, True, 12, 1.0),  # 12-row gate loads (9 <= M <= 12), full router shape
+    (257, 9, 136, True, 11, 1.0),    # 12-row gate loads, ragged E and H
+    (512, 10, 4096, True, 13, 1.0),  # 16-row gate loads from M = 13
 ])
 def test_router_shapes(E, k, H, shared, M, scale):
     _say("shape", E, k, H, shared, M, scale)
