@@ -67,7 +67,7 @@ int64_t tight_capacity(int64_t n, int64_t Ep, int64_t A) {
 // Workspace regions for one call.  Every region grows with M, so a workspace
 // sized for M_max serves every M <= M_max.
 struct Layout {
-  size_t counters = 0, keys = 0, shared = 0;  // small-M route
+  size_t counters = 0, keys = 0, shared = 0, hids = 0;  // small-M route
   size_t counts = 0, ranks = 0;               // standalone align
   size_t part = 0, tcnt = 0;                   // prefill route (split-K partials, tile counters)
   size_t total = 0;
@@ -85,6 +85,7 @@ Layout layout_for(int64_t M, int64_t E, int64_t k, int64_t sh) {
   size_t o = mr::kCounterBytes;
   L.keys = take(o, (size_t)mr::kSmallMaxTokens * (size_t)E * 4);
   L.shared = take(o, (size_t)mr::kSmallMaxTokens * 8);
+  L.hids = take(o, (size_t)mr::kSmallMaxTokens * (mr::kMaxTopK + 1) * 4);
   const int W = mr::align_words_per_expert((int)(Ep > 0 ? Ep : 1));
   const int64_t nch = (n + 64 * W - 1) / (64 * W);
   L.counts = take(o, (size_t)(nch * ((Ep + 3) / 4 * 4)) * 4);
@@ -266,6 +267,7 @@ int route_impl(const char *fn, const void *x, const void *gate_w, const void *sh
   p.wts = wts;
   p.keys = reinterpret_cast<uint32_t *>(wsb + L.keys);
   p.shared_logit = reinterpret_cast<unsigned long long *>(wsb + L.shared);
+  p.hids = reinterpret_cast<uint32_t *>(wsb + L.hids);
   p.logits_out = logits_out;
   p.ctr = ctr;
   p.logits_only = logits_only ? 1 : 0;

@@ -34,8 +34,11 @@
 //   sentinel pre-fill of sorted_token_ids is issued first in every block and
 //   completed before that block's keys are written, so block 0 never races it.
 //
-// Tail (block 0): wave w takes token rows w, w+4, ... (two at a time, the
-//   selections interleaved, when it holds more than one) and selects the
+// Tail: at M >= 9 the first ceil(M/4) blocks each take four token rows, one
+//   per wave, and blocks 1.. hand their ids to block 0 (id + 1, written
+//   through, polled), which aligns.  Otherwise block 0 alone: wave w takes
+//   token rows w, w+4, ... (two at a time, the selections interleaved, when
+//   it holds more than one).  A wave selects the
 //   top-k as k rounds of a wave-wide maximum over the packed keys (DPP within
 //   rows of 16, then gfx950's permlane16/32 swaps), then the softmax, shared
 //   slot and stores, marking each pair in two LDS bitmaps; then the align:
@@ -173,10 +176,11 @@ __device__ void route_tail_rows2(const SmallParams &p, int32_t *lds_ids, uint32_
 // lane, lane+64, ...); a selection round is the lane maximum, a wave-wide
 // maximum, and clearing the one key equal to it (keys are unique).
 template <int NK>
-__device__ void route_tail_rows1(const SmallParams &p, int32_t *lds_ids, uint32_t *rowbm, uint32_t *touched) {
+__device__ void route_tail_rows1(const SmallParams &p, int32_t *lds_ids, uint32_t *rowbm, uint32_t *touched,
+                                 int m0, int m1, bool hand_off) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = p.E, k = p.k, S = p.S;
-  for (int m = wave; m < p.M; m += kThreads / kWave) {
+  for (int m = m0 + wave; m < m1; m += kThreads / kWave) {
     uint32_t *kr = p.keys + (size_t)m * E;
     uint32_t keys[NK];
     unsigned long long sv = 0;
@@ -217,8 +221,49 @@ __device__ void route_tail_rows1(const SmallParams &p, int32_t *lds_ids, uint32_
     if (lane < S) {
       p.ids[(size_t)m * S + lane] = id;
       p.wts[(size_t)m * S + lane] = w;
+      if (hand_off) {
+        st_agent(p.hids + (size_t)m * S + lane, (uint32_t)id + 1u);  // for block 0's align
+      } else {
+        lds_ids[m * S + lane] = id;
+        if (p.do_align) mark_pair(p, id, m, rowbm, touched);
+      }
+    }
+  }
+}
+
+// Block 0's side of the hand-off at M >= 9: wave w gathers the ids of rows
+// 4 + w, 8 + w, 12 + w (< M) that tail blocks 1.. wrote as id + 1 with
+// write-through stores, polling until every slot is non-zero (bounded, as
+// the key poll), then puts them in lds_ids, marks the align bitmaps and
+// re-zeroes the slots for the next launch.
+__device__ void gather_tail_ids(const SmallParams &p, int32_t *lds_ids, uint32_t *rowbm, uint32_t *touched) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int S = p.S;
+  constexpr int kRows = kSmallMaxTokens / (kThreads / kWave) - 1;  // rows 4 + w + 4 r, r < 3
+  uint32_t v[kRows];
+  for (int it = 0;; ++it) {
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      const int m = min(4 + wave + 4 * r, p.M - 1);  // branch-free: rows past M reload row M - 1
+      v[r] = ld_agent(p.hids + (size_t)m * S + min(lane, S - 1));
+    }
+    bool missing = false;
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) missing |= (4 + wave + 4 * r < p.M) && lane < S && v[r] == 0u;
+    if (__builtin_amdgcn_ballot_w64(missing) == 0) break;
+    if (it == kPollSpin) {
+      if (lane == 0) st_agent(p.ctr + kCtrError, 1u);
+      break;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    const int m = 4 + wave + 4 * r;
+    if (m < p.M && lane < S) {
+      const int32_t id = (int32_t)v[r] - 1;
       lds_ids[m * S + lane] = id;
-      if (p.do_align) mark_pair(p, id, m, rowbm, touched);
+      mark_pair(p, id, m, rowbm, touched);
+      st_agent(p.hids + (size_t)m * S + lane, 0u);
     }
   }
 }
@@ -462,13 +507,26 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
       }
     }
   }
-  if (p.logits_only || blockIdx.x != 0) return;
+  if (p.logits_only) return;
+  if constexpr (MAXM > 2 * (kThreads / kWave)) {
+    // M >= 9: the first ceil(M / 4) blocks take four token rows each, one
+    // per wave; blocks 1.. hand their ids to block 0, which aligns.
+    if ((int)blockIdx.x >= (M + 3) / 4) return;
+    __shared__ int32_t lds_ids[MAXM * (kMaxTopK + 1)];
+    const int m0 = 4 * blockIdx.x;
+    route_tail_rows1<NK>(p, lds_ids, rowbm, touched, m0, min(M, m0 + 4), blockIdx.x != 0 && p.do_align);
+    if (blockIdx.x != 0 || !p.do_align) return;
+    gather_tail_ids(p, lds_ids, rowbm, touched);
+    __syncthreads();  // every pair is marked and in lds_ids
+    align_small(p, lds_ids, rowbm, touched);
+    return;
+  }
+  if (blockIdx.x != 0) return;
 
   // ---- block 0: the tail ---------------------------------------------------
   __shared__ int32_t lds_ids[MAXM * (kMaxTopK + 1)];
-  // Token rows in pairs when a wave holds more than one (M >= 5).
   if constexpr (MAXM > kThreads / kWave) route_tail_rows2<NK>(p, lds_ids, rowbm, touched);
-  else route_tail_rows1<NK>(p, lds_ids, rowbm, touched);
+  else route_tail_rows1<NK>(p, lds_ids, rowbm, touched, 0, p.M, false);
   if (p.do_align) {
     __syncthreads();  // every pair is marked and in lds_ids
     align_small(p, lds_ids, rowbm, touched);
@@ -477,7 +535,10 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
 
 template <int RPB, int MAXM, bool SHARED, int ML = MAXM>
 hipError_t launch_nk(const SmallParams &p, hipStream_t stream) {
-  const int grid = (p.Ep + RPB - 1) / RPB;
+  // at M >= 9 the first ceil(M / 4) blocks also run the tail: there must be
+  // that many (extra blocks own no gate rows: their sums are dropped)
+  int grid = (p.Ep + RPB - 1) / RPB;
+  if (MAXM > 2 * (kThreads / kWave) && grid < (p.M + 3) / 4) grid = (p.M + 3) / 4;
   const int nk = (p.E + kWave - 1) / kWave;
   if (nk <= 2) route_small_kernel<RPB, MAXM, SHARED, 2, ML><<<grid, kThreads, 0, stream>>>(p);
   else if (nk <= 4) route_small_kernel<RPB, MAXM, SHARED, 4, ML><<<grid, kThreads, 0, stream>>>(p);
