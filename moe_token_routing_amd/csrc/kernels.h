@@ -57,7 +57,7 @@ struct SmallParams {
   // written), the shared logits [M] as (1 << 32 | fp32 bits), and hids.
   uint32_t *keys;
   unsigned long long *shared_logit;
-  uint32_t *hids;  // [M, S] at M >= 9: tail blocks 1.. hand block 0 their ids as id + 1 (0 = not yet)
+  uint32_t *hids;  // [M, S] at M >= 5: tail blocks 1.. hand block 0 their ids as id + 1 (0 = not yet)
   float *logits_out;  // logits_only: the caller's [M, Ep] fp32 buffer
   uint32_t *ctr;      // counter words (kCounterBytes)
   int logits_only;

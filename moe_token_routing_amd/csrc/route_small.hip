@@ -34,11 +34,9 @@
 //   sentinel pre-fill of sorted_token_ids is issued first in every block and
 //   completed before that block's keys are written, so block 0 never races it.
 //
-// Tail: at M >= 9 the first ceil(M/4) blocks each take four token rows, one
-//   per wave, and blocks 1.. hand their ids to block 0 (id + 1, written
-//   through, polled), which aligns.  Otherwise block 0 alone: wave w takes
-//   token rows w, w+4, ... (two at a time, the selections interleaved, when
-//   it holds more than one).  A wave selects the
+// Tail: the first ceil(M/4) blocks each take four token rows, one per wave
+//   (at M <= 4 that is block 0 alone); blocks 1.. hand their ids to block 0
+//   (id + 1, written through, polled), which aligns.  A wave selects the
 //   top-k as k rounds of a wave-wide maximum over the packed keys (DPP within
 //   rows of 16, then gfx950's permlane16/32 swaps), then the softmax, shared
 //   slot and stores, marking each pair in two LDS bitmaps; then the align:
@@ -82,99 +80,12 @@ __device__ __forceinline__ void mark_pair(const SmallParams &p, int32_t id, int 
   }
 }
 
-// Tail, part 1, token rows in pairs: wave w takes the token rows w, w+4,
-// w+8, ..., two at a time (w + 8i and w + 8i + 4) so that the two
-// selections interleave.  Each
-// lane holds NK keys per row (experts lane, lane+64, ...); a selection round
-// is a wave-wide maximum of the lanes' sorted heads, and the lane that held
-// it drops its head (keys are unique).
-template <int NK>
-__device__ void route_tail_rows2(const SmallParams &p, int32_t *lds_ids, uint32_t *rowbm, uint32_t *touched) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int E = p.E, k = p.k, S = p.S;
-  constexpr int kWaves = kThreads / kWave;
-  // softmax over the chosen k, the shared slot, the stores
-  auto finish = [&](int m, uint32_t mine, unsigned long long sv) {
-    const float r = key_value(mine);
-    const float r0 = readlane_f32(r, 0);
-    const float ex = (lane < k) ? expf(r - r0) : 0.0f;
-    const float den = wave_sum_f32(ex);
-    int32_t id = (int32_t)key_id(mine);
-    float w = ex / den;
-    if (p.has_shared && lane == k) {
-      const float s = __uint_as_float((uint32_t)sv);
-      id = E;
-      w = p.scale / (1.0f + expf(-s));
-    }
-    if (lane < S) {
-      p.ids[(size_t)m * S + lane] = id;
-      p.wts[(size_t)m * S + lane] = w;
-      lds_ids[m * S + lane] = id;
-      if (p.do_align) mark_pair(p, id, m, rowbm, touched);
-    }
-  };
-  for (int ma = wave; ma < p.M; ma += 2 * kWaves) {
-    const int mb = ma + kWaves;
-    const bool two = mb < p.M;
-    const int mb_ = two ? mb : ma;
-    uint32_t *kra = p.keys + (size_t)ma * E, *krb = p.keys + (size_t)mb_ * E;
-    uint32_t ka[NK], kb[NK];
-    unsigned long long sa = 0, sb = 0;
-    // poll until every key of the row(s) (and their shared logits) has
-    // arrived; a single row is polled alone
-    for (int it = 0;; ++it) {
-      bool missing = false;
-#pragma unroll
-      for (int i = 0; i < NK; ++i) ka[i] = ld_agent(kra + min(lane + kWave * i, E - 1));
-      if (p.has_shared) sa = ld_agent(p.shared_logit + ma);
-      if (two) {
-#pragma unroll
-        for (int i = 0; i < NK; ++i) kb[i] = ld_agent(krb + min(lane + kWave * i, E - 1));
-        if (p.has_shared) sb = ld_agent(p.shared_logit + mb);
-        missing = p.has_shared && (sb >> 32) == 0;
-#pragma unroll
-        for (int i = 0; i < NK; ++i) missing |= (lane + kWave * i < E) && kb[i] == 0u;
-      }
-      missing |= p.has_shared && (sa >> 32) == 0;
-#pragma unroll
-      for (int i = 0; i < NK; ++i) missing |= (lane + kWave * i < E) && ka[i] == 0u;
-      if (__builtin_amdgcn_ballot_w64(missing) == 0) break;
-      if (it == kPollSpin) {
-        if (lane == 0) st_agent(p.ctr + kCtrError, 1u);
-        break;
-      }
-    }
-    // consume: mask lanes past E, re-zero the slots for the next launch
-#pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      if (lane + kWave * i < E) {
-        st_agent(kra + lane + kWave * i, 0u);
-        if (two) st_agent(krb + lane + kWave * i, 0u);
-      } else {
-        ka[i] = 0u;
-        kb[i] = 0u;
-      }
-    }
-    if (p.has_shared && lane == 0) {
-      st_agent(p.shared_logit + ma, 0ull);
-      if (two) st_agent(p.shared_logit + mb, 0ull);
-    }
-    sort_desc_u32(ka);
-    if (two) {
-      sort_desc_u32(kb);
-      uint32_t mine_a, mine_b;
-      topk_sorted2_u32(ka, kb, k, lane, mine_a, mine_b);  // lane j < k: the j-th chosen key
-      finish(ma, mine_a, sa);
-      finish(mb, mine_b, sb);
-    } else {
-      finish(ma, topk_sorted_u32(ka, k, lane), sa);
-    }
-  }
-}
-
-// Tail, part 1, one token row at a time: rows m = wave, wave+4, ...  Each lane holds NK keys (experts
-// lane, lane+64, ...); a selection round is the lane maximum, a wave-wide
-// maximum, and clearing the one key equal to it (keys are unique).
+// Tail, part 1: token rows m0 + wave (< m1), one per wave.  Each lane
+// holds NK keys (experts lane, lane + 64, ...); a selection round is a
+// wave-wide maximum of the lanes' sorted heads, and the lane that held it
+// drops its head (keys are unique).  The ids go to the outputs and either
+// into lds_ids and the align bitmaps (block 0) or, with hand_off, to block 0
+// through the hids row (id + 1, written through).
 template <int NK>
 __device__ void route_tail_rows1(const SmallParams &p, int32_t *lds_ids, uint32_t *rowbm, uint32_t *touched,
                                  int m0, int m1, bool hand_off) {
@@ -231,7 +142,7 @@ __device__ void route_tail_rows1(const SmallParams &p, int32_t *lds_ids, uint32_
   }
 }
 
-// Block 0's side of the hand-off at M >= 9: wave w gathers the ids of rows
+// Block 0's side of the hand-off at M >= 5: wave w gathers the ids of rows
 // 4 + w, 8 + w, 12 + w (< M) that tail blocks 1.. wrote as id + 1 with
 // write-through stores, polling until every slot is non-zero (bounded, as
 // the key poll), then puts them in lds_ids, marks the align bitmaps and
@@ -508,9 +419,11 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
     }
   }
   if (p.logits_only) return;
-  if constexpr (MAXM > 2 * (kThreads / kWave)) {
-    // M >= 9: the first ceil(M / 4) blocks take four token rows each, one
-    // per wave; blocks 1.. hand their ids to block 0, which aligns.
+  if constexpr (MAXM > kThreads / kWave) {
+    // M >= 5: the first ceil(M / 4) blocks take four token rows each, one
+    // per wave; blocks 1.. hand their ids to block 0, which aligns (against
+    // block 0 alone taking two rows per wave: -0.7 to -0.9 us at M = 5..8,
+    // -2.7 to -3.8 us at M = 9..16).
     if ((int)blockIdx.x >= (M + 3) / 4) return;
     __shared__ int32_t lds_ids[MAXM * (kMaxTopK + 1)];
     const int m0 = 4 * blockIdx.x;
@@ -525,8 +438,7 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
 
   // ---- block 0: the tail ---------------------------------------------------
   __shared__ int32_t lds_ids[MAXM * (kMaxTopK + 1)];
-  if constexpr (MAXM > kThreads / kWave) route_tail_rows2<NK>(p, lds_ids, rowbm, touched);
-  else route_tail_rows1<NK>(p, lds_ids, rowbm, touched, 0, p.M, false);
+  route_tail_rows1<NK>(p, lds_ids, rowbm, touched, 0, p.M, false);
   if (p.do_align) {
     __syncthreads();  // every pair is marked and in lds_ids
     align_small(p, lds_ids, rowbm, touched);
@@ -535,10 +447,10 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
 
 template <int RPB, int MAXM, bool SHARED, int ML = MAXM>
 hipError_t launch_nk(const SmallParams &p, hipStream_t stream) {
-  // at M >= 9 the first ceil(M / 4) blocks also run the tail: there must be
+  // at M >= 5 the first ceil(M / 4) blocks also run the tail: there must be
   // that many (extra blocks own no gate rows: their sums are dropped)
   int grid = (p.Ep + RPB - 1) / RPB;
-  if (MAXM > 2 * (kThreads / kWave) && grid < (p.M + 3) / 4) grid = (p.M + 3) / 4;
+  if (MAXM > kThreads / kWave && grid < (p.M + 3) / 4) grid = (p.M + 3) / 4;
   const int nk = (p.E + kWave - 1) / kWave;
   if (nk <= 2) route_small_kernel<RPB, MAXM, SHARED, 2, ML><<<grid, kThreads, 0, stream>>>(p);
   else if (nk <= 4) route_small_kernel<RPB, MAXM, SHARED, 4, ML><<<grid, kThreads, 0, stream>>>(p);
