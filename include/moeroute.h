@@ -167,7 +167,8 @@ int mr_route_align(const void *x, const void *gate_w, const void *shared_w,
 /* Test hook, not part of the routing API: writes the fp32 gate logits the
  * route kernels compute for these inputs -- logits [M, E + has_shared]
  * (the shared logit in the last column) -- using the same kernel code and
- * summation order as mr_route for the same M. */
+ * summation order as mr_route for the same M (and as mr_route_align, except
+ * at 17 <= M <= 32 with an alignment A < M, which takes the prefill launch). */
 int mr_debug_gate_logits(const void *x, const void *gate_w, const void *shared_w,
                          int32_t M, int32_t H, int32_t E, float *logits,
                          void *ws, size_t ws_bytes, void *stream);

@@ -186,7 +186,10 @@ int route_impl(const char *fn, const void *x, const void *gate_w, const void *sh
     if (fill > sorted_cap) fill = sorted_cap;
   }
 
-  if (M > mr::kSmallMaxTokens) {
+  // The small-M launch takes M <= kSmallMaxTokens, and with align also
+  // M <= 16 or M <= A (its align puts each expert's pairs in one block).
+  const bool small = M <= mr::kSmallMaxTokens && (M <= 16 || !do_align || A >= M);
+  if (!small) {
     const int cap = mr::mfma_capacity(E);
     if (cap < 1) {
       g_last_error = std::string(fn) + ": could not size the prefill launch (no device or occupancy query failed)";

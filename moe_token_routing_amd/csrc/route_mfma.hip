@@ -1,5 +1,6 @@
 // route_mfma.hip -- one-launch router + align for prefill token counts
-// (M > 16): the gate pass is a split-K MFMA tile contraction.
+// (M > 32, or 17 <= M <= 32 aligned with A < M): the gate pass is a split-K
+// MFMA tile contraction.
 //
 // Computes what "[AMD] One-launch small-M MoE router ... on gfx950"
 // (sglang), Modifications, and "W4A16 MoE prefill: M-aware moe_align block

@@ -1,5 +1,6 @@
 // route_small.hip -- one-launch router + align for small token counts
-// (M <= 16): the gate pass is a weight-streaming GEMV.
+// (M <= 32; with align, M <= 16 or M <= A): the gate pass is a
+// weight-streaming GEMV.
 //
 // What it computes follows "[AMD] One-launch small-M MoE router ... on
 // gfx950" (sglang), Modifications, and "W4A16 MoE prefill: M-aware
@@ -40,7 +41,7 @@
 //   top-k as k rounds of a wave-wide maximum over the packed keys (DPP within
 //   rows of 16, then gfx950's permlane16/32 swaps), then the softmax, shared
 //   slot and stores, marking each pair in two LDS bitmaps; then the align:
-//   with M <= 16 <= A every touched expert takes exactly one block, so the
+//   with M <= A every touched expert takes exactly one block, so the
 //   bitmap of touched experts (block index = rank among them, one wave scan)
 //   and the one of token rows per expert (slot in the block) place every
 //   pair, one pair per thread.
@@ -53,7 +54,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kPollSpin = 1 << 21;  // bound on block 0's polls (each is one memory round trip)
-static_assert(kSmallMaxTokens <= 16, "the small-M align puts each expert's pairs (one per row) in one block of A >= 16 slots");
+static_assert(kSmallMaxTokens <= 32, "one bit per token row in rowbm; the host sends M > A to the prefill launch, so each expert's pairs (one per row) fit one block of A slots");
 
 // Max of N keys held in registers (a balanced tree, depth log2 N).
 template <int N>
@@ -143,14 +144,14 @@ __device__ void route_tail_rows1(const SmallParams &p, int32_t *lds_ids, uint32_
 }
 
 // Block 0's side of the hand-off at M >= 5: wave w gathers the ids of rows
-// 4 + w, 8 + w, 12 + w (< M) that tail blocks 1.. wrote as id + 1 with
+// 4 + w, 8 + w, ... (< M) that tail blocks 1.. wrote as id + 1 with
 // write-through stores, polling until every slot is non-zero (bounded, as
 // the key poll), then puts them in lds_ids, marks the align bitmaps and
 // re-zeroes the slots for the next launch.
 __device__ void gather_tail_ids(const SmallParams &p, int32_t *lds_ids, uint32_t *rowbm, uint32_t *touched) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int S = p.S;
-  constexpr int kRows = kSmallMaxTokens / (kThreads / kWave) - 1;  // rows 4 + w + 4 r, r < 3
+  constexpr int kRows = kSmallMaxTokens / (kThreads / kWave) - 1;  // rows 4 + w + 4 r
   uint32_t v[kRows];
   for (int it = 0;; ++it) {
 #pragma unroll
@@ -179,7 +180,7 @@ __device__ void gather_tail_ids(const SmallParams &p, int32_t *lds_ids, uint32_t
   }
 }
 
-// Tail, part 2: align of the n = M*S pairs in lds_ids.  Here M <= 16 <= A,
+// Tail, part 2: align of the n = M*S pairs in lds_ids.  Here M <= A,
 // and a token row holds an expert at most once, so an expert's pairs always
 // fit one block of A slots: every touched expert pads to exactly A.  Its
 // block index is its rank among the touched experts -- the touched-bitmap
@@ -250,15 +251,16 @@ __device__ __forceinline__ void halve(float (&v)[V], int lane) {
 // timing.  Returns the total and sets idx to its value index.
 template <int V>
 __device__ __forceinline__ float wave_totals(float (&v)[V], int lane, int &idx) {
-  static_assert(V == 16 || V == 32, "16 or 32 sums per lane");
+  static_assert(V == 16 || V == 32 || V == 64, "16, 32 or 64 sums per lane");
   halve<V, 1>(v, lane);
   halve<V / 2, 2>(v, lane);
   halve<V / 4, 4>(v, lane);
   halve<V / 8, 8>(v, lane);
-  if constexpr (V == 32) halve<2, 16>(v, lane);
+  if constexpr (V >= 32) halve<V / 16, 16>(v, lane);
+  if constexpr (V == 64) halve<2, 32>(v, lane);
   float t = v[0];
   if constexpr (V == 16) t += xor_lane_f32<16>(t, lane);
-  t += xor_lane_f32<32>(t, lane);
+  if constexpr (V <= 32) t += xor_lane_f32<32>(t, lane);
   idx = 0;
 #pragma unroll
   for (int b = 0; (1 << b) < V; ++b) idx |= ((lane >> b) & 1) << (__builtin_ctz(V) - 1 - b);
@@ -271,7 +273,7 @@ template <int RPB, int MAXM, bool SHARED, int NK, int ML = MAXM>
 __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
   constexpr int V = RPB * MAXM;
   constexpr int WPR = (kThreads / kWave) / RPB;  // waves per gate row (split layout)
-  static_assert(!SHARED || V == 16 || V == 32, "the butterfly reduces 16 or 32 sums per thread");
+  static_assert(!SHARED || V == 16 || V == 32 || V == 64, "the butterfly reduces 16, 32 or 64 sums per thread");
   __shared__ float red[kThreads / kWave][SHARED ? V : MAXM];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row0 = blockIdx.x * RPB;
@@ -476,7 +478,8 @@ hipError_t launch_route_small(const SmallParams &p, hipStream_t stream) {
   // 9 <= M <= 12: the same 16-row layout loading only 12 token rows
   // (measured -0.9 to -1.0 us at M = 9..12 against loading 16)
   if (p.M <= 12) return launch_nk<2, 16, true, 12>(p, stream);
-  return launch_nk<2, 16, true>(p, stream);
+  if (p.M <= 16) return launch_nk<2, 16, true>(p, stream);
+  return launch_nk<2, 32, true>(p, stream);
 }
 
 }  // namespace mr

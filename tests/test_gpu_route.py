@@ -97,6 +97,10 @@ def test_router_sweep_small_m(M):
     (512, 10, 4096, True, 12, 1.0),  # 12-row gate loads (9 <= M <= 12), full router shape
     (257, 9, 136, True, 11, 1.0),    # 12-row gate loads, ragged E and H
     (512, 10, 4096, True, 13, 1.0),  # 16-row gate loads from M = 13
+    (512, 10, 4096, True, 17, 1.0),  # 32-row gate layout (17 <= M <= 32), 5 tail blocks
+    (512, 10, 4096, True, 32, 1.0),  # 32-row gate layout, 8 tail blocks
+    (3, 2, 8, True, 32, 1.0),        # 8 tail blocks but E' = 4: the grid is raised to cover them
+    (100, 7, 200, False, 24, 2.0),   # ragged E and H, no shared expert
 ])
 def test_router_shapes(E, k, H, shared, M, scale):
     _say("shape", E, k, H, shared, M, scale)
@@ -108,6 +112,14 @@ def test_router_shapes(E, k, H, shared, M, scale):
 def test_router_forced_alignment(A):
     _say("A", A)
     d = workloads.make_inputs(8, 512, 4096, True, "int", seed=7)
+    _run_and_check(d, 10, 1.0, A=A, exact=True)
+
+
+@pytest.mark.parametrize("M,A", [(32, 32), (20, 16), (32, 16)])
+def test_router_forced_alignment_17_to_32(M, A):
+    # M <= A stays on the small-M launch; A < M goes to the prefill launch
+    _say("M", M, "A", A)
+    d = workloads.make_inputs(M, 512, 4096, True, "int", seed=M + A)
     _run_and_check(d, 10, 1.0, A=A, exact=True)
 
 
