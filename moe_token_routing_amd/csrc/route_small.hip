@@ -475,9 +475,12 @@ hipError_t launch_route_small(const SmallParams &p, hipStream_t stream) {
   if (p.M <= 4) return small_rows_per_block(p.Ep, p.M) == 2 ? launch_nk<2, 4, false>(p, stream)
                                                             : launch_nk<1, 4, false>(p, stream);
   if (p.M <= 8) return launch_nk<2, 8, true>(p, stream);
-  // 9 <= M <= 12: the same 16-row layout loading only 12 token rows
-  // (measured -0.9 to -1.0 us at M = 9..12 against loading 16)
+  // 9 <= M <= 14: the same 16-row layout loading only 10, 12 or 14 token
+  // rows (measured -0.9 to -1.4 us at M = 9..12, -0.3 at 13..14 against
+  // loading 16)
+  if (p.M <= 10) return launch_nk<2, 16, true, 10>(p, stream);
   if (p.M <= 12) return launch_nk<2, 16, true, 12>(p, stream);
+  if (p.M <= 14) return launch_nk<2, 16, true, 14>(p, stream);
   if (p.M <= 16) return launch_nk<2, 16, true>(p, stream);
   // 17 <= M <= 32: the 32-row layout loading 20, 24, 28 or 32 token rows
   // (against always 32: -2.3 us at M = 17, -2.1 at 20, -1.3 at 24)

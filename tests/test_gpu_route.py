@@ -101,6 +101,8 @@ def test_router_sweep_small_m(M):
     (512, 10, 4096, True, 32, 1.0),  # 32-row gate layout, 8 tail blocks
     (3, 2, 8, True, 32, 1.0),        # 8 tail blocks but E' = 4: the grid is raised to cover them
     (100, 7, 200, False, 24, 2.0),   # ragged E and H, no shared expert
+    (512, 10, 4096, True, 10, 1.0),  # 10-row loads
+    (64, 4, 520, False, 14, 1.0),    # 14-row loads, H not a multiple of 64
     (512, 10, 4096, True, 21, 1.0),  # 24-row loads
     (512, 10, 4096, True, 28, 1.0),  # 28-row loads
     (512, 10, 4096, True, 29, 1.0),  # 32-row loads
