@@ -69,6 +69,7 @@ constexpr int kRowBytes = kKS * 2;       // one operand row of a stage
 constexpr int kStageBytes = (kTE + kTT) * kRowBytes;  // 32 KB
 constexpr int kRingBytes = kNS * kStageBytes;          // 128 KB
 constexpr int kTilePitch = kTT + 4;      // fp32 pitch of the transpose tile
+constexpr int kOwnBytes = 17408;         // phases T and A: a group's ids (tpb * S <= 128 * 33) at the start of LDS
 constexpr int kBarrierSpin = 1 << 22;    // bound on a grid-barrier wait
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
@@ -461,6 +462,9 @@ __device__ void topk_group(const MfmaParams &p, int32_t *own, int g, const float
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int M = p.M, E = p.E, k = p.k, S = p.S, SK = p.SK, Epad = p.Epad;
   const int t0 = g * p.tpb, t1 = min(M, t0 + p.tpb);
+  // compiled in only where E > 128 (E <= 128 takes all its splits in one
+  // batch at H <= 2048, and the extra code slowed that instantiation)
+  constexpr bool kCoop = NCH >= 2;
   const int rowc = Epad >> 2;  // 16-byte chunks per partial row
   // Lane l holds experts 4c .. 4c + 3 of the chunks c = l + 64 j, j < NCH:
   // the partial rows are summed straight from their 16-byte loads, in split
@@ -534,12 +538,71 @@ __device__ void topk_group(const MfmaParams &p, int32_t *own, int g, const float
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   };
-  for (int ti = 0; ti < ntw; ti += 2) {
-    const bool two = ti + 1 < ntw;
-    const int ma = t0 + wave + 4 * ti, mb = two ? ma + 4 : ma;
+  if (kCoop && t1 - t0 == 1 && SK > SB) {
+    const int ma = t0, mb = t0;
+    float za[NK], zb[NK];
+#pragma unroll
+    for (int i = 0; i < NK; ++i) za[i] = zb[i] = 0.f;
+    for (int s0 = wave; s0 < SK; s0 += 4 * SB) {
+      u32x4_coh va[SB][NCH], vb[SB][NCH];
+#pragma unroll
+      for (int s = 0; s < SB; ++s) {
+        const int sp = min(s0 + 4 * s, SK - 1);
+        const u32x4_coh *ra = reinterpret_cast<const u32x4_coh *>(p.part + ((size_t)sp * M + ma) * Epad);
+        const u32x4_coh *rb = reinterpret_cast<const u32x4_coh *>(p.part + ((size_t)sp * M + mb) * Epad);
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+          va[s][j] = ra[chunk[j]];
+          vb[s][j] = rb[chunk[j]];
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < SB; ++s)
+        if (s0 + 4 * s < SK) {
+#pragma unroll
+          for (int j = 0; j < NCH; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              za[4 * j + i] += __uint_as_float(va[s][j][i]);
+              zb[4 * j + i] += __uint_as_float(vb[s][j][i]);
+            }
+        }
+    }
+    float *red = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(own) + kOwnBytes);  // [wave][token][NK][lane]
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      red[((2 * wave + 0) * NK + i) * 64 + lane] = za[i];
+      red[((2 * wave + 1) * NK + i) * 64 + lane] = zb[i];
+    }
+    __syncthreads();
+  }
+  // A one-token group (M <= grid) whose splits take more than one batch of
+  // loads: the four waves split the K splits (wave w sums splits w, w + 4,
+  // ... in order), meet in LDS in a fixed order, and wave 0 goes on; the
+  // logits still do not depend on timing.  (Measured: -0.4 us at M = 40;
+  // with one batch (C3) or two-token groups (M = 512) it was slower, so
+  // those keep the one-wave-per-token path.)
+  const bool coop = kCoop && t1 - t0 == 1 && SK > SB;
+  const int nsel = coop ? (wave == 0 ? 2 : 0) : ntw;
+  for (int ti = 0; ti < nsel; ti += 2) {
+    const bool two = coop ? t1 - t0 == 2 : ti + 1 < ntw;
+    const int ma = coop ? t0 : t0 + wave + 4 * ti, mb = two ? (coop ? t0 + 1 : ma + 4) : ma;
     float za[NK], zb[NK];
     float2 shl = make_float2(0.f, 0.f);
-    sum_rows(ma, mb, za, zb, shl);
+    if (coop) {
+      // every wave's share is in LDS (written before this loop)
+      const float *red = reinterpret_cast<const float *>(reinterpret_cast<const uint8_t *>(own) + kOwnBytes);
+#pragma unroll
+      for (int i = 0; i < NK; ++i) {
+        za[i] = ((red[(0 * NK + i) * 64 + lane] + red[(2 * NK + i) * 64 + lane]) + red[(4 * NK + i) * 64 + lane]) +
+                red[(6 * NK + i) * 64 + lane];
+        zb[i] = ((red[(1 * NK + i) * 64 + lane] + red[(3 * NK + i) * 64 + lane]) + red[(5 * NK + i) * 64 + lane]) +
+                red[(7 * NK + i) * 64 + lane];
+      }
+      if (p.has_shared) shl = sh ? make_float2(sh[ma - t0], sh[mb - t0]) : shared_pair(p, ma, mb);
+    } else {
+      sum_rows(ma, mb, za, zb, shl);
+    }
     if (p.logits_only) {
       for (int h = 0; h < (two ? 2 : 1); ++h) {
         const int m = h ? mb : ma;
@@ -567,6 +630,7 @@ __device__ void topk_group(const MfmaParams &p, int32_t *own, int g, const float
       finish(ma, topk_sorted_u32(ka, k, lane), shl.x);
     }
   }
+  if (coop) __syncthreads();  // wave 0 is done with the LDS sums before they are reused
 }
 
 // ------------------------------------------------------------- phase A ---
@@ -574,7 +638,6 @@ __device__ void topk_group(const MfmaParams &p, int32_t *own, int g, const float
 // LDS layout of phase A (byte offsets into the dynamic LDS).  The group's ids
 // (`own`, written in phase T) stay at the start; the phase-T staging slices
 // above them are free again.
-constexpr int kOwnBytes = 17408;                        // tpb * S <= 128 * 33 ids
 constexpr int kMaskOff = kOwnBytes;                     // per expert: 4 words of token bits
 constexpr int kMaskWords = (kMaxRouteExperts + 1) * 4;
 constexpr int kArrOff = kMaskOff + kMaskWords * 4;      // tot, pre, off, hist: per expert
