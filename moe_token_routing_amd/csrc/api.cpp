@@ -219,8 +219,14 @@ int route_impl(const char *fn, const void *x, const void *gate_w, const void *sh
     // at least 4 stages of 64 k per item: a split of one or two stages pays
     // the item's fixed costs (first loads, partial-tile stores, one more
     // partial row per token in the top-k phase) for too little work
-    // (measured at M = 17 .. 128; no change at M >= 512)
-    if (sk > q.nstages / 4) sk = q.nstages / 4 > 0 ? q.nstages / 4 : 1;
+    // (measured at M = 17 .. 128, E = 512; no change at M >= 512).  A launch
+    // of one tile keeps only 2: it has so few items that twice as many CUs
+    // on the gate outweighs the extra partial rows (M = 128, E = 128:
+    // -0.4 us; one stage per item: +1.4 us)
+    {
+      const int min_stages = (q.NE * q.NT == 1) ? 2 : 4;
+      if (sk > q.nstages / min_stages) sk = q.nstages / min_stages > 0 ? q.nstages / min_stages : 1;
+    }
     q.spp = (q.nstages + sk - 1) / sk;
     q.SK = (q.nstages + q.spp - 1) / q.spp;
     q.items = q.NE * q.NT * q.SK;
