@@ -219,12 +219,13 @@ int route_impl(const char *fn, const void *x, const void *gate_w, const void *sh
     // at least 4 stages of 64 k per item: a split of one or two stages pays
     // the item's fixed costs (first loads, partial-tile stores, one more
     // partial row per token in the top-k phase) for too little work
-    // (measured at M = 17 .. 128, E = 512; no change at M >= 512).  A launch
-    // of one tile keeps only 2: it has so few items that twice as many CUs
-    // on the gate outweighs the extra partial rows (M = 128, E = 128:
-    // -0.4 us; one stage per item: +1.4 us)
+    // (measured at M = 17 .. 128, E = 512; no change at M >= 512).  With a
+    // single expert tile (E <= 128) a partial row is at most 512 bytes, so
+    // the extra rows are cheap and 2 stages per item pay: twice as many CUs
+    // run the gate (M = 128, E = 128: -0.4 us; M = 2048, E = 128: -0.5 us;
+    // one stage per item: +1.4 us at M = 128)
     {
-      const int min_stages = (q.NE * q.NT == 1) ? 2 : 4;
+      const int min_stages = (q.NE == 1) ? 2 : 4;
       if (sk > q.nstages / min_stages) sk = q.nstages / min_stages > 0 ? q.nstages / min_stages : 1;
     }
     q.spp = (q.nstages + sk - 1) / sk;
