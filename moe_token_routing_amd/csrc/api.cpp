@@ -219,7 +219,8 @@ int route_impl(const char *fn, const void *x, const void *gate_w, const void *sh
     // at least 4 stages of 64 k per item: a split of one or two stages pays
     // the item's fixed costs (first loads, partial-tile stores, one more
     // partial row per token in the top-k phase) for too little work
-    // (measured at M = 17 .. 128, E = 512; no change at M >= 512).  With a
+    // (measured at M = 17 .. 128, E = 512; no change at M >= 512; 8 stages,
+    // which halve the partial rows, cost 0.5 .. 1.5 us at M = 40 .. 512).  With a
     // single expert tile (E <= 128) a partial row is at most 512 bytes, so
     // the extra rows are cheap and 2 stages per item pay: twice as many CUs
     // run the gate (M = 128, E = 128: -0.4 us; M = 2048, E = 128: -0.5 us;
