@@ -48,8 +48,9 @@
  * - Device-side preconditions that are documented, not checked: inputs are
  *   finite; align's ids are in [0, num_experts) -- ids outside that range
  *   are skipped (never written out of bounds).
- * - Workspace `ws` (ws_bytes >= mr_workspace_bytes(...)) must be zeroed ONCE
- *   by the caller before first use (e.g. torch.zeros).  Every launch leaves
+ * - Workspace `ws` (ws_bytes >= mr_workspace_bytes(...)), 256-byte aligned
+ *   (as device allocators return it), must be zeroed ONCE by the caller
+ *   before first use (e.g. torch.zeros).  Every launch leaves
  *   it ready for the next one (its counters at zero again, apart from a
  *   launch count kept by the prefill kernel, whose parity selects one of two
  *   grid-barrier counter sets), so the same workspace can be reused and
@@ -99,8 +100,11 @@ const char *mr_last_error(void);
 int32_t mr_select_alignment(int32_t M, int32_t k, int32_t E);
 
 /* Entries sorted_token_ids needs so that any routing of M*S pairs over
- * num_experts ids fits: M*S + min(num_experts, M*S) * (A - 1).  (Passing the
- * looser M*S + num_experts*(A-1) is also fine.)  Negative on bad input. */
+ * num_experts ids fits: M*S + min(num_experts, M*S) * (A - 1).  [A], Scope
+ * and safety, sizes this buffer (its num_slots figures) as the routed pairs
+ * plus A - 1 padding slots per expert; since no more than M*S experts can be
+ * touched, the min() bound is also enough.  (Passing that section's looser
+ * M*S + num_experts*(A-1) is fine.)  Negative on bad input. */
 int64_t mr_align_capacity(int32_t M, int32_t S, int32_t num_experts, int32_t A);
 
 /* Entries expert_ids needs: mr_align_capacity(...) / A. */
@@ -113,8 +117,47 @@ int64_t mr_expert_ids_capacity(int32_t M, int32_t S, int32_t num_experts, int32_
 size_t mr_workspace_bytes(int32_t M_max, int32_t E, int32_t k, int32_t has_shared);
 
 /* Re-zero the whole workspace (ws_bytes bytes) on `stream` with a small fill
- * kernel (safe to capture).  Needed only after an aborted launch. */
+ * kernel (safe to capture).  Needed only after an aborted launch, or after
+ * one whose status (below) is not MR_STATUS_OK. */
 int mr_workspace_reset(void *ws, size_t ws_bytes, void *stream);
+
+/* Status of the launches on a workspace.  Blocks of one route launch wait
+ * for each other (the small-M tail for the gate keys, the prefill launch at
+ * its grid barriers and token-tile waits), which assumes that every block of
+ * the launch runs: the prefill launch sizes its grid so that all its blocks
+ * fit on the GPU at once, but other work holding compute units can still
+ * delay some.  Every such wait is bounded; one that gives up ORs its bit
+ * into a status word in the workspace and the launch runs to its end with
+ * whatever data it has.  The outputs of such a launch are undefined, an
+ * align launch writes *npp = -1, and the workspace must be reset
+ * (mr_workspace_reset) before its next use, since blocks that arrived late
+ * may have left its counters out of step.  This is the failure signal of
+ * "monokernel decode for ..." (vLLM PR), Limitations/follow-ups, Failure:
+ * a sticky failed word that the caller reads after each step, so that the
+ * engine stops instead of hanging or going on with bad routing.
+ * The word is sticky: it keeps its bits until mr_workspace_reset.
+ *
+ * mr_workspace_status enqueues on `stream` one small kernel that copies the
+ * word into *status (device int32, caller-owned, 4-byte aligned), so it
+ * orders after the launches before it on that stream and can be captured
+ * into a graph.  Returns MR_OK; MR_EINVAL for a NULL ws or status;
+ * MR_EUNSUPPORTED for a ws that is not 256-byte aligned or a misaligned
+ * status; MR_ECAPACITY if ws_bytes is smaller than the counter region;
+ * MR_ELAUNCH if the launch fails. */
+#define MR_STATUS_OK 0
+#define MR_STATUS_KEY_WAIT 1   /* small M: the tail's wait for the gate keys */
+#define MR_STATUS_ID_WAIT 2    /* small M: block 0's wait for the other tail blocks' ids */
+#define MR_STATUS_GRID_WAIT 4  /* prefill: a grid barrier */
+#define MR_STATUS_TILE_WAIT 8  /* prefill: the wait for a token tile's gate items */
+int mr_workspace_status(const void *ws, size_t ws_bytes, int32_t *status, void *stream);
+
+/* Test hook, not part of the routing API: the number of polls every bounded
+ * wait of later route launches (any workspace, this process) makes before it
+ * gives up.  0 makes each wait give up at once, without polling, which lets
+ * a test drive the failure path while every kernel still runs to its end;
+ * a negative value restores the kernels' own bounds (millions of polls, far
+ * beyond any launch that runs normally).  Always returns MR_OK. */
+int mr_debug_set_wait_limit(int32_t polls);
 
 /* Route [R], Modifications: gate contraction in fp32, bf16 rounding of the
  * routed logits, top-k (lower id wins ties), softmax + renormalise, shared

@@ -18,6 +18,11 @@ MR_EUNSUPPORTED = -2
 MR_ECAPACITY = -3
 MR_ELAUNCH = -4
 MR_STREAM_READ_OUT_WORDS = 4096
+MR_STATUS_OK = 0
+MR_STATUS_KEY_WAIT = 1
+MR_STATUS_ID_WAIT = 2
+MR_STATUS_GRID_WAIT = 4
+MR_STATUS_TILE_WAIT = 8
 
 # Every symbol include/moeroute.h declares, with (restype, argtypes).
 _P = ctypes.c_void_p
@@ -33,6 +38,8 @@ SIGNATURES = {
     "mr_expert_ids_capacity": (_I64, [_I32, _I32, _I32, _I32]),
     "mr_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
     "mr_workspace_reset": (ctypes.c_int, [_P, _SZ, _P]),
+    "mr_workspace_status": (ctypes.c_int, [_P, _SZ, _P, _P]),
+    "mr_debug_set_wait_limit": (ctypes.c_int, [_I32]),
     "mr_route": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _F32, _P, _P, _P, _SZ, _P]),
     "mr_align": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _P, _I64, _P, _I64, _P, _P, _SZ, _P]),
     "mr_align_local": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _I32, _I32, _P, _I64, _P, _I64, _P, _P, _SZ,
@@ -103,6 +110,55 @@ def _bf16_2d(t, name):
     return t
 
 
+def _on(t, name, device):
+    """t must be a tensor on `device` (a GPU): the library dereferences every
+    pointer on that device, so a host tensor or another GPU's memory would be
+    read or written out of bounds instead of refused."""
+    if t.device != device or device.type != "cuda":
+        raise ValueError(f"{name} is on {t.device}, expected {device} (a GPU device)")
+    return t
+
+
+def _out(t, name, dtype, device, numel=None, min_numel=None):
+    """A caller-supplied buffer: dtype, contiguity, device and size."""
+    if t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor")
+    _on(t, name, device)
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected at least {min_numel}")
+    return t
+
+
+def _ws_bytes(workspace, device):
+    """Byte size of a workspace tensor (contiguous, on `device`)."""
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    _on(workspace, "workspace", device)
+    return workspace.numel() * workspace.element_size()
+
+
+def _gate_inputs(x, gate_w, shared_w):
+    """Checks the router inputs; returns (M, H, E, device)."""
+    import torch
+
+    _bf16_2d(x, "x")
+    _bf16_2d(gate_w, "gate_w")
+    M, H = x.shape
+    E, H2 = gate_w.shape
+    if H2 != H:
+        raise ValueError(f"gate_w is [{E}, {H2}], expected [E, {H}] (x is [{M}, {H}])")
+    dev = x.device
+    _on(x, "x", dev)
+    _on(gate_w, "gate_w", dev)
+    if shared_w is not None:
+        if shared_w.dtype != torch.bfloat16 or not shared_w.is_contiguous() or shared_w.numel() != H:
+            raise ValueError(f"shared_w must be a contiguous bfloat16 tensor of {H} elements")
+        _on(shared_w, "shared_w", dev)
+    return M, H, E, dev
+
+
 # --------------------------------------------------------------- host-only --
 
 def mr_abi_version() -> int:
@@ -140,7 +196,29 @@ def new_workspace(M_max: int, E: int, k: int, has_shared: bool, device="cuda"):
 
 
 def mr_workspace_reset(workspace, stream=None) -> None:
-    _check(lib().mr_workspace_reset(_ptr(workspace), workspace.numel(), _stream(stream, workspace.device)))
+    nbytes = _ws_bytes(workspace, workspace.device)
+    _check(lib().mr_workspace_reset(_ptr(workspace), nbytes, _stream(stream, workspace.device)))
+
+
+def mr_workspace_status(workspace, out=None, stream=None):
+    """The workspace's sticky status word (MR_STATUS_* bits of the bounded
+    waits that gave up since the last reset), copied on the stream into a
+    device int32 tensor [1] (returned; `out` if given)."""
+    import torch
+
+    dev = workspace.device
+    nbytes = _ws_bytes(workspace, dev)
+    if out is None:
+        out = torch.empty(1, dtype=torch.int32, device=dev)
+    _out(out, "out", torch.int32, dev, min_numel=1)
+    _check(lib().mr_workspace_status(_ptr(workspace), nbytes, _ptr(out), _stream(stream, dev)))
+    return out
+
+
+def mr_debug_set_wait_limit(polls: int) -> None:
+    """Test hook: polls every bounded wait of later launches makes before
+    giving up (0: at once; negative: the kernels' own bounds)."""
+    _check(lib().mr_debug_set_wait_limit(int(polls)))
 
 
 def mr_route(x, gate_w, shared_w, k: int, scale: float = 1.0, *, workspace,
@@ -148,18 +226,17 @@ def mr_route(x, gate_w, shared_w, k: int, scale: float = 1.0, *, workspace,
     """Returns (topk_ids [M, S] int32, topk_weights [M, S] float32)."""
     import torch
 
-    _bf16_2d(x, "x")
-    _bf16_2d(gate_w, "gate_w")
-    M, H = x.shape
-    E = gate_w.shape[0]
+    M, H, E, dev = _gate_inputs(x, gate_w, shared_w)
     S = k + (shared_w is not None)
     if topk_ids is None:
-        topk_ids = torch.empty((M, S), dtype=torch.int32, device=x.device)
+        topk_ids = torch.empty((M, S), dtype=torch.int32, device=dev)
     if topk_weights is None:
-        topk_weights = torch.empty((M, S), dtype=torch.float32, device=x.device)
+        topk_weights = torch.empty((M, S), dtype=torch.float32, device=dev)
+    _out(topk_ids, "topk_ids", torch.int32, dev, numel=M * S)
+    _out(topk_weights, "topk_weights", torch.float32, dev, numel=M * S)
+    nbytes = _ws_bytes(workspace, dev)
     _check(lib().mr_route(_ptr(x), _ptr(gate_w), _ptr(shared_w), M, H, E, k, float(scale),
-                          _ptr(topk_ids), _ptr(topk_weights), _ptr(workspace), workspace.numel(),
-                          _stream(stream, x.device)))
+                          _ptr(topk_ids), _ptr(topk_weights), _ptr(workspace), nbytes, _stream(stream, dev)))
     return topk_ids, topk_weights
 
 
@@ -173,6 +250,10 @@ def _align_outputs(M, S, num_experts, A, device, sorted_token_ids, expert_ids, n
         expert_ids = torch.empty(max(cap // A, 1), dtype=torch.int32, device=device)
     if npp is None:
         npp = torch.empty(1, dtype=torch.int32, device=device)
+    # capacities are checked by the library against the lengths passed
+    _out(sorted_token_ids, "sorted_token_ids", torch.int32, device)
+    _out(expert_ids, "expert_ids", torch.int32, device)
+    _out(npp, "npp", torch.int32, device, min_numel=1)
     return sorted_token_ids, expert_ids, npp
 
 
@@ -184,14 +265,16 @@ def mr_align(topk_ids, num_experts: int, A: int, *, workspace, sorted_token_ids=
 
     if topk_ids.dtype != torch.int32 or not topk_ids.is_contiguous():
         raise ValueError("topk_ids must be a contiguous int32 tensor")
+    dev = topk_ids.device
+    _on(topk_ids, "topk_ids", dev)
     ids2 = topk_ids.view(topk_ids.shape[0], -1) if topk_ids.dim() >= 1 and topk_ids.numel() else topk_ids
     M = topk_ids.shape[0] if topk_ids.dim() else 0
     S = ids2.shape[1] if ids2.dim() == 2 else 1
-    sorted_token_ids, expert_ids, npp = _align_outputs(M, S, num_experts, A, topk_ids.device,
-                                                       sorted_token_ids, expert_ids, npp)
+    sorted_token_ids, expert_ids, npp = _align_outputs(M, S, num_experts, A, dev, sorted_token_ids, expert_ids, npp)
+    nbytes = _ws_bytes(workspace, dev)
     _check(lib().mr_align(_ptr(topk_ids), M, S, num_experts, A, _ptr(sorted_token_ids),
                           sorted_token_ids.numel(), _ptr(expert_ids), expert_ids.numel(), _ptr(npp),
-                          _ptr(workspace), workspace.numel(), _stream(stream, topk_ids.device)))
+                          _ptr(workspace), nbytes, _stream(stream, dev)))
     return sorted_token_ids, expert_ids, npp
 
 
@@ -207,15 +290,18 @@ def mr_align_local(topk_ids, expert_map, num_local_experts: int, A: int, *, work
         raise ValueError("topk_ids must be a contiguous int32 tensor")
     if expert_map.dtype != torch.int32 or not expert_map.is_contiguous():
         raise ValueError("expert_map must be a contiguous int32 tensor")
+    dev = topk_ids.device
+    _on(topk_ids, "topk_ids", dev)
+    _on(expert_map, "expert_map", dev)
     ids2 = topk_ids.view(topk_ids.shape[0], -1) if topk_ids.dim() >= 1 and topk_ids.numel() else topk_ids
     M = topk_ids.shape[0] if topk_ids.dim() else 0
     S = ids2.shape[1] if ids2.dim() == 2 else 1
-    sorted_token_ids, expert_ids, npp = _align_outputs(M, S, num_local_experts, A, topk_ids.device,
-                                                       sorted_token_ids, expert_ids, npp)
+    sorted_token_ids, expert_ids, npp = _align_outputs(M, S, num_local_experts, A, dev, sorted_token_ids,
+                                                       expert_ids, npp)
+    nbytes = _ws_bytes(workspace, dev)
     _check(lib().mr_align_local(_ptr(topk_ids), M, S, expert_map.numel(), _ptr(expert_map), num_local_experts, A,
                                 _ptr(sorted_token_ids), sorted_token_ids.numel(), _ptr(expert_ids),
-                                expert_ids.numel(), _ptr(npp), _ptr(workspace), workspace.numel(),
-                                _stream(stream, topk_ids.device)))
+                                expert_ids.numel(), _ptr(npp), _ptr(workspace), nbytes, _stream(stream, dev)))
     return sorted_token_ids, expert_ids, npp
 
 
@@ -226,24 +312,23 @@ def mr_route_align(x, gate_w, shared_w, k: int, scale: float = 1.0, A: int | Non
     Returns dict(topk_ids, topk_weights, sorted_token_ids, expert_ids, npp, A)."""
     import torch
 
-    _bf16_2d(x, "x")
-    _bf16_2d(gate_w, "gate_w")
-    M, H = x.shape
-    E = gate_w.shape[0]
+    M, H, E, dev = _gate_inputs(x, gate_w, shared_w)
     sh = shared_w is not None
     S = k + sh
     if A is None:
         A = mr_select_alignment(M, k, E)
     if topk_ids is None:
-        topk_ids = torch.empty((M, S), dtype=torch.int32, device=x.device)
+        topk_ids = torch.empty((M, S), dtype=torch.int32, device=dev)
     if topk_weights is None:
-        topk_weights = torch.empty((M, S), dtype=torch.float32, device=x.device)
-    sorted_token_ids, expert_ids, npp = _align_outputs(M, S, E + sh, A, x.device, sorted_token_ids,
-                                                       expert_ids, npp)
+        topk_weights = torch.empty((M, S), dtype=torch.float32, device=dev)
+    _out(topk_ids, "topk_ids", torch.int32, dev, numel=M * S)
+    _out(topk_weights, "topk_weights", torch.float32, dev, numel=M * S)
+    sorted_token_ids, expert_ids, npp = _align_outputs(M, S, E + sh, A, dev, sorted_token_ids, expert_ids, npp)
+    nbytes = _ws_bytes(workspace, dev)
     _check(lib().mr_route_align(_ptr(x), _ptr(gate_w), _ptr(shared_w), M, H, E, k, float(scale), A,
                                 _ptr(topk_ids), _ptr(topk_weights), _ptr(sorted_token_ids),
                                 sorted_token_ids.numel(), _ptr(expert_ids), expert_ids.numel(), _ptr(npp),
-                                _ptr(workspace), workspace.numel(), _stream(stream, x.device)))
+                                _ptr(workspace), nbytes, _stream(stream, dev)))
     return {"topk_ids": topk_ids, "topk_weights": topk_weights, "sorted_token_ids": sorted_token_ids,
             "expert_ids": expert_ids, "npp": npp, "A": A}
 
@@ -252,15 +337,14 @@ def mr_debug_gate_logits(x, gate_w, shared_w, *, workspace, logits=None, stream=
     """Test hook: the fp32 logits [M, E + shared] the route kernels compute."""
     import torch
 
-    _bf16_2d(x, "x")
-    _bf16_2d(gate_w, "gate_w")
-    M, H = x.shape
-    E = gate_w.shape[0]
+    M, H, E, dev = _gate_inputs(x, gate_w, shared_w)
     Ep = E + (shared_w is not None)
     if logits is None:
-        logits = torch.empty((M, Ep), dtype=torch.float32, device=x.device)
+        logits = torch.empty((M, Ep), dtype=torch.float32, device=dev)
+    _out(logits, "logits", torch.float32, dev, numel=M * Ep)
+    nbytes = _ws_bytes(workspace, dev)
     _check(lib().mr_debug_gate_logits(_ptr(x), _ptr(gate_w), _ptr(shared_w), M, H, E, _ptr(logits),
-                                      _ptr(workspace), workspace.numel(), _stream(stream, x.device)))
+                                      _ptr(workspace), nbytes, _stream(stream, dev)))
     return logits
 
 
@@ -268,11 +352,15 @@ def mr_debug_stream_read(src, out, nbytes=None, stream=None):
     """Measurement hook: one plain streaming-read launch over the first
     nbytes of src (default: all of it).  out: MR_STREAM_READ_OUT_WORDS int32
     words on the device; block b stores the XOR of what it read in out[b]."""
-    if not src.is_contiguous():
-        raise ValueError("src must be contiguous")
+    if not src.is_contiguous() or not out.is_contiguous():
+        raise ValueError("src and out must be contiguous")
+    _on(src, "src", src.device)
+    _on(out, "out", src.device)
     if out.numel() * out.element_size() < 4 * MR_STREAM_READ_OUT_WORDS:
         raise ValueError(f"out must hold {MR_STREAM_READ_OUT_WORDS} 32-bit words")
     n = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    if n < 0 or n > src.numel() * src.element_size():
+        raise ValueError(f"nbytes={n} is outside src ({src.numel() * src.element_size()} bytes)")
     _check(lib().mr_debug_stream_read(_ptr(src), n, _ptr(out), _stream(stream, src.device)))
 
 
@@ -295,14 +383,19 @@ def mr_argmax_rows_f32(x, *, workspace, out=None, n=None, stream=None):
 
     if x.dtype != torch.float32 or x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be a 2-D float32 tensor with contiguous rows")
+    dev = x.device
+    _on(x, "x", dev)
     R, N = x.shape
+    if n is not None and not 1 <= int(n) <= N:
+        raise ValueError(f"n={n} is outside [1, {N}]")
     N = N if n is None else int(n)
     if out is None:
-        out = torch.empty(R, dtype=torch.int64, device=x.device)
+        out = torch.empty(R, dtype=torch.int64, device=dev)
+    _out(out, "out", torch.int64, dev, min_numel=R)
     # a single row's stride is never used: pass N rounded up to 4
     ld = x.stride(0) if R > 1 else N + (-N) % 4
-    _check(lib().mr_argmax_rows_f32(_ptr(x), R, N, ld, _ptr(out), _ptr(workspace), workspace.numel(),
-                                    _stream(stream, x.device)))
+    nbytes = _ws_bytes(workspace, dev)
+    _check(lib().mr_argmax_rows_f32(_ptr(x), R, N, ld, _ptr(out), _ptr(workspace), nbytes, _stream(stream, dev)))
     return out
 
 
@@ -319,9 +412,18 @@ def mr_grouped_gemm_bf16(x, w_experts, S: int, sorted_token_ids, expert_ids, npp
     Ep, N, H2 = w_experts.shape
     if H2 != H:
         raise ValueError("w_experts hidden size differs from x")
+    dev = x.device
+    _on(x, "x", dev)
+    _on(w_experts, "w_experts", dev)
+    _out(sorted_token_ids, "sorted_token_ids", torch.int32, dev)
+    # the kernel reads expert_ids for every block below npp / A, and npp can
+    # reach sorted_cap
+    _out(expert_ids, "expert_ids", torch.int32, dev, min_numel=sorted_token_ids.numel() // A)
+    _out(npp, "npp", torch.int32, dev, min_numel=1)
     if y is None:
-        y = torch.full((M * S, N), float("nan"), dtype=torch.float32, device=x.device)
+        y = torch.full((M * S, N), float("nan"), dtype=torch.float32, device=dev)
+    _out(y, "y", torch.float32, dev, numel=M * S * N)
     _check(lib().mr_grouped_gemm_bf16(_ptr(x), M, H, _ptr(w_experts), Ep, N, S, _ptr(sorted_token_ids),
                                       sorted_token_ids.numel(), _ptr(expert_ids), _ptr(npp), A, _ptr(y),
-                                      _stream(stream, x.device)))
+                                      _stream(stream, dev)))
     return y

@@ -206,6 +206,12 @@ __global__ void zero_words_kernel(uint32_t *p, size_t n) {
 
 __global__ void store_zero_kernel(int32_t *p) { *p = 0; }
 
+// Reads the status word past every cache (the route kernels OR bits into it
+// with agent-scope atomics) into the caller's buffer.
+__global__ void read_status_kernel(const uint32_t *ctr, int32_t *out) {
+  *out = (int32_t)ld_agent(ctr + kCtrError);
+}
+
 }  // namespace
 
 int align_words_per_expert(int Ep) {
@@ -230,6 +236,11 @@ hipError_t launch_zero_words(uint32_t *p, size_t n, hipStream_t stream) {
 
 hipError_t launch_store_zero(int32_t *p, hipStream_t stream) {
   store_zero_kernel<<<1, 1, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_read_status(const uint32_t *ctr, int32_t *out, hipStream_t stream) {
+  read_status_kernel<<<1, 1, 0, stream>>>(ctr, out);
   return hipGetLastError();
 }
 

@@ -7,6 +7,7 @@
 // ROCm Kernels for AMD MI350X", Compile exact contracts).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -23,10 +24,21 @@
 static_assert(MR_MAX_ROUTED_EXPERTS == mr::kMaxRouteExperts, "route expert limit");
 static_assert(MR_MAX_ALIGN_EXPERTS == mr::kMaxAlignExperts, "align expert limit");
 static_assert(MR_MAX_TOPK == mr::kMaxTopK, "top-k limit");
+static_assert(MR_STATUS_KEY_WAIT == mr::kWaitKeys && MR_STATUS_ID_WAIT == mr::kWaitIds &&
+                  MR_STATUS_GRID_WAIT == mr::kWaitGrid && MR_STATUS_TILE_WAIT == mr::kWaitTile,
+              "status bits");
 
 namespace {
 
 thread_local std::string g_last_error;
+
+// Polls a bounded wait may make before giving up: < 0 keeps each kernel's
+// own bound (mr_debug_set_wait_limit).
+std::atomic<int> g_wait_limit{-1};
+int wait_limit(int fallback) {
+  const int v = g_wait_limit.load(std::memory_order_relaxed);
+  return v < 0 ? fallback : v;
+}
 
 struct Checks {
   std::string msg;
@@ -56,6 +68,14 @@ struct Checks {
 };
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Row stride (floats) of the prefill launch's split-K partial rows: E rounded
+// up to 32, so that every partial row starts on its own 128-byte line (the
+// workspace is 256-byte aligned and the region offsets are multiples of 256).
+// Rows written by different gate items then never share a line, and a
+// reader can never pull a line into its L2 before every writer of that line
+// is done.
+inline int64_t partial_stride(int64_t E) { return (E + 31) / 32 * 32; }
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
 
@@ -91,7 +111,7 @@ Layout layout_for(int64_t M, int64_t E, int64_t k, int64_t sh) {
   L.counts = take(o, (size_t)(nch * ((Ep + 3) / 4 * 4)) * 4);
   L.ranks = take(o, (size_t)n * 4);
   // split-K partials: for any M' <= M, splits * M' <= max(M, (grid / NE) * min(M, 128))
-  const int64_t Epad = (E + 3) / 4 * 4;
+  const int64_t Epad = partial_stride(E);
   const int64_t NT = (M + 127) / 128;
   int64_t rows = (mr::kMfmaMaxGrid / (NE > 0 ? NE : 1)) * (M < 128 ? M : 128);
   if (rows < M) rows = M;
@@ -146,7 +166,7 @@ void check_align_outputs(Checks &ck, int64_t n, int64_t Ep, int32_t A, const int
 
 void check_workspace(Checks &ck, const void *ws, size_t ws_bytes, size_t need) {
   if (!ws) ck.fail(MR_EINVAL, "ws is NULL");
-  else if (!aligned16(ws)) ck.fail(MR_EUNSUPPORTED, "ws is not 16-byte aligned");
+  else if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) ck.fail(MR_EUNSUPPORTED, "ws is not 256-byte aligned");
   if (ws_bytes < need) ck.fail(MR_ECAPACITY, "ws_bytes=%zu < %zu", ws_bytes, need);
 }
 
@@ -234,7 +254,7 @@ int route_impl(const char *fn, const void *x, const void *gate_w, const void *sh
     q.items = q.NE * q.NT * q.SK;
     q.grid = grid;
     q.xcd_map = (grid % 8 == 0) ? 1 : 0;
-    q.Epad = (E + 3) / 4 * 4;
+    q.Epad = (int)partial_stride(E);
     q.part = reinterpret_cast<float *>(wsb + L.part);
     q.tcnt = reinterpret_cast<uint32_t *>(wsb + L.tcnt);
     q.tcnt_row = (int)((Ep + 3) / 4 * 4);
@@ -255,10 +275,13 @@ int route_impl(const char *fn, const void *x, const void *gate_w, const void *sh
     q.A = do_align ? A : 64;
     q.log2A = do_align ? log2A : 6;
     q.sorted = sorted;
+    q.sorted_cap = sorted_cap;
     q.expert_ids = expert_ids;
+    q.expert_cap = expert_cap;
     q.npp = npp;
     q.logits_out = logits_out;
     q.logits_only = logits_only ? 1 : 0;
+    q.wait_limit = wait_limit(mr::kBarrierSpin);
     return launch_result(mr::launch_route_mfma(q, s), fn);
   }
 
@@ -282,6 +305,7 @@ int route_impl(const char *fn, const void *x, const void *gate_w, const void *sh
   p.logits_out = logits_out;
   p.ctr = ctr;
   p.logits_only = logits_only ? 1 : 0;
+  p.wait_limit = wait_limit(mr::kPollSpin);
   p.do_align = do_align ? 1 : 0;
   p.A = do_align ? A : 64;
   p.log2A = do_align ? log2A : 6;
@@ -336,6 +360,25 @@ int mr_workspace_reset(void *ws, size_t ws_bytes, void *stream) {
   return launch_result(mr::launch_zero_words(static_cast<uint32_t *>(ws), ws_bytes / 4,
                                              reinterpret_cast<hipStream_t>(stream)),
                        "mr_workspace_reset");
+}
+
+int mr_workspace_status(const void *ws, size_t ws_bytes, int32_t *status, void *stream) {
+  Checks ck;
+  if (!ws) ck.fail(MR_EINVAL, "ws is NULL");
+  else if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) ck.fail(MR_EUNSUPPORTED, "ws is not 256-byte aligned");
+  if (ws_bytes < mr::kCounterBytes) ck.fail(MR_ECAPACITY, "ws_bytes=%zu < %zu", ws_bytes, mr::kCounterBytes);
+  if (!status) ck.fail(MR_EINVAL, "status is NULL");
+  else if ((reinterpret_cast<uintptr_t>(status) & 3u) != 0) ck.fail(MR_EUNSUPPORTED, "status is not 4-byte aligned");
+  if (ck.code() != MR_OK) return ck.finish("mr_workspace_status");
+  return launch_result(mr::launch_read_status(static_cast<const uint32_t *>(ws), status,
+                                              reinterpret_cast<hipStream_t>(stream)),
+                       "mr_workspace_status");
+}
+
+int mr_debug_set_wait_limit(int32_t polls) {
+  g_wait_limit.store(polls < 0 ? -1 : polls, std::memory_order_relaxed);
+  g_last_error.clear();
+  return MR_OK;
 }
 
 int mr_route(const void *x, const void *gate_w, const void *shared_w, int32_t M, int32_t H, int32_t E,

@@ -78,18 +78,6 @@ constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0
 constexpr int kQuadRev = 0x1B;        // quad_perm [3,2,1,0]
 constexpr int kRowRor8 = 0x128;       // lane i <- lane (i + 8) mod 16 within 16: i ^ 8
 
-// Max over the 64 lanes; every lane must be active.  Returns a wave-uniform
-// value.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, dpp_u32<kQuadXor1>(v));
-  v = max(v, dpp_u32<kQuadXor2>(v));
-  v = max(v, dpp_u32<kRowHalfMirror>(v));
-  v = max(v, dpp_u32<kRowMirror>(v));
-  uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
-  uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
-  return max(max(a, b), max(c, d));
-}
-
 // Max over the 64 lanes, left in every lane (no scalar round trip): DPP
 // within rows of 16, then gfx950's permlane16/permlane32 swaps pair each lane
 // with lane^16 and lane^32.  Every lane must be active.
@@ -273,15 +261,6 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   return (a + b) + (c + d);
 }
 
-__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-  v += dpp_u32<kQuadXor1>(v);
-  v += dpp_u32<kQuadXor2>(v);
-  v += dpp_u32<kRowHalfMirror>(v);
-  v += dpp_u32<kRowMirror>(v);
-  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
-         __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
-}
-
 // Inclusive prefix sum over the 64 lanes; every lane must be active.
 __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v, int lane) {
   v += dpp_u32<kRowShr1>(v);
@@ -316,16 +295,6 @@ __device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t *tm
   __syncthreads();
   *total = tot;
   return base + incl - v;
-}
-
-// Makes LDS writes by other lanes of this wave visible to this lane's later
-// LDS reads.  The hardware already executes a wave's LDS operations in order;
-// the fence stops the compiler from reusing a value this lane itself stored
-// or loaded earlier (lanes exchanging data through LDS without it is a data
-// race the compiler may optimise away).
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-  __builtin_amdgcn_wave_barrier();
 }
 
 // ------------------------------------------------------- grid hand-off ---
@@ -387,37 +356,6 @@ __device__ __forceinline__ void ld_coherent8(uint32_t (&v)[8], const uint32_t *c
       : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
       : "memory");
 }
-__device__ __forceinline__ void ld_coherent8(unsigned long long (&v)[8], const unsigned long long *const (&a)[8]) {
-  asm volatile(
-      "global_load_dwordx2 %0, %8, off sc1\n\t"
-      "global_load_dwordx2 %1, %9, off sc1\n\t"
-      "global_load_dwordx2 %2, %10, off sc1\n\t"
-      "global_load_dwordx2 %3, %11, off sc1\n\t"
-      "global_load_dwordx2 %4, %12, off sc1\n\t"
-      "global_load_dwordx2 %5, %13, off sc1\n\t"
-      "global_load_dwordx2 %6, %14, off sc1\n\t"
-      "global_load_dwordx2 %7, %15, off sc1\n\t"
-      "s_waitcnt vmcnt(0)"
-      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
-      : "memory");
-}
-__device__ __forceinline__ void ld_coherent8(u32x4_coh (&v)[8], const u32x4_coh *const (&a)[8]) {
-  asm volatile(
-      "global_load_dwordx4 %0, %8, off sc1\n\t"
-      "global_load_dwordx4 %1, %9, off sc1\n\t"
-      "global_load_dwordx4 %2, %10, off sc1\n\t"
-      "global_load_dwordx4 %3, %11, off sc1\n\t"
-      "global_load_dwordx4 %4, %12, off sc1\n\t"
-      "global_load_dwordx4 %5, %13, off sc1\n\t"
-      "global_load_dwordx4 %6, %14, off sc1\n\t"
-      "global_load_dwordx4 %7, %15, off sc1\n\t"
-      "s_waitcnt vmcnt(0)"
-      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
-      : "memory");
-}
-
 // Sixteen 16-byte coherent loads, one wait (see ld_coherent8).
 __device__ __forceinline__ void ld_coherent16(u32x4_coh (&v)[16], const u32x4_coh *const (&a)[16]) {
   asm volatile(

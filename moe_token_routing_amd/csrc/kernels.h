@@ -27,11 +27,21 @@ enum CounterIndex : int {
   kCtrPublished = 3,  // winner's publication flag
   kCtrWork = 4,       // work-queue head
   kCtrExited = 5,     // block exits
-  kCtrError = 6,      // set to 1 if a bounded wait gave up (never expected)
+  kCtrError = 6,      // status: kWait* bits of the bounded waits that gave up (sticky until a reset)
   kCtrEpoch = 16,     // prefill launches so far (any value is a valid start)
   kCtrBarTop1 = 32,   // prefill grid barrier, set 1: completed lanes
   kCtrZero16 = 60,    // words 60..63: always zero (a 16-byte zero source)
 };
+// Bits of the status word (kCtrError), one per kind of bounded wait.  A
+// wait that gives up ORs its bit in and the launch goes on with whatever data
+// it has; its outputs are then undefined and an align launch writes npp = -1.
+constexpr uint32_t kWaitKeys = 1;     // small M: a tail wave's poll of the gate keys (MR_STATUS_KEY_WAIT)
+constexpr uint32_t kWaitIds = 2;      // small M: block 0's poll of the other tail blocks' ids (MR_STATUS_ID_WAIT)
+constexpr uint32_t kWaitGrid = 4;     // prefill: a grid barrier (MR_STATUS_GRID_WAIT)
+constexpr uint32_t kWaitTile = 8;     // prefill: a token tile's gate items (MR_STATUS_TILE_WAIT)
+// Bounds on the waits (polls), unless the caller sets one for tests.
+constexpr int kPollSpin = 1 << 21;     // small M: each poll is one memory round trip
+constexpr int kBarrierSpin = 1 << 22;  // prefill: each poll is a load and a short sleep
 constexpr int kTicketLanes = 16;
 constexpr int kTicketLaneStride = 64;  // words (256 bytes); set s of lane r at word 64 + 64 r + 32 s
 constexpr int kReleaseWord = 8;        // words after a lane counter: its barrier release word
@@ -61,6 +71,7 @@ struct SmallParams {
   float *logits_out;  // logits_only: the caller's [M, Ep] fp32 buffer
   uint32_t *ctr;      // counter words (kCounterBytes)
   int logits_only;
+  int wait_limit;     // polls a wait makes before it gives up (0: gives up at once)
   // align
   int do_align, A, log2A;
   uint32_t S_magic;  // ceil(2^32 / S): i / S == umulhi(i, S_magic) for i < 2^32 / S
@@ -111,7 +122,7 @@ struct MfmaParams {
   int items;     // NE * NT * SK
   int grid;      // blocks (all resident)
   int xcd_map;   // deal items to XCDs (grid % 8 == 0)
-  int Epad;      // row stride of the partials (E rounded up to 4)
+  int Epad;      // row stride of the partials (E rounded up to 32: one 128-byte line per row start)
   float *part;   // [SK, M, Epad] fp32 gate partials
   uint32_t *tcnt;       // [NT, tcnt_row]: pairs per (128-token tile, expert)
   int tcnt_row;         // words per tcnt row: Ep rounded up to 4
@@ -121,10 +132,13 @@ struct MfmaParams {
   int tpb, ngroups;     // tokens per top-k group (power of two <= 128) and groups
   int do_align, A, log2A;
   int32_t *sorted;
+  int64_t sorted_cap;
   int32_t *expert_ids;
+  int64_t expert_cap;
   int32_t *npp;
   float *logits_out;  // logits_only: the caller's [M, Ep] fp32 buffer
   int logits_only;
+  int wait_limit;     // polls a wait makes before it gives up (0: gives up at once)
 };
 size_t mfma_lds_bytes();
 int mfma_capacity(int E);
@@ -140,5 +154,7 @@ hipError_t launch_align(const AlignParams &p, hipStream_t stream);
 // Fill n words with zero / write *npp = 0 (small kernels, graph-safe).
 hipError_t launch_zero_words(uint32_t *p, size_t n, hipStream_t stream);
 hipError_t launch_store_zero(int32_t *p, hipStream_t stream);
+// *out = the status word (a coherent read), on the stream.
+hipError_t launch_read_status(const uint32_t *ctr, int32_t *out, hipStream_t stream);
 
 }  // namespace mr

@@ -70,7 +70,6 @@ constexpr int kStageBytes = (kTE + kTT) * kRowBytes;  // 32 KB
 constexpr int kRingBytes = kNS * kStageBytes;          // 128 KB
 constexpr int kTilePitch = kTT + 4;      // fp32 pitch of the transpose tile
 constexpr int kOwnBytes = 17408;         // phases T and A: a group's ids (tpb * S <= 128 * 33) at the start of LDS
-constexpr int kBarrierSpin = 1 << 22;    // bound on a grid-barrier wait
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
@@ -96,11 +95,13 @@ __device__ __forceinline__ void wait_vmcnt() {
 // not treat every later LDS read as dependent on it (it would wait for all
 // outstanding loads); the pipeline waits for these loads itself with
 // wait_vmcnt before the barrier that publishes a stage.
+// The LDS base goes in through an M0 operand (the compiler writes M0); the
+// s_nop gives the M0 write its wait state before the load reads it.
 __device__ __forceinline__ void load_lds16(const void *src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
-               : "v"(src), "s"(lds_base)
-               : "memory", "m0");
+               : "v"(src), "{m0}"(lds_base)
+               : "memory");
 }
 
 __device__ __forceinline__ uint4 lds16(const uint8_t *p) { return *reinterpret_cast<const uint4 *>(p); }
@@ -139,8 +140,9 @@ __device__ __forceinline__ void wait_stages(int n) {
 // waits on its own lane's release word, so no address has more than
 // grid / kTicketLanes pollers.  Data written with st_agent (or agent-scope
 // atomics) before the barrier is visible to coherent loads (ld_agent,
-// ld_coherent8) after it.  The wait is bounded: if it gives up, the error
-// word is set and the block goes on.  Only thread 0's arguments matter.
+// ld_coherent8) after it.  The wait is bounded (limit polls): if it gives
+// up, its bit goes into the status word, the block's failed flag is raised
+// and the block goes on.  Only thread 0's arguments matter.
 __device__ __forceinline__ uint32_t *barrier_lane(uint32_t *ctr, uint32_t set, uint32_t r) {
   return ctr + 64 + (size_t)r * kTicketLaneStride + 32 * set;
 }
@@ -169,24 +171,36 @@ __device__ __forceinline__ void grid_arrive(uint32_t *ctr, uint32_t set, uint32_
     }
   }
 }
-__device__ __forceinline__ void grid_wait(uint32_t *ctr, uint32_t set, uint32_t gen, uint32_t grid) {
+// Thread 0 polls *word until it reaches `target`, at most `limit` times
+// (none at limit 0); on giving up it ORs `bit` into the status word and
+// raises *failed.
+__device__ __forceinline__ void bounded_wait(const uint32_t *word, uint32_t target, int limit, uint32_t *ctr,
+                                             uint32_t bit, uint32_t *failed) {
+  bool done = false;
+  for (int it = 0; it < limit; ++it) {
+    if (__hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) {
+      done = true;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  if (!done) {
+    __hip_atomic_fetch_or(ctr + kCtrError, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *failed = 1u;
+  }
+}
+__device__ __forceinline__ void grid_wait(uint32_t *ctr, uint32_t set, uint32_t gen, uint32_t grid, int limit,
+                                          uint32_t *failed) {
   if (threadIdx.x == 0) {
     const uint32_t nl = grid < (uint32_t)kTicketLanes ? grid : (uint32_t)kTicketLanes;
-    uint32_t *rel = barrier_release(ctr, set, blockIdx.x % nl);
-    int it = 0;
-    while (__hip_atomic_load(rel, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < gen) {
-      if (++it == kBarrierSpin) {
-        __hip_atomic_store(ctr + kCtrError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
+    bounded_wait(barrier_release(ctr, set, blockIdx.x % nl), gen, limit, ctr, kWaitGrid, failed);
   }
   __syncthreads();
 }
-__device__ __forceinline__ void grid_barrier(uint32_t *ctr, uint32_t set, uint32_t gen, uint32_t grid) {
+__device__ __forceinline__ void grid_barrier(uint32_t *ctr, uint32_t set, uint32_t gen, uint32_t grid, int limit,
+                                             uint32_t *failed) {
   grid_arrive(ctr, set, gen, grid);
-  grid_wait(ctr, set, gen, grid);
+  grid_wait(ctr, set, gen, grid, limit, failed);
 }
 
 // Tile-ready counter of token tile t in counter set `set` (zero at launch
@@ -203,18 +217,9 @@ __device__ __forceinline__ void tile_arrive(uint32_t *ctr, uint32_t set, int t) 
 }
 // Waits until all `count` items of token tile t have arrived (bounded, like
 // grid_wait).  Every thread of the block must call it.
-__device__ __forceinline__ void tile_wait(uint32_t *ctr, uint32_t set, int t, uint32_t count) {
-  if (threadIdx.x == 0) {
-    uint32_t *r = tile_ready(ctr, set, t);
-    int it = 0;
-    while (__hip_atomic_load(r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < count) {
-      if (++it == kBarrierSpin) {
-        __hip_atomic_store(ctr + kCtrError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
-  }
+__device__ __forceinline__ void tile_wait(uint32_t *ctr, uint32_t set, int t, uint32_t count, int limit,
+                                          uint32_t *failed) {
+  if (threadIdx.x == 0) bounded_wait(tile_ready(ctr, set, t), count, limit, ctr, kWaitTile, failed);
   __syncthreads();
 }
 
@@ -771,7 +776,8 @@ __device__ uint32_t align_group(const MfmaParams &p, int g, const int32_t *own, 
     } else {
       continue;
     }
-    p.sorted[dst] = (t0 + tok) * S + (i - tok * S);
+    // in range unless a wait gave up (the counts are then not to be trusted)
+    if (dst < (uint64_t)p.sorted_cap) p.sorted[dst] = (t0 + tok) * S + (i - tok * S);
   }
   return npp;
 }
@@ -781,8 +787,10 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(MfmaParams p) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   __shared__ uint32_t scan_tmp[kThreads / kWave + 1];
   __shared__ float sh_first[128];  // shared logits of the block's first token group
+  __shared__ uint32_t failed;      // a wait of this block gave up (set by thread 0 only)
   const int b = blockIdx.x;
   const uint32_t grid = gridDim.x;
+  if (threadIdx.x == 0) failed = 0u;
 
   // Barrier counter set of this launch: the parity of the launch count.  The
   // other set was used by the previous launch (which has finished); block 0
@@ -857,8 +865,8 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(MfmaParams p) {
   // shared gate row: they are computed while the other blocks' items finish.
   if (!p.tile_wait) grid_arrive(p.ctr, set, 1, grid);
   if (p.has_shared && gb < p.ngroups) shared_logits(p, gb * p.tpb, min(p.M, gb * p.tpb + p.tpb), sh_first);
-  if (!p.tile_wait) grid_wait(p.ctr, set, 1, grid);
-  if (touch == 0xFFFFFFFFu && threadIdx.x == 1000) p.npp[0] = 0;  // never true
+  if (!p.tile_wait) grid_wait(p.ctr, set, 1, grid, p.wait_limit, &failed);
+  asm volatile("" : : "v"(touch));  // keeps the warm-up loads: their value is otherwise unused
 
   // ---- T: logits, top-k, weights ----------------------------------------
   // LDS from here on: this block's ids at the start (kept until phase A);
@@ -870,11 +878,16 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(MfmaParams p) {
   const bool multi = (int)grid < p.ngroups;
   for (int g = gb; g < p.ngroups; g += grid) {
     // with tile waits, a group starts once its own token tile's items are in
-    if (p.tile_wait) tile_wait(p.ctr, set, (g * p.tpb) >> 7, (uint32_t)tile_items);
+    if (p.tile_wait) tile_wait(p.ctr, set, (g * p.tpb) >> 7, (uint32_t)tile_items, p.wait_limit, &failed);
     topk_group<NKP>(p, own, g, (p.has_shared && g == gb) ? sh_first : nullptr);
   }
   if (align) {
-    grid_barrier(p.ctr, set, p.tile_wait ? 1 : 2, grid);
+    grid_barrier(p.ctr, set, p.tile_wait ? 1 : 2, grid, p.wait_limit, &failed);
+    // A wait of any block that gave up before this barrier has set the
+    // status word before arriving here; block 0 reads it now and uses it
+    // last, so the load's latency hides under the align.
+    uint32_t status = 0;
+    if (b == 0 && threadIdx.x == 0) status = ld_agent(p.ctr + kCtrError);
     uint32_t npp = 0;
     if (!multi) {
       npp = align_group(p, gb, own, smem, scan_tmp);
@@ -887,15 +900,19 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(MfmaParams p) {
         npp = align_group(p, g, own, smem, scan_tmp);
       }
     }
-    if (b == 0 && threadIdx.x == 0) *p.npp = (int32_t)npp;
-    // padding and expert_ids of the experts dealt to this block
+    // npp = -1 marks a launch one of whose waits gave up
+    if (b == 0 && threadIdx.x == 0) *p.npp = (failed || status) ? -1 : (int32_t)npp;
+    // padding and expert_ids of the experts dealt to this block (the bounds
+    // matter only after a wait gave up: the counts are then not to be trusted)
     const uint32_t *tot = reinterpret_cast<const uint32_t *>(smem + kArrOff);
     const uint32_t *off = tot + 2 * kArrWords;
     for (int e = b; e < p.Ep; e += grid) {
-      const uint32_t c = tot[e], o = off[e];
-      const uint32_t P = (c + (uint32_t)p.A - 1u) & ~((uint32_t)p.A - 1u);
-      for (uint32_t i = c + threadIdx.x; i < P; i += kThreads) p.sorted[o + i] = p.M * p.S;
-      for (uint32_t blk = (o >> p.log2A) + threadIdx.x; blk < ((o + P) >> p.log2A); blk += kThreads)
+      const uint64_t c = tot[e], o = off[e];
+      const uint64_t P = (c + (uint64_t)p.A - 1u) & ~((uint64_t)p.A - 1u);
+      for (uint64_t i = c + threadIdx.x; i < P && o + i < (uint64_t)p.sorted_cap; i += kThreads)
+        p.sorted[o + i] = p.M * p.S;
+      for (uint64_t blk = (o >> p.log2A) + threadIdx.x; blk < ((o + P) >> p.log2A) && blk < (uint64_t)p.expert_cap;
+           blk += kThreads)
         p.expert_ids[blk] = e;
     }
   }

@@ -53,7 +53,9 @@ namespace mr {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kPollSpin = 1 << 21;  // bound on block 0's polls (each is one memory round trip)
+// What a tail block hands block 0 in place of its ids when its own key wait
+// gave up (a real hand-off value is id + 1 <= 65536).
+constexpr uint32_t kFailedHandOff = 0xFFFFFFFFu;
 static_assert(kSmallMaxTokens <= 32, "one bit per token row in rowbm; the host sends M > A to the prefill launch, so each expert's pairs (one per row) fit one block of A slots");
 
 // Max of N keys held in registers (a balanced tree, depth log2 N).
@@ -81,35 +83,48 @@ __device__ __forceinline__ void mark_pair(const SmallParams &p, int32_t id, int 
   }
 }
 
+// A bounded wait that gave up: its bit goes into the status word (agent-scope
+// atomic OR) and the block's LDS flag is raised.
+__device__ __forceinline__ void wait_failed(const SmallParams &p, uint32_t bit, uint32_t *failed, int lane) {
+  if (lane == 0) {
+    __hip_atomic_fetch_or(p.ctr + kCtrError, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *failed = 1u;
+  }
+}
+
 // Tail, part 1: token rows m0 + wave (< m1), one per wave.  Each lane
 // holds NK keys (experts lane, lane + 64, ...); a selection round is a
 // wave-wide maximum of the lanes' sorted heads, and the lane that held it
 // drops its head (keys are unique).  The ids go to the outputs and either
 // into lds_ids and the align bitmaps (block 0) or, with hand_off, to block 0
-// through the hids row (id + 1, written through).
+// through the hids row (id + 1, written through; kFailedHandOff if this
+// wave's key wait gave up).
 template <int NK>
 __device__ void route_tail_rows1(const SmallParams &p, int32_t *lds_ids, uint32_t *rowbm, uint32_t *touched,
-                                 int m0, int m1, bool hand_off) {
+                                 int m0, int m1, bool hand_off, uint32_t *failed) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = p.E, k = p.k, S = p.S;
   for (int m = m0 + wave; m < m1; m += kThreads / kWave) {
     uint32_t *kr = p.keys + (size_t)m * E;
     uint32_t keys[NK];
+#pragma unroll
+    for (int i = 0; i < NK; ++i) keys[i] = 0u;
     unsigned long long sv = 0;
     // poll until every key of this row (and its shared logit) has arrived
-    for (int it = 0;; ++it) {
+    bool arrived = false;
+    for (int it = 0; it < p.wait_limit; ++it) {
 #pragma unroll
       for (int i = 0; i < NK; ++i) keys[i] = ld_agent(kr + min(lane + kWave * i, E - 1));
       if (p.has_shared) sv = ld_agent(p.shared_logit + m);
       bool missing = p.has_shared && (sv >> 32) == 0;
 #pragma unroll
       for (int i = 0; i < NK; ++i) missing |= (lane + kWave * i < E) && keys[i] == 0u;
-      if (__builtin_amdgcn_ballot_w64(missing) == 0) break;
-      if (it == kPollSpin) {
-        if (lane == 0) st_agent(p.ctr + kCtrError, 1u);
+      if (__builtin_amdgcn_ballot_w64(missing) == 0) {
+        arrived = true;
         break;
       }
     }
+    if (!arrived) wait_failed(p, kWaitKeys, failed, lane);
     // consume: mask lanes past E, re-zero the slots for the next launch
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
@@ -134,7 +149,8 @@ __device__ void route_tail_rows1(const SmallParams &p, int32_t *lds_ids, uint32_
       p.ids[(size_t)m * S + lane] = id;
       p.wts[(size_t)m * S + lane] = w;
       if (hand_off) {
-        st_agent(p.hids + (size_t)m * S + lane, (uint32_t)id + 1u);  // for block 0's align
+        // for block 0's align
+        st_agent(p.hids + (size_t)m * S + lane, arrived ? (uint32_t)id + 1u : kFailedHandOff);
       } else {
         lds_ids[m * S + lane] = id;
         if (p.do_align) mark_pair(p, id, m, rowbm, touched);
@@ -147,13 +163,18 @@ __device__ void route_tail_rows1(const SmallParams &p, int32_t *lds_ids, uint32_
 // 4 + w, 8 + w, ... (< M) that tail blocks 1.. wrote as id + 1 with
 // write-through stores, polling until every slot is non-zero (bounded, as
 // the key poll), then puts them in lds_ids, marks the align bitmaps and
-// re-zeroes the slots for the next launch.
-__device__ void gather_tail_ids(const SmallParams &p, int32_t *lds_ids, uint32_t *rowbm, uint32_t *touched) {
+// re-zeroes the slots for the next launch.  A slot holding kFailedHandOff
+// (that block's key wait gave up) raises the block's failed flag.
+__device__ void gather_tail_ids(const SmallParams &p, int32_t *lds_ids, uint32_t *rowbm, uint32_t *touched,
+                                uint32_t *failed) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int S = p.S;
   constexpr int kRows = kSmallMaxTokens / (kThreads / kWave) - 1;  // rows 4 + w + 4 r
   uint32_t v[kRows];
-  for (int it = 0;; ++it) {
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) v[r] = 0u;
+  bool arrived = false;
+  for (int it = 0; it < p.wait_limit; ++it) {
 #pragma unroll
     for (int r = 0; r < kRows; ++r) {
       const int m = min(4 + wave + 4 * r, p.M - 1);  // branch-free: rows past M reload row M - 1
@@ -162,22 +183,25 @@ __device__ void gather_tail_ids(const SmallParams &p, int32_t *lds_ids, uint32_t
     bool missing = false;
 #pragma unroll
     for (int r = 0; r < kRows; ++r) missing |= (4 + wave + 4 * r < p.M) && lane < S && v[r] == 0u;
-    if (__builtin_amdgcn_ballot_w64(missing) == 0) break;
-    if (it == kPollSpin) {
-      if (lane == 0) st_agent(p.ctr + kCtrError, 1u);
+    if (__builtin_amdgcn_ballot_w64(missing) == 0) {
+      arrived = true;
       break;
     }
   }
+  if (!arrived) wait_failed(p, kWaitIds, failed, lane);
+  bool marker = false;
 #pragma unroll
   for (int r = 0; r < kRows; ++r) {
     const int m = 4 + wave + 4 * r;
     if (m < p.M && lane < S) {
-      const int32_t id = (int32_t)v[r] - 1;
+      marker |= v[r] == kFailedHandOff;
+      const int32_t id = (int32_t)v[r] - 1;  // kFailedHandOff and 0 give ids < 0: skipped
       lds_ids[m * S + lane] = id;
       mark_pair(p, id, m, rowbm, touched);
       st_agent(p.hids + (size_t)m * S + lane, 0u);
     }
   }
+  if (__builtin_amdgcn_ballot_w64(marker) != 0 && lane == 0) *failed = 1u;
 }
 
 // Tail, part 2: align of the n = M*S pairs in lds_ids.  Here M <= A,
@@ -193,7 +217,7 @@ __device__ void gather_tail_ids(const SmallParams &p, int32_t *lds_ids, uint32_t
 // thread of the block calls this after the block barrier that follows the
 // tail's marks.
 __device__ void align_small(const SmallParams &p, const int32_t *lds_ids, const uint32_t *rowbm,
-                            const uint32_t *touched) {
+                            const uint32_t *touched, const uint32_t *failed) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = p.M * p.S, Ep = p.Ep, sh = p.log2A;
   const int words = (Ep + 31) >> 5;  // <= 33 for E' <= 1025: one wave scan covers them
@@ -201,7 +225,8 @@ __device__ void align_small(const SmallParams &p, const int32_t *lds_ids, const 
   const uint32_t pc = lane < words ? __builtin_popcount(touched[lane]) : 0u;
   const uint32_t incl = wave_incl_scan_u32(pc, lane);
   const uint32_t excl = incl - pc;  // touched experts in the words before lane's
-  if (tid == 0) *p.npp = (int32_t)(__builtin_amdgcn_readlane(incl, 63) << sh);
+  // npp = -1 marks a launch one of whose waits gave up
+  if (tid == 0) *p.npp = *failed ? -1 : (int32_t)(__builtin_amdgcn_readlane(incl, 63) << sh);
   for (int i0 = wave * kWave; i0 < n; i0 += kThreads) {  // wave-uniform trip count: every lane active
     const int i = i0 + lane;
     const int e = lds_ids[min(i, n - 1)];
@@ -284,10 +309,12 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
   // gate's block barrier orders these stores before the tail's marks)
   __shared__ uint32_t rowbm[kWave * NK + 1];  // E' <= 64 NK + 1
   __shared__ uint32_t touched[kMaxRouteExperts / 32 + 1];
+  __shared__ uint32_t failed;  // a wait of this block gave up
   if (blockIdx.x == 0 && p.do_align && !p.logits_only) {
     for (int e = tid; e < p.Ep; e += kThreads) rowbm[e] = 0u;
     for (int w = tid; w < ((p.Ep + 31) >> 5); w += kThreads) touched[w] = 0u;
   }
+  if (tid == 0) failed = 0u;
 
   // ---- sentinel pre-fill of this block's slice of sorted_token_ids ------
   if (p.do_align) {
@@ -429,21 +456,21 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
     if ((int)blockIdx.x >= (M + 3) / 4) return;
     __shared__ int32_t lds_ids[MAXM * (kMaxTopK + 1)];
     const int m0 = 4 * blockIdx.x;
-    route_tail_rows1<NK>(p, lds_ids, rowbm, touched, m0, min(M, m0 + 4), blockIdx.x != 0 && p.do_align);
+    route_tail_rows1<NK>(p, lds_ids, rowbm, touched, m0, min(M, m0 + 4), blockIdx.x != 0 && p.do_align, &failed);
     if (blockIdx.x != 0 || !p.do_align) return;
-    gather_tail_ids(p, lds_ids, rowbm, touched);
+    gather_tail_ids(p, lds_ids, rowbm, touched, &failed);
     __syncthreads();  // every pair is marked and in lds_ids
-    align_small(p, lds_ids, rowbm, touched);
+    align_small(p, lds_ids, rowbm, touched, &failed);
     return;
   }
   if (blockIdx.x != 0) return;
 
   // ---- block 0: the tail ---------------------------------------------------
   __shared__ int32_t lds_ids[MAXM * (kMaxTopK + 1)];
-  route_tail_rows1<NK>(p, lds_ids, rowbm, touched, 0, p.M, false);
+  route_tail_rows1<NK>(p, lds_ids, rowbm, touched, 0, p.M, false, &failed);
   if (p.do_align) {
     __syncthreads();  // every pair is marked and in lds_ids
-    align_small(p, lds_ids, rowbm, touched);
+    align_small(p, lds_ids, rowbm, touched, &failed);
   }
 }
 

@@ -102,6 +102,32 @@ def check_ids_random(ids_gpu, ref, k):
     return int(exempt.sum())
 
 
+# Bounds on how many rows leave the direct comparisons on random inputs (the
+# backstop still covers every row).  Exempt rows depend on the seeded input
+# alone; measured with the oracle over this suite's random cases: 5.5%
+# (skewed E = 128 prefill) to 26% (E = 512, k = 10) of rows at M >= 50, 42%
+# at E = 1024, k = 32, and 4 of 7 rows at that shape with M = 7.  Among
+# exempt rows the kernel's fp32 sums pick a different expert set only when
+# two logits sit within fp32 error (about 2^-18 relative) of each other
+# across a bf16 rounding boundary: rare.  Rounding-excluded rows: a chosen
+# logit within fp32 error of a bf16 midpoint (ulp 2^-8 relative) is roughly
+# a 2^-9 event per logit.
+MAX_EXEMPT_FRAC = 0.6
+MAX_FLIPPED_FRAC = 0.01
+MAX_ROUNDING_EXCLUDED_FRAC = 0.05
+
+
+def check_exemptions(M, exempt, flipped, excluded):
+    """Prints and bounds the rows left out of the direct id comparison
+    (exempt), the exempt rows whose chosen set differs from the oracle's
+    (flipped), and the rows left out of the direct weight comparison
+    (rounding-excluded)."""
+    print(f"[rows] M={M} exempt={exempt} flipped={flipped} rounding_excluded={excluded}", flush=True)
+    assert exempt <= max(4, MAX_EXEMPT_FRAC * M), (exempt, M)
+    assert flipped <= max(2, MAX_FLIPPED_FRAC * M), (flipped, M)
+    assert excluded <= max(2, MAX_ROUNDING_EXCLUDED_FRAC * M), (excluded, M)
+
+
 def check_align(ids_gpu, num_experts, A, srt_gpu, eids_gpu, npp_gpu):
     srt, eids, npp = oracle.align(ids_gpu, num_experts, A)
     assert int(npp_gpu) == npp, (int(npp_gpu), npp)

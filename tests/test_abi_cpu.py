@@ -182,3 +182,35 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(mr._binding, "_LIB_PATH", str(tmp_path / "libmoeroute.so"))
     with pytest.raises(mr.MoeRouteError, match="is missing"):
         mr.mr_abi_version()
+
+
+def test_status_refusals(lib):
+    """mr_workspace_status refuses, listing every reason, before any launch."""
+    rc = lib.mr_workspace_status(None, 0, None, None)
+    assert rc == mr.MR_EINVAL
+    msg = _err(lib)
+    for needle in ["ws is NULL", "ws_bytes=0", "status is NULL"]:
+        assert needle in msg, (needle, msg)
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: refused before launch
+    rc = lib.mr_workspace_status(ctypes.c_void_p((1 << 20) + 16), 1 << 20, ctypes.c_void_p((1 << 20) + 2), None)
+    assert rc == mr.MR_EUNSUPPORTED
+    msg = _err(lib)
+    assert "ws is not 256-byte aligned" in msg and "status is not 4-byte aligned" in msg, msg
+    rc = lib.mr_workspace_status(fake, 64, fake, None)
+    assert rc == mr.MR_ECAPACITY and "ws_bytes=64 <" in _err(lib)
+
+
+def test_workspace_must_be_256_byte_aligned(lib):
+    """The prefill launch's partial rows start on 128-byte lines only when
+    the workspace base is 256-byte aligned."""
+    fake = ctypes.c_void_p(1 << 20)
+    ws = ctypes.c_void_p((1 << 20) + 128)
+    rc = lib.mr_route_align(fake, fake, None, 4, 64, 16, 4, 1.0, 64, fake, fake, fake, 1 << 20, fake, 1 << 20,
+                            fake, ws, 1 << 30, None)
+    assert rc == mr.MR_EUNSUPPORTED and "ws is not 256-byte aligned" in _err(lib), _err(lib)
+
+
+def test_wait_limit_hook(lib):
+    for v in (0, 5, -3, -1):
+        assert lib.mr_debug_set_wait_limit(v) == mr.MR_OK
+    assert mr.MR_STATUS_KEY_WAIT | mr.MR_STATUS_ID_WAIT | mr.MR_STATUS_GRID_WAIT | mr.MR_STATUS_TILE_WAIT == 15

@@ -5,7 +5,8 @@ import pytest
 
 import oracle
 from moe_token_routing_amd import workloads
-from parity_util import check_align, check_backstop, check_ids_random, check_weights, same_rounding_rows
+from parity_util import (check_align, check_backstop, check_exemptions, check_ids_random, check_weights,
+                         same_rounding_rows)
 from gpu_util import lane_heavy_inputs, logits_gpu, route_align_gpu, to_dev
 
 pytestmark = pytest.mark.gpu
@@ -41,8 +42,10 @@ def _run_and_check(d, k, scale, A=None, exact=False):
     else:
         exempt = check_ids_random(g["topk_ids"], ref, k)
         rows = same_rounding_rows(lg, ref, g["topk_ids"], k)
-        same = [m for m in rows if sorted(g["topk_ids"][m].tolist()) == sorted(ref["ids"][m].tolist())]
+        same_set = [sorted(g["topk_ids"][m].tolist()) == sorted(ref["ids"][m].tolist()) for m in range(M)]
+        same = [m for m in rows if same_set[m]]
         check_weights(g["topk_weights"], g["topk_ids"], ref["weights"], ref["ids"], same)
+        check_exemptions(M, exempt, M - sum(same_set), M - len(rows))
     check_align(g["topk_ids"], E + has_shared, A, g["sorted_token_ids"], g["expert_ids"], g["npp"][0])
     return exempt
 
