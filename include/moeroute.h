@@ -92,6 +92,15 @@ extern "C" {
 /* ABI version of the loaded library (MR_ABI_VERSION). */
 int mr_abi_version(void);
 
+/* Optional per-device set-up, for the CURRENT device: sets the prefill
+ * kernel's dynamic-LDS limit and caches how many of its blocks fit on the
+ * device at once.  The route entry points do the same on their first call on
+ * a device; call this once per device before capturing launches into a HIP
+ * graph, so that no runtime query runs during capture.  Idempotent.  Returns
+ * MR_OK; MR_ELAUNCH if there is no current device or a runtime query fails;
+ * MR_EUNSUPPORTED for a device ordinal >= 64. */
+int mr_init(void);
+
 /* Every failed check of the last refused call on this thread, or "". */
 const char *mr_last_error(void);
 

@@ -32,6 +32,7 @@ _SZ = ctypes.c_size_t
 _F32 = ctypes.c_float
 SIGNATURES = {
     "mr_abi_version": (ctypes.c_int, []),
+    "mr_init": (ctypes.c_int, []),
     "mr_last_error": (ctypes.c_char_p, []),
     "mr_select_alignment": (_I32, [_I32, _I32, _I32]),
     "mr_align_capacity": (_I64, [_I32, _I32, _I32, _I32]),
@@ -163,6 +164,15 @@ def _gate_inputs(x, gate_w, shared_w):
 
 def mr_abi_version() -> int:
     return int(lib().mr_abi_version())
+
+
+def mr_init(device=None) -> None:
+    """Per-device set-up (see include/moeroute.h) on `device` (default: the
+    current one)."""
+    import torch
+
+    with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
+        _check(lib().mr_init())
 
 
 def mr_last_error() -> str:

@@ -329,6 +329,25 @@ extern "C" {
 
 int mr_abi_version(void) { return MR_ABI_VERSION; }
 
+int mr_init(void) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    g_last_error = std::string("mr_init: no current device: ") + hipGetErrorString(e);
+    return MR_ELAUNCH;
+  }
+  if (dev < 0 || dev >= mr::kMaxDevices) {
+    g_last_error = "mr_init: device ordinal " + std::to_string(dev) + " >= " + std::to_string(mr::kMaxDevices);
+    return MR_EUNSUPPORTED;
+  }
+  if (!mr::mfma_prepare(dev)) {
+    g_last_error = "mr_init: setting up the prefill kernel on device " + std::to_string(dev) + " failed";
+    return MR_ELAUNCH;
+  }
+  g_last_error.clear();
+  return MR_OK;
+}
+
 const char *mr_last_error(void) { return g_last_error.c_str(); }
 
 int32_t mr_select_alignment(int32_t M, int32_t k, int32_t E) {

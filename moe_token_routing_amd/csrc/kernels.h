@@ -140,8 +140,14 @@ struct MfmaParams {
   int logits_only;
   int wait_limit;     // polls a wait makes before it gives up (0: gives up at once)
 };
+constexpr int kMaxDevices = 64;  // per-device set-up is kept for device ordinals below this
 size_t mfma_lds_bytes();
+// Blocks of the prefill launch for E routed experts that fit on the current
+// device at once (0 if a runtime query failed); the first call on a device
+// also sets the kernel's dynamic-LDS limit there.
 int mfma_capacity(int E);
+// Does that set-up for every instantiation on device dev (current).
+bool mfma_prepare(int dev);
 hipError_t launch_route_mfma(const MfmaParams &p, hipStream_t stream);
 
 

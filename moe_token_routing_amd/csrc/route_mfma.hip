@@ -54,6 +54,8 @@
 // launch clears the other set and block 0 advances the count at the end);
 // the tile counters (one word per expert and 128-token tile) are cleared
 // during phase G.
+#include <atomic>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -938,13 +940,14 @@ int mfma_nkp(int E) {
   return need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
 }
 
-int mfma_capacity(int E) {
-  static int cached[4][64];  // [nkp index][device]
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  const int nkp = mfma_nkp(E);
-  const int ki = nkp == 1 ? 0 : nkp == 2 ? 1 : nkp == 4 ? 2 : 3;
-  if (cached[ki][dev] > 0) return cached[ki][dev];
+namespace {
+std::atomic<int> g_capacity[4][kMaxDevices];  // [nkp index][device]: resident blocks, 0 = not yet known
+}  // namespace
+
+// Sets the dynamic-LDS limit of the instantiation for nkp index ki on the
+// current device and caches how many of its blocks fit on the device at
+// once.  Returns that number, or 0 if a runtime query failed.
+static int mfma_setup(int ki, int dev) {
   const void *fn = ki == 0 ? kernel_ptr<1>() : ki == 1 ? kernel_ptr<2>() : ki == 2 ? kernel_ptr<4>() : kernel_ptr<8>();
   if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)mfma_lds_bytes()) != hipSuccess)
     return 0;
@@ -952,8 +955,24 @@ int mfma_capacity(int E) {
   if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, mfma_lds_bytes()) != hipSuccess) return 0;
   const int cap = ncu * per_cu;
-  cached[ki][dev] = cap;
+  g_capacity[ki][dev].store(cap, std::memory_order_relaxed);
   return cap;
+}
+
+int mfma_capacity(int E) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  const int nkp = mfma_nkp(E);
+  const int ki = nkp == 1 ? 0 : nkp == 2 ? 1 : nkp == 4 ? 2 : 3;
+  const int cap = g_capacity[ki][dev].load(std::memory_order_relaxed);
+  return cap > 0 ? cap : mfma_setup(ki, dev);
+}
+
+bool mfma_prepare(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return false;
+  for (int ki = 0; ki < 4; ++ki)
+    if (mfma_setup(ki, dev) < 1) return false;
+  return true;
 }
 
 hipError_t launch_route_mfma(const MfmaParams &p, hipStream_t stream) {

@@ -224,3 +224,56 @@ def test_large_debug_logits_exact():
     lg = logits_gpu(d)
     assert np.array_equal(lg[:, :512].astype(np.float64), z)
     assert np.array_equal(lg[:, 512].astype(np.float64), s)
+
+
+_FIRST_CALL_IN_CAPTURE = r"""
+import sys, torch
+sys.path.insert(0, {root!r})
+import moe_token_routing_amd as mr
+from moe_token_routing_amd import workloads
+from gpu_util import to_dev
+if {init}:
+    mr.mr_init()
+d = workloads.make_inputs(512, 512, 4096, True, "int", seed=31)
+x, w, s = to_dev(d["x"]), to_dev(d["w"]), to_dev(d["ws"])
+ws = mr.new_workspace(512, 512, 10, True)
+A = mr.mr_select_alignment(512, 10, 512)
+ids = torch.empty(512, 11, dtype=torch.int32, device="cuda")
+wts = torch.empty(512, 11, dtype=torch.float32, device="cuda")
+cap = mr.mr_align_capacity(512, 11, 513, A)
+srt = torch.empty(cap, dtype=torch.int32, device="cuda")
+eids = torch.empty(cap // A, dtype=torch.int32, device="cuda")
+npp = torch.empty(1, dtype=torch.int32, device="cuda")
+torch.cuda.synchronize()
+g = torch.cuda.CUDAGraph()
+with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+    mr.mr_route_align(x, w, s, 10, 1.0, A, workspace=ws, topk_ids=ids, topk_weights=wts,
+                      sorted_token_ids=srt, expert_ids=eids, npp=npp)
+ref = mr.mr_route_align(x, w, s, 10, 1.0, A, workspace=ws)
+torch.cuda.synchronize()
+n = int(ref["npp"].item())
+for rep in range(3):
+    ids.fill_(-1); npp.fill_(-1)
+    g.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ref["topk_ids"]) and int(npp.item()) == n, rep
+    assert torch.equal(srt[:n], ref["sorted_token_ids"][:n])
+print("first call in capture ok", {init})
+"""
+
+
+@pytest.mark.parametrize("init", [True, False])
+def test_first_prefill_call_inside_graph_capture(init):
+    """A fresh process whose very first prefill call is made inside graph
+    capture (its one-time set-up queries then run during capture), after
+    mr_init and without it; the replays must equal an eager launch."""
+    import os
+    import subprocess
+    import sys
+
+    _say("first call in capture, init", init)
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = _FIRST_CALL_IN_CAPTURE.format(root=root, init=init)
+    env = dict(os.environ, PYTHONPATH=os.path.join(root, "tests") + os.pathsep + root)
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=240, env=env)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-4000:]
