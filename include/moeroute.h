@@ -96,7 +96,9 @@ int mr_abi_version(void);
  * kernel's dynamic-LDS limit and caches how many of its blocks fit on the
  * device at once.  The route entry points do the same on their first call on
  * a device; call this once per device before capturing launches into a HIP
- * graph, so that no runtime query runs during capture.  Idempotent.  Returns
+ * graph, so that no runtime query runs during capture.  It also looks up
+ * the device address of mr_route_align_noalloc's static scratch array on
+ * this device.  Idempotent.  Returns
  * MR_OK; MR_ELAUNCH if there is no current device or a runtime query fails;
  * MR_EUNSUPPORTED for a device ordinal >= 64. */
 int mr_init(void);
@@ -215,6 +217,31 @@ int mr_route_align(const void *x, const void *gate_w, const void *shared_w,
                    int32_t *sorted_token_ids, int64_t sorted_cap,
                    int32_t *expert_ids, int64_t expert_cap, int32_t *npp,
                    void *ws, size_t ws_bytes, void *stream);
+
+/* mr_route_align for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments minus the workspace, the same kernels and results.
+ * Its workspace is a static device array of 32 MiB per GPU, part of the
+ * library's code object (held on each GPU the library runs on until the
+ * process ends); its address is looked up once per device, by mr_init or by
+ * this call's first use on a device.  No call allocates or frees anything.
+ * Each call first clears the array's counter and hand-off regions with a
+ * small fill kernel on `stream`, so a call never depends on an earlier one,
+ * even one whose waits gave up (such a call still writes *npp = -1; its
+ * status word is cleared by the next call and cannot be read).  Every call
+ * on one GPU shares that GPU's array: calls that may overlap in time on one
+ * GPU (different streams, or graphs replayed concurrently) race and give
+ * undefined results -- use mr_route_align with one workspace per stream
+ * there.  Returns what mr_route_align returns, and MR_ECAPACITY (before
+ * touching the device) when mr_workspace_bytes(M, E, k, shared) exceeds the
+ * 32 MiB (about M <= 15000 at E = 512, k = 10); MR_ELAUNCH if the address
+ * look-up fails. */
+int mr_route_align_noalloc(const void *x, const void *gate_w, const void *shared_w,
+                           int32_t M, int32_t H, int32_t E, int32_t k, float scale,
+                           int32_t A, int32_t *topk_ids, float *topk_weights,
+                           int32_t *sorted_token_ids, int64_t sorted_cap,
+                           int32_t *expert_ids, int64_t expert_cap, int32_t *npp,
+                           void *stream);
 
 /* Test hook, not part of the routing API: writes the fp32 gate logits the
  * route kernels compute for these inputs -- logits [M, E + has_shared]

@@ -47,6 +47,8 @@ SIGNATURES = {
                                       _P]),
     "mr_route_align": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _F32, _I32, _P, _P, _P, _I64,
                                       _P, _I64, _P, _P, _SZ, _P]),
+    "mr_route_align_noalloc": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _F32, _I32, _P, _P, _P, _I64,
+                                              _P, _I64, _P, _P]),
     "mr_debug_gate_logits": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _P, _P, _SZ, _P]),
     "mr_debug_stream_read": (ctypes.c_int, [_P, _SZ, _P, _P]),
     "mr_argmax_workspace_bytes": (_SZ, [_I32, _I64]),
@@ -339,6 +341,32 @@ def mr_route_align(x, gate_w, shared_w, k: int, scale: float = 1.0, A: int | Non
                                 _ptr(topk_ids), _ptr(topk_weights), _ptr(sorted_token_ids),
                                 sorted_token_ids.numel(), _ptr(expert_ids), expert_ids.numel(), _ptr(npp),
                                 _ptr(workspace), nbytes, _stream(stream, dev)))
+    return {"topk_ids": topk_ids, "topk_weights": topk_weights, "sorted_token_ids": sorted_token_ids,
+            "expert_ids": expert_ids, "npp": npp, "A": A}
+
+
+def mr_route_align_noalloc(x, gate_w, shared_w, k: int, scale: float = 1.0, A: int | None = None, *,
+                           topk_ids, topk_weights, sorted_token_ids, expert_ids, npp, stream=None):
+    """mr_route_align without a workspace (the library's static per-GPU
+    scratch array) and without allocating: every output buffer is the
+    caller's.  Returns dict(topk_ids, topk_weights, sorted_token_ids,
+    expert_ids, npp, A)."""
+    import torch
+
+    M, H, E, dev = _gate_inputs(x, gate_w, shared_w)
+    sh = shared_w is not None
+    S = k + sh
+    if A is None:
+        A = mr_select_alignment(M, k, E)
+    _out(topk_ids, "topk_ids", torch.int32, dev, numel=M * S)
+    _out(topk_weights, "topk_weights", torch.float32, dev, numel=M * S)
+    _out(sorted_token_ids, "sorted_token_ids", torch.int32, dev)
+    _out(expert_ids, "expert_ids", torch.int32, dev)
+    _out(npp, "npp", torch.int32, dev, min_numel=1)
+    _check(lib().mr_route_align_noalloc(_ptr(x), _ptr(gate_w), _ptr(shared_w), M, H, E, k, float(scale), A,
+                                        _ptr(topk_ids), _ptr(topk_weights), _ptr(sorted_token_ids),
+                                        sorted_token_ids.numel(), _ptr(expert_ids), expert_ids.numel(), _ptr(npp),
+                                        _stream(stream, dev)))
     return {"topk_ids": topk_ids, "topk_weights": topk_weights, "sorted_token_ids": sorted_token_ids,
             "expert_ids": expert_ids, "npp": npp, "A": A}
 

@@ -344,6 +344,11 @@ int mr_init(void) {
     g_last_error = "mr_init: setting up the prefill kernel on device " + std::to_string(dev) + " failed";
     return MR_ELAUNCH;
   }
+  const hipError_t se = mr::scratch_setup(dev);
+  if (se != hipSuccess) {
+    g_last_error = std::string("mr_init: looking up the static scratch array failed: ") + hipGetErrorString(se);
+    return MR_ELAUNCH;
+  }
   g_last_error.clear();
   return MR_OK;
 }
@@ -413,6 +418,44 @@ int mr_route_align(const void *x, const void *gate_w, const void *shared_w, int3
                    int32_t *npp, void *ws, size_t ws_bytes, void *stream) {
   return route_impl("mr_route_align", x, gate_w, shared_w, M, H, E, k, scale, A, topk_ids, topk_weights,
                     sorted_token_ids, sorted_cap, expert_ids, expert_cap, npp, nullptr, ws, ws_bytes, stream, true);
+}
+
+int mr_route_align_noalloc(const void *x, const void *gate_w, const void *shared_w, int32_t M, int32_t H,
+                           int32_t E, int32_t k, float scale, int32_t A, int32_t *topk_ids, float *topk_weights,
+                           int32_t *sorted_token_ids, int64_t sorted_cap, int32_t *expert_ids, int64_t expert_cap,
+                           int32_t *npp, void *stream) {
+  static const char *fn = "mr_route_align_noalloc";
+  // Sizes first, from the arguments alone (no device call): the call's
+  // workspace must fit the static array.
+  if (M >= 0 && E >= 1 && k >= 1 && M <= MR_MAX_TOKENS && E <= mr::kMaxRouteExperts && k <= mr::kMaxTopK) {
+    const size_t need = layout_for(M, E, k, shared_w ? 1 : 0).total;
+    if (need > mr::kScratchBytes) {
+      g_last_error = std::string(fn) + ": M=" + std::to_string(M) + ", E=" + std::to_string(E) + ", k=" +
+                     std::to_string(k) + " needs " + std::to_string(need) + " bytes of workspace, more than the " +
+                     std::to_string(mr::kScratchBytes) + "-byte static scratch array (use mr_route_align)";
+      return MR_ECAPACITY;
+    }
+  }
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess && (dev < 0 || dev >= mr::kMaxDevices)) e = hipErrorInvalidDevice;
+  if (e == hipSuccess) e = mr::scratch_setup(dev);  // once per device, unless mr_init did it
+  if (e != hipSuccess) {
+    g_last_error = std::string(fn) + ": static scratch set-up failed: " + hipGetErrorString(e);
+    return MR_ELAUNCH;
+  }
+  char *ws = static_cast<char *>(mr::scratch_ptr(dev));
+  // The array keeps the last call's contents.  The route launches leave
+  // their zero-between-launches regions (counters, keys, hand-off rows) at
+  // zero, but a launch whose waits gave up does not: clear them.
+  if (M > 0 && E >= 1 && k >= 1) {
+    const Layout L = layout_for(M, E, k, shared_w ? 1 : 0);
+    const hipError_t ze = mr::launch_zero_words(reinterpret_cast<uint32_t *>(ws), L.counts / 4,
+                                                reinterpret_cast<hipStream_t>(stream));
+    if (ze != hipSuccess) return launch_result(ze, fn);
+  }
+  return route_impl(fn, x, gate_w, shared_w, M, H, E, k, scale, A, topk_ids, topk_weights, sorted_token_ids,
+                    sorted_cap, expert_ids, expert_cap, npp, nullptr, ws, mr::kScratchBytes, stream, true);
 }
 
 int mr_debug_gate_logits(const void *x, const void *gate_w, const void *shared_w, int32_t M, int32_t H,

@@ -163,4 +163,12 @@ hipError_t launch_store_zero(int32_t *p, hipStream_t stream);
 // *out = the status word (a coherent read), on the stream.
 hipError_t launch_read_status(const uint32_t *ctr, int32_t *out, hipStream_t stream);
 
+// The workspace of the entry point that allocates nothing: a static device
+// array of kScratchBytes per GPU (static_scratch.hip).  scratch_setup looks
+// up its device address on device dev (which must be current) once;
+// scratch_ptr returns it (null before the set-up).
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+hipError_t scratch_setup(int dev);
+void *scratch_ptr(int dev);
+
 }  // namespace mr
