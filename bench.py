@@ -652,7 +652,54 @@ def measure(wl, steps, warmup, A=None):
     timing = "HIP graph of launches over rotated inputs; HIP events on the launch stream"
     result = result_fields(wl, A, ms_per_step, sum(npps) / len(npps), npps, steps, warmup, timing)
     result["config"].update({"rotation_copies": R, "rotation_bytes": R * per_copy})
+    if wl.M > 32:
+        result["phases"] = prefill_phases(wl, capture, R)
     return d, result
+
+
+def prefill_phases(wl, capture, R):
+    """Per-phase times of one prefill launch in the steady state: a graph of
+    the same R rotated launches is captured with phase stamps on (every launch
+    overwrites them) and replayed once; the stamps of its last launch give,
+    from the first block's start, when the last block finished each phase.
+    The gate pass is every block's gate items done, partial tiles stored;
+    its rate is the launch's flops over that time."""
+    import torch
+
+    import moe_token_routing_amd as mr
+
+    stamps = torch.zeros(8 * 256, dtype=torch.int64, device="cuda:0")
+    mr.mr_debug_set_phase_stamps(stamps)
+    try:
+        g = capture(R)
+    finally:
+        mr.mr_debug_set_phase_stamps(None)
+    g.replay()
+    torch.cuda.synchronize()
+    st = stamps.view(256, 8).cpu().numpy()
+    st = st[st[:, 0] != 0]
+    t0 = st[:, 0].min()
+    tick_us = 0.01  # s_memrealtime counts at 100 MHz
+
+    def col(i):  # blocks that reached point i (a block with no gate item never stamps 1)
+        c = st[:, i]
+        return c[c != 0]
+
+    def last(i):
+        return round(float((col(i).max() - t0) * tick_us), 3)
+
+    def median(i):
+        c = sorted(col(i))
+        return round(float((c[len(c) // 2] - t0) * tick_us), 3)
+
+    flops = 2.0 * wl.M * (wl.E + int(wl.shared)) * wl.H
+    gate_us = last(2)
+    return {"blocks": int(len(st)), "unit": "us from the first block's start (last block / median block)",
+            "gate_mfma_loop_done": [last(1), median(1)], "gate_done": [last(2), median(2)],
+            "topk_start": [last(3), median(3)], "topk_done": [last(4), median(4)],
+            "align_start": [last(5), median(5)], "end": [last(6), median(6)],
+            "gate_pass": {"us": gate_us, "tflops": round(flops / (gate_us * 1e-6) / 1e12, 2),
+                          "frac_of_bf16_peak": round(flops / (gate_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}}
 
 
 def main():
@@ -709,7 +756,8 @@ def main():
     result = {"metric": METRIC, **result}
     if args.secondary_steps > 0 and args.workload == "m4" and args.method == "rotate" and args.align is None:
         _, sec = measure(workload("m2048"), args.secondary_steps, min(args.warmup, 256))
-        result["secondary"] = {kk: sec[kk] for kk in ["value", "unit", "ms_per_step", "steps", "config", "roofline"]}
+        result["secondary"] = {kk: sec[kk] for kk in ["value", "unit", "ms_per_step", "steps", "config", "roofline",
+                                                      "phases"]}
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(d, wl, args.cpu_seconds, args.cpu_threads, args.align)
     print(json.dumps(result), flush=True)

@@ -41,6 +41,7 @@ SIGNATURES = {
     "mr_workspace_reset": (ctypes.c_int, [_P, _SZ, _P]),
     "mr_workspace_status": (ctypes.c_int, [_P, _SZ, _P, _P]),
     "mr_debug_set_wait_limit": (ctypes.c_int, [_I32]),
+    "mr_debug_set_phase_stamps": (ctypes.c_int, [_P, _SZ]),
     "mr_route": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _F32, _P, _P, _P, _SZ, _P]),
     "mr_align": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _P, _I64, _P, _I64, _P, _P, _SZ, _P]),
     "mr_align_local": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _I32, _I32, _P, _I64, _P, _I64, _P, _P, _SZ,
@@ -231,6 +232,20 @@ def mr_debug_set_wait_limit(polls: int) -> None:
     """Test hook: polls every bounded wait of later launches makes before
     giving up (0: at once; negative: the kernels' own bounds)."""
     _check(lib().mr_debug_set_wait_limit(int(polls)))
+
+
+def mr_debug_set_phase_stamps(stamps=None) -> None:
+    """Measurement hook: later prefill launches record per-block phase
+    times (100 MHz clock) into `stamps`, an int64 device tensor of at least
+    8 * 256 elements; None turns it off."""
+    import torch
+
+    if stamps is None:
+        _check(lib().mr_debug_set_phase_stamps(None, 0))
+        return
+    _out(stamps, "stamps", torch.int64, stamps.device)
+    _on(stamps, "stamps", stamps.device)
+    _check(lib().mr_debug_set_phase_stamps(_ptr(stamps), stamps.numel()))
 
 
 def mr_route(x, gate_w, shared_w, k: int, scale: float = 1.0, *, workspace,

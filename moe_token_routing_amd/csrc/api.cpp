@@ -35,6 +35,10 @@ thread_local std::string g_last_error;
 // Polls a bounded wait may make before giving up: < 0 keeps each kernel's
 // own bound (mr_debug_set_wait_limit).
 std::atomic<int> g_wait_limit{-1};
+
+// Phase-stamp buffer for prefill launches (mr_debug_set_phase_stamps).
+std::atomic<uint64_t *> g_stamps{nullptr};
+std::atomic<size_t> g_stamp_words{0};
 int wait_limit(int fallback) {
   const int v = g_wait_limit.load(std::memory_order_relaxed);
   return v < 0 ? fallback : v;
@@ -282,6 +286,8 @@ int route_impl(const char *fn, const void *x, const void *gate_w, const void *sh
     q.logits_out = logits_out;
     q.logits_only = logits_only ? 1 : 0;
     q.wait_limit = wait_limit(mr::kBarrierSpin);
+    uint64_t *st = g_stamps.load(std::memory_order_relaxed);
+    q.stamps = (st && g_stamp_words.load(std::memory_order_relaxed) >= (size_t)grid * mr::kStamps) ? st : nullptr;
     return launch_result(mr::launch_route_mfma(q, s), fn);
   }
 
@@ -397,6 +403,13 @@ int mr_workspace_status(const void *ws, size_t ws_bytes, int32_t *status, void *
   return launch_result(mr::launch_read_status(static_cast<const uint32_t *>(ws), status,
                                               reinterpret_cast<hipStream_t>(stream)),
                        "mr_workspace_status");
+}
+
+int mr_debug_set_phase_stamps(uint64_t *stamps, size_t n_words) {
+  g_stamps.store(n_words ? stamps : nullptr, std::memory_order_relaxed);
+  g_stamp_words.store(stamps ? n_words : 0, std::memory_order_relaxed);
+  g_last_error.clear();
+  return MR_OK;
 }
 
 int mr_debug_set_wait_limit(int32_t polls) {

@@ -139,7 +139,13 @@ struct MfmaParams {
   float *logits_out;  // logits_only: the caller's [M, Ep] fp32 buffer
   int logits_only;
   int wait_limit;     // polls a wait makes before it gives up (0: gives up at once)
+  uint64_t *stamps;   // null, or [grid, kStamps]: per-block phase times (100 MHz clock)
 };
+// Phase stamps of the prefill launch (per block, thread 0): kernel start,
+// first gate item's MFMA loop done, every gate item done (partial tiles
+// stored), first top-k group ready to start, top-k done, align barrier
+// passed, block end.
+constexpr int kStamps = 8;
 constexpr int kMaxDevices = 64;  // per-device set-up is kept for device ordinals below this
 size_t mfma_lds_bytes();
 // Blocks of the prefill launch for E routed experts that fit on the current

@@ -114,9 +114,14 @@ __device__ __forceinline__ void st_agent2(float *p, float a, float b) {
 }
 
 // 16-byte write-through store (sc1, like st_agent): the partial tiles are
-// read by other blocks after a grid barrier.
+// read by other blocks after a grid barrier.  A store of more than 8 bytes
+// reads its data registers after it issues, and a VALU write to them must
+// wait; the compiler cannot see that this asm is such a store and may write
+// those registers in the very next instruction, so the wait states are
+// part of the asm (the store otherwise writes lanes' later values: seen as
+// a few wrong partial sums).
 __device__ __forceinline__ void st_agent16(float *p, u32x4_coh v) {
-  asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
+  asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" : : "v"(p), "v"(v) : "memory");
 }
 
 // Launches with at most this many gate items store their partial tiles with
@@ -225,9 +230,14 @@ __device__ __forceinline__ void tile_wait(uint32_t *ctr, uint32_t set, int t, ui
   __syncthreads();
 }
 
+// Phase stamp i of this block (thread 0), when the caller asked for stamps.
+__device__ __forceinline__ void stamp(const MfmaParams &p, int i) {
+  if (p.stamps && threadIdx.x == 0) p.stamps[(size_t)blockIdx.x * kStamps + i] = __builtin_amdgcn_s_memrealtime();
+}
+
 // ------------------------------------------------------------- phase G ---
 
-__device__ void gate_item(const MfmaParams &p, uint8_t *smem, int et, int tt, int sp) {
+__device__ void gate_item(const MfmaParams &p, uint8_t *smem, int et, int tt, int sp, bool first) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int M = p.M, H = p.H, E = p.E;
   const int st0 = sp * p.spp;
@@ -348,6 +358,7 @@ __device__ void gate_item(const MfmaParams &p, uint8_t *smem, int et, int tt, in
 
   // partial tile -> LDS [token][expert] -> whole token rows in global memory
   __syncthreads();  // every wave is done with the ring
+  if (first) stamp(p, 1);
   float *tile = reinterpret_cast<float *>(smem);
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -793,6 +804,7 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(MfmaParams p) {
   const int b = blockIdx.x;
   const uint32_t grid = gridDim.x;
   if (threadIdx.x == 0) failed = 0u;
+  stamp(p, 0);
 
   // Barrier counter set of this launch: the parity of the launch count.  The
   // other set was used by the previous launch (which has finished); block 0
@@ -829,7 +841,7 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(MfmaParams p) {
     const int L = it * (int)grid + lmap;
     if (L >= p.items) break;
     const int et = L % p.NE, sp = (L / p.NE) % p.SK, tt = L / (p.NE * p.SK);
-    gate_item(p, smem, et, tt, sp);
+    gate_item(p, smem, et, tt, sp, it == 0);
     if (p.tile_wait) {
       if (clear_tcnt) {
         const int share = (p.tcnt_row + tile_items - 1) / tile_items, q = sp * p.NE + et;
@@ -840,6 +852,7 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(MfmaParams p) {
       tile_arrive(p.ctr, set, tt);
     }
   }
+  stamp(p, 2);
   // phases T and A: block b takes token group lmap (+ grid, ...), so a
   // group's partial rows were written by blocks of its own XCD
   const int gb = lmap;
@@ -881,10 +894,13 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(MfmaParams p) {
   for (int g = gb; g < p.ngroups; g += grid) {
     // with tile waits, a group starts once its own token tile's items are in
     if (p.tile_wait) tile_wait(p.ctr, set, (g * p.tpb) >> 7, (uint32_t)tile_items, p.wait_limit, &failed);
+    if (g == gb) stamp(p, 3);
     topk_group<NKP>(p, own, g, (p.has_shared && g == gb) ? sh_first : nullptr);
   }
+  stamp(p, 4);
   if (align) {
     grid_barrier(p.ctr, set, p.tile_wait ? 1 : 2, grid, p.wait_limit, &failed);
+    stamp(p, 5);
     // A wait of any block that gave up before this barrier has set the
     // status word before arriving here; block 0 reads it now and uses it
     // last, so the load's latency hides under the align.
@@ -924,6 +940,7 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(MfmaParams p) {
   // count already)
   if (b == 0 && threadIdx.x == 0)
     __hip_atomic_fetch_add(p.ctr + kCtrEpoch, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  stamp(p, 6);
 }
 
 template <int NKP>
