@@ -62,29 +62,37 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[g][i] = 0.f;
 
-  // one round = 4 steps of 16 k = 64 k; a step's 16 bytes sit at uint4 index 2 s
-  uint4 a[2][4], x[2][4][NTG];
-  auto load = [&](int buf, int k0) {
+  // one round = 4 steps of 16 k = 64 k; a step's 16 bytes sit at uint4 index
+  // 2 s.  Two register buffers alternate; the loop is unrolled by two so
+  // that each buffer is named at compile time (a buffer picked by a runtime
+  // index would live in scratch memory).
+  uint4 a0[4], x0[4][NTG], a1[4], x1[4][NTG];
+  auto load = [&](uint4 (&a)[4], uint4 (&x)[4][NTG], int k0) {
     const int c0 = k0 >> 3;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      a[buf][s] = wrow[c0 + 2 * s];
+      a[s] = wrow[c0 + 2 * s];
 #pragma unroll
-      for (int g = 0; g < NTG; ++g) x[buf][s][g] = xrow[g][c0 + 2 * s];
+      for (int g = 0; g < NTG; ++g) x[s][g] = xrow[g][c0 + 2 * s];
     }
   };
-  const int rounds = p.H >> 6;
-  load(0, 0);
-  for (int r = 0; r < rounds; ++r) {
-    const int cur = r & 1;
-    if (r + 1 < rounds) load(cur ^ 1, (r + 1) << 6);
+  auto round = [&](const uint4 (&a)[4], const uint4 (&x)[4][NTG]) {
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int g = 0; g < NTG; ++g) {
-        const uint4 xv = valid[g] ? x[cur][s][g] : make_uint4(0u, 0u, 0u, 0u);
-        acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8_g(a[cur][s]), as_bf16x8_g(xv), acc[g], 0, 0, 0);
+        const uint4 xv = valid[g] ? x[s][g] : make_uint4(0u, 0u, 0u, 0u);
+        acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8_g(a[s]), as_bf16x8_g(xv), acc[g], 0, 0, 0);
       }
+  };
+  const int rounds = p.H >> 6;
+  load(a0, x0, 0);
+  for (int r = 0; r < rounds; r += 2) {
+    if (r + 1 < rounds) load(a1, x1, (r + 1) << 6);
+    round(a0, x0);
+    if (r + 1 == rounds) break;
+    if (r + 2 < rounds) load(a0, x0, (r + 2) << 6);
+    round(a1, x1);
   }
   // lane holds slot column lane % 32 of each group and the features
   // n0 + 8 q + 4 (lane / 32) + {0..3} in elements 4q .. 4q + 3
