@@ -654,7 +654,39 @@ def measure(wl, steps, warmup, A=None):
     result["config"].update({"rotation_copies": R, "rotation_bytes": R * per_copy})
     if wl.M > 32:
         result["phases"] = prefill_phases(wl, capture, R)
+    elif wl.M <= 4:
+        result["phases"] = small_phases(capture, R)
     return d, result
+
+
+def small_phases(capture, R):
+    """Phase times of one small-M launch in the steady state (as
+    prefill_phases): when the last and the median block published their gate
+    keys, then block 0's tail for its first token row."""
+    import torch
+
+    import moe_token_routing_amd as mr
+
+    stamps = torch.zeros(8 * 256, dtype=torch.int64, device="cuda:0")
+    mr.mr_debug_set_phase_stamps(stamps)
+    try:
+        g = capture(R)
+    finally:
+        mr.mr_debug_set_phase_stamps(None)
+    g.replay()
+    torch.cuda.synchronize()
+    st = stamps.view(256, 8).cpu().numpy()
+    st = st[st[:, 0] != 0]
+    t0 = st[:, 0].min()
+    us = lambda v: round(float((v - t0) * 0.01), 3)  # noqa: E731  (100 MHz clock)
+    pub = sorted(st[:, 1])
+    tail = st[0] if st[0, 2] != 0 else None
+    out = {"blocks": int(len(st)), "unit": "us from the first block's start",
+           "last_block_start": us(st[:, 0].max()), "keys_published": [us(pub[-1]), us(pub[len(pub) // 2])]}
+    if tail is not None:
+        out.update({"block0_keys_arrived": us(tail[2]), "sorted": us(tail[3]), "selected": us(tail[4]),
+                    "stored": us(tail[5]), "align_done": us(tail[6])})
+    return out
 
 
 def prefill_phases(wl, capture, R):
@@ -757,7 +789,7 @@ def main():
     if args.secondary_steps > 0 and args.workload == "m4" and args.method == "rotate" and args.align is None:
         _, sec = measure(workload("m2048"), args.secondary_steps, min(args.warmup, 256))
         result["secondary"] = {kk: sec[kk] for kk in ["value", "unit", "ms_per_step", "steps", "config", "roofline",
-                                                      "phases"]}
+                                                      "phases"] if kk in sec}
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(d, wl, args.cpu_seconds, args.cpu_threads, args.align)
     print(json.dumps(result), flush=True)

@@ -170,16 +170,18 @@ int mr_workspace_status(const void *ws, size_t ws_bytes, int32_t *status, void *
  * beyond any launch that runs normally).  Always returns MR_OK. */
 int mr_debug_set_wait_limit(int32_t polls);
 
-/* Measurement hook, not part of the routing API: later prefill launches (the
- * launch mr_route / mr_route_align take for M > 32) of this process record,
- * per block b, thread 0's 100 MHz clock (s_memrealtime) at 8 points into
- * stamps[b * 8 + i]: 0 kernel start, 1 the first gate item's MFMA loop done,
- * 2 every gate item done (partial tiles stored), 3 the first top-k group
- * ready to start, 4 top-k done, 5 the align's grid barrier passed, 6 block
- * end (7 unused).  stamps: device, n_words >= 8 * (blocks of the launch,
- * at most 256) uint64 words, caller-owned; a launch with more blocks than
- * the buffer holds records nothing.  NULL or n_words = 0 turns it off.
- * Always returns MR_OK. */
+/* Measurement hook, not part of the routing API: later route launches of
+ * this process record, per block b, thread 0's 100 MHz clock (s_memrealtime)
+ * at up to 8 points into stamps[b * 8 + i].  The prefill launch (M > 32):
+ * 0 kernel start, 1 the first gate item's MFMA loop done, 2 every gate item
+ * done (partial tiles stored), 3 the first top-k group ready to start, 4
+ * top-k done, 5 the align's grid barrier passed, 6 block end.  The small-M
+ * launch (blocks b < 256 only): 0 start, 1 gate keys published; block 0,
+ * for its first token row: 2 keys arrived, 3 keys sorted, 4 top-k
+ * selected, 5 slots stored, 6 align done.  stamps: device, n_words >= 8 *
+ * 256 uint64 words, caller-owned; with fewer words the small-M launch
+ * records nothing and the prefill launch records only if its blocks fit.
+ * NULL or n_words = 0 turns it off.  Always returns MR_OK. */
 int mr_debug_set_phase_stamps(uint64_t *stamps, size_t n_words);
 
 /* Route [R], Modifications: gate contraction in fp32, bf16 rounding of the

@@ -312,6 +312,8 @@ int route_impl(const char *fn, const void *x, const void *gate_w, const void *sh
   p.ctr = ctr;
   p.logits_only = logits_only ? 1 : 0;
   p.wait_limit = wait_limit(mr::kPollSpin);
+  uint64_t *st = g_stamps.load(std::memory_order_relaxed);
+  p.stamps = (st && g_stamp_words.load(std::memory_order_relaxed) >= (size_t)256 * mr::kStamps) ? st : nullptr;
   p.do_align = do_align ? 1 : 0;
   p.A = do_align ? A : 64;
   p.log2A = do_align ? log2A : 6;

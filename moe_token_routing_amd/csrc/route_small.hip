@@ -83,6 +83,14 @@ __device__ __forceinline__ void mark_pair(const SmallParams &p, int32_t id, int 
   }
 }
 
+// Phase stamp i of this block (thread 0), when the caller asked for stamps:
+// 0 start, 1 gate keys published; block 0 (its first token row): 2 keys
+// arrived, 3 keys sorted, 4 top-k selected, 5 slots stored, 6 align done.
+__device__ __forceinline__ void stamp(const SmallParams &p, int i) {
+  if (p.stamps && threadIdx.x == 0 && blockIdx.x < 256)
+    p.stamps[(size_t)blockIdx.x * kStamps + i] = __builtin_amdgcn_s_memrealtime();
+}
+
 // A bounded wait that gave up: its bit goes into the status word (agent-scope
 // atomic OR) and the block's LDS flag is raised.
 __device__ __forceinline__ void wait_failed(const SmallParams &p, uint32_t bit, uint32_t *failed, int lane) {
@@ -125,6 +133,7 @@ __device__ void route_tail_rows1(const SmallParams &p, int32_t *lds_ids, uint32_
       }
     }
     if (!arrived) wait_failed(p, kWaitKeys, failed, lane);
+    stamp(p, 2);
     // consume: mask lanes past E, re-zero the slots for the next launch
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
@@ -133,7 +142,9 @@ __device__ void route_tail_rows1(const SmallParams &p, int32_t *lds_ids, uint32_
     }
     if (p.has_shared && lane == 0) st_agent(p.shared_logit + m, 0ull);
     sort_desc_u32(keys);
+    stamp(p, 3);
     const uint32_t mine = topk_sorted_u32(keys, k, lane);  // lane j < k: the j-th chosen key
+    stamp(p, 4);
     const float r = key_value(mine);
     const float r0 = readlane_f32(r, 0);
     const float ex = (lane < k) ? expf(r - r0) : 0.0f;
@@ -156,6 +167,7 @@ __device__ void route_tail_rows1(const SmallParams &p, int32_t *lds_ids, uint32_
         if (p.do_align) mark_pair(p, id, m, rowbm, touched);
       }
     }
+    stamp(p, 5);
   }
 }
 
@@ -315,6 +327,7 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
     for (int w = tid; w < ((p.Ep + 31) >> 5); w += kThreads) touched[w] = 0u;
   }
   if (tid == 0) failed = 0u;
+  stamp(p, 0);
 
   // ---- sentinel pre-fill of this block's slice of sorted_token_ids ------
   if (p.do_align) {
@@ -447,6 +460,7 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
       }
     }
   }
+  stamp(p, 1);
   if (p.logits_only) return;
   if constexpr (MAXM > kThreads / kWave) {
     // M >= 5: the first ceil(M / 4) blocks take four token rows each, one
@@ -461,6 +475,7 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
     gather_tail_ids(p, lds_ids, rowbm, touched, &failed);
     __syncthreads();  // every pair is marked and in lds_ids
     align_small(p, lds_ids, rowbm, touched, &failed);
+    stamp(p, 6);
     return;
   }
   if (blockIdx.x != 0) return;
@@ -472,6 +487,7 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
     __syncthreads();  // every pair is marked and in lds_ids
     align_small(p, lds_ids, rowbm, touched, &failed);
   }
+  stamp(p, 6);
 }
 
 template <int RPB, int MAXM, bool SHARED, int ML = MAXM>
