@@ -176,8 +176,8 @@ int mr_debug_set_wait_limit(int32_t polls);
  * 0 kernel start, 1 the first gate item's MFMA loop done, 2 every gate item
  * done (partial tiles stored), 3 the first top-k group ready to start, 4
  * top-k done, 5 the align's grid barrier passed, 6 block end.  The small-M
- * launch (blocks b < 256 only): 0 start, 1 gate keys published; block 0,
- * for its first token row: 2 keys arrived, 3 keys sorted, 4 top-k
+ * launch (the blocks b < n_words / 8): 0 start, 1 gate keys published;
+ * block 0, for its first token row: 2 keys arrived, 3 keys sorted, 4 top-k
  * selected, 5 slots stored, 6 align done.  stamps: device, n_words >= 8 *
  * 256 uint64 words, caller-owned; with fewer words the small-M launch
  * records nothing and the prefill launch records only if its blocks fit.

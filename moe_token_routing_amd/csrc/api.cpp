@@ -7,6 +7,7 @@
 // ROCm Kernels for AMD MI350X", Compile exact contracts).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdarg>
 #include <cstdint>
@@ -313,7 +314,9 @@ int route_impl(const char *fn, const void *x, const void *gate_w, const void *sh
   p.logits_only = logits_only ? 1 : 0;
   p.wait_limit = wait_limit(mr::kPollSpin);
   uint64_t *st = g_stamps.load(std::memory_order_relaxed);
-  p.stamps = (st && g_stamp_words.load(std::memory_order_relaxed) >= (size_t)256 * mr::kStamps) ? st : nullptr;
+  const size_t words = g_stamp_words.load(std::memory_order_relaxed);
+  p.stamps = (st && words >= (size_t)256 * mr::kStamps) ? st : nullptr;
+  p.stamp_blocks = (int)std::min<size_t>(words / mr::kStamps, (size_t)1 << 20);
   p.do_align = do_align ? 1 : 0;
   p.A = do_align ? A : 64;
   p.log2A = do_align ? log2A : 6;

@@ -72,7 +72,8 @@ struct SmallParams {
   uint32_t *ctr;      // counter words (kCounterBytes)
   int logits_only;
   int wait_limit;     // polls a wait makes before it gives up (0: gives up at once)
-  uint64_t *stamps;   // null, or [256, kStamps]: per-block phase times (100 MHz clock), blocks < 256
+  uint64_t *stamps;   // null, or [stamp_blocks, kStamps]: per-block phase times (100 MHz clock)
+  int stamp_blocks;   // blocks b < stamp_blocks record
   // align
   int do_align, A, log2A;
   uint32_t S_magic;  // ceil(2^32 / S): i / S == umulhi(i, S_magic) for i < 2^32 / S

@@ -87,7 +87,7 @@ __device__ __forceinline__ void mark_pair(const SmallParams &p, int32_t id, int 
 // 0 start, 1 gate keys published; block 0 (its first token row): 2 keys
 // arrived, 3 keys sorted, 4 top-k selected, 5 slots stored, 6 align done.
 __device__ __forceinline__ void stamp(const SmallParams &p, int i) {
-  if (p.stamps && threadIdx.x == 0 && blockIdx.x < 256)
+  if (p.stamps && threadIdx.x == 0 && (int)blockIdx.x < p.stamp_blocks)
     p.stamps[(size_t)blockIdx.x * kStamps + i] = __builtin_amdgcn_s_memrealtime();
 }
 
@@ -118,12 +118,14 @@ __device__ void route_tail_rows1(const SmallParams &p, int32_t *lds_ids, uint32_
 #pragma unroll
     for (int i = 0; i < NK; ++i) keys[i] = 0u;
     unsigned long long sv = 0;
-    // poll until every key of this row (and its shared logit) has arrived
+    // Poll until every key of this row (and its shared logit) has arrived,
+    // at most wait_limit times.  Every poll is the same 1 + NK loads (the
+    // shared-logit slot exists in every workspace, used or not).
     bool arrived = false;
     for (int it = 0; it < p.wait_limit; ++it) {
 #pragma unroll
       for (int i = 0; i < NK; ++i) keys[i] = ld_agent(kr + min(lane + kWave * i, E - 1));
-      if (p.has_shared) sv = ld_agent(p.shared_logit + m);
+      sv = ld_agent(p.shared_logit + m);
       bool missing = p.has_shared && (sv >> 32) == 0;
 #pragma unroll
       for (int i = 0; i < NK; ++i) missing |= (lane + kWave * i < E) && keys[i] == 0u;
@@ -134,13 +136,8 @@ __device__ void route_tail_rows1(const SmallParams &p, int32_t *lds_ids, uint32_
     }
     if (!arrived) wait_failed(p, kWaitKeys, failed, lane);
     stamp(p, 2);
-    // consume: mask lanes past E, re-zero the slots for the next launch
 #pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      if (lane + kWave * i < E) st_agent(kr + lane + kWave * i, 0u);
-      else keys[i] = 0u;
-    }
-    if (p.has_shared && lane == 0) st_agent(p.shared_logit + m, 0ull);
+    for (int i = 0; i < NK; ++i) keys[i] = (lane + kWave * i < E) ? keys[i] : 0u;  // lanes past E
     sort_desc_u32(keys);
     stamp(p, 3);
     const uint32_t mine = topk_sorted_u32(keys, k, lane);  // lane j < k: the j-th chosen key
@@ -167,6 +164,12 @@ __device__ void route_tail_rows1(const SmallParams &p, int32_t *lds_ids, uint32_
         if (p.do_align) mark_pair(p, id, m, rowbm, touched);
       }
     }
+    // Re-zero the row's slots for the next launch.  Branch-free: lanes past
+    // E re-zero slot E - 1 too (one branch per slot, and a conditional
+    // shared-logit load in the poll, cost 0.25 us per launch at M = 1..4).
+#pragma unroll
+    for (int i = 0; i < NK; ++i) st_agent(kr + min(lane + kWave * i, E - 1), 0u);
+    if (p.has_shared && lane == 0) st_agent(p.shared_logit + m, 0ull);
     stamp(p, 5);
   }
 }
