@@ -39,21 +39,24 @@
 //    alone; a further group dots its two x rows with the shared gate row
 //    while its partial-row loads are in flight), builds the packed keys,
 //    takes k rounds of a wave-wide maximum, then the softmax, the shared
-//    slot and the stores.  Each routed pair also bumps a per-(128-token
-//    tile, expert) counter.
+//    slot and the stores.  With more than one token tile, each routed pair
+//    also bumps a per-(128-token tile, expert) counter.
 // A. Align.  Every block turns the tile counters into padded expert offsets
 //    (block scan) and the prefix of earlier tiles, adds the counts of the
 //    earlier tokens of its own tile (read back from topk_ids, in the same
 //    round of loads as the counters) and of its own earlier tokens (a bit
 //    mask per expert), and scatters its pairs in parallel: inside an expert,
-//    pairs keep ascending flat index.  Blocks also pad the experts dealt to
-//    them and write expert_ids; block 0 writes npp.
+//    pairs keep ascending flat index.  With one token tile (M <= 128) there
+//    are no counters: every block reads all M * S ids and counts them in
+//    LDS (the counters' atomics, all on a few cache lines, cost more: C3
+//    17.3 -> 15.8 us).  Blocks also pad the experts dealt to them and write
+//    expert_ids; block 0 writes npp.
 //
 // Workspace: the counter words as the library leaves them (the grid
 // barriers use one of two counter sets by the parity of a launch count; each
 // launch clears the other set and block 0 advances the count at the end);
-// the tile counters (one word per expert and 128-token tile) are cleared
-// during phase G.
+// the tile counters (one word per expert and 128-token tile, used with more
+// than one tile) are cleared during phase G.
 #include <atomic>
 
 #include "device_common.h"
@@ -551,7 +554,7 @@ __device__ void topk_group(const MfmaParams &p, int32_t *own, int g, const float
       st_agent(p.ids + (size_t)m * S + lane, id);
       p.wts[(size_t)m * S + lane] = w;
       own[(m - t0) * S + lane] = id;
-      if (p.do_align && lane < k)
+      if (p.do_align && p.NT > 1 && lane < k)  // (one token tile: the align counts the ids itself)
         __hip_atomic_fetch_add(p.tcnt + (size_t)(m >> 7) * p.tcnt_row + id, 1u,
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -672,7 +675,8 @@ static_assert(kMaxRouteExperts <= 4 * kThreads, "one 4-expert column chunk per t
 //   off[e] + (pairs of e in the 128-token tiles before m's)
 //          + (pairs of e among the earlier tokens of m's tile),
 // so each expert's pairs keep ascending flat index m * S + j.  The first
-// term comes from the per-(tile, expert) counters, the second from the ids
+// term comes from the per-(tile, expert) counters (one tile: none, and the
+// totals come from counting all the ids), the second from the ids
 // of the tile's tokens before the group (read back from topk_ids) plus a bit
 // mask per expert of the group's own tokens.  The shared slot of token m
 // sits at off[E] + m.  The counter table and the earlier ids are fetched in
@@ -693,11 +697,15 @@ __device__ uint32_t align_group(const MfmaParams &p, int g, const int32_t *own, 
   // first rows of the counter table (one word per expert, tcnt_row words
   // per tile).  The histogram of the earlier ids and the masks of the own
   // tokens are built while the table is in flight.
+  // A launch of one token tile keeps no counter table: every block reads all
+  // M * S ids instead (at most 128 * 33) and counts the totals itself.
+  const bool one_tile = NT == 1;
   const int nprev = (t0 - tstart) * S;
+  const int nread = one_tile ? M * S : nprev;
   const uint32_t *prev = reinterpret_cast<const uint32_t *>(p.ids + (size_t)tstart * S);
   uint32_t pv[8];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) pv[u] = prev[min(u * kThreads + tid, max(nprev - 1, 0))];
+  for (int u = 0; u < 8; ++u) pv[u] = prev[min(u * kThreads + tid, max(nread - 1, 0))];
   // The counter table: thread t sums the column chunk of experts 4t .. 4t+3
   // over every tile row (tot) and over the rows before the group's tile
   // (pre), straight from 16-byte loads, kRowBatch rows per round.
@@ -709,22 +717,46 @@ __device__ uint32_t align_group(const MfmaParams &p, int g, const int32_t *own, 
 #pragma unroll
     for (int u = 0; u < kRowBatch; ++u) v[u] = src[(size_t)min(u, NT - 1 - r0) * (W / 4)];
   };
-  load_rows(0);
-  for (int e = tid; e < Ep; e += kThreads) {
-    hist[e] = 0u;
-    for (int w = 0; w < nmw; ++w) mask[e * nmw + w] = 0u;
-  }
-  __syncthreads();
+  if (one_tile) {
+    for (int e = tid; e < Ep; e += kThreads) {
+      hist[e] = 0u;
+      tot[e] = 0u;
+      for (int w = 0; w < nmw; ++w) mask[e * nmw + w] = 0u;
+    }
+    __syncthreads();
+    auto count = [&](int i, uint32_t e) {  // id e at flat index i of the tile
+      if (i < nread && e < (uint32_t)E) {
+        if (i < nprev) atomicAdd(hist + e, 1u);
+        atomicAdd(tot + e, 1u);
+      }
+    };
 #pragma unroll
-  for (int u = 0; u < 8; ++u)
-    if (u * kThreads + tid < nprev && pv[u] < (uint32_t)E) atomicAdd(hist + pv[u], 1u);
-  for (int i0 = 8 * kThreads; i0 < nprev; i0 += 8 * kThreads) {
-    uint32_t w[8];
+    for (int u = 0; u < 8; ++u) count(u * kThreads + tid, pv[u]);
+    for (int i0 = 8 * kThreads; i0 < nread; i0 += 8 * kThreads) {
+      uint32_t w[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) w[u] = prev[min(i0 + u * kThreads + tid, nprev - 1)];
+      for (int u = 0; u < 8; ++u) w[u] = prev[min(i0 + u * kThreads + tid, nread - 1)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) count(i0 + u * kThreads + tid, w[u]);
+    }
+  } else {
+    load_rows(0);
+    for (int e = tid; e < Ep; e += kThreads) {
+      hist[e] = 0u;
+      for (int w = 0; w < nmw; ++w) mask[e * nmw + w] = 0u;
+    }
+    __syncthreads();
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      if (i0 + u * kThreads + tid < nprev && w[u] < (uint32_t)E) atomicAdd(hist + w[u], 1u);
+      if (u * kThreads + tid < nprev && pv[u] < (uint32_t)E) atomicAdd(hist + pv[u], 1u);
+    for (int i0 = 8 * kThreads; i0 < nprev; i0 += 8 * kThreads) {
+      uint32_t w[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) w[u] = prev[min(i0 + u * kThreads + tid, nprev - 1)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (i0 + u * kThreads + tid < nprev && w[u] < (uint32_t)E) atomicAdd(hist + w[u], 1u);
+    }
   }
   const int npairs = (t1 - t0) * S;
   for (int i = tid; i < npairs; i += kThreads) {
@@ -735,7 +767,11 @@ __device__ uint32_t align_group(const MfmaParams &p, int g, const int32_t *own, 
     }
   }
   uint32_t tot4[4] = {0u, 0u, 0u, 0u}, pre4[4] = {0u, 0u, 0u, 0u};
-  for (int r0 = 0; r0 < NT; r0 += kRowBatch) {
+  if (one_tile) {
+    __syncthreads();  // every id is counted
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tot4[j] = (has_c && ce + j < E) ? tot[ce + j] : 0u;
+  } else for (int r0 = 0; r0 < NT; r0 += kRowBatch) {
     if (r0) load_rows(r0);
 #pragma unroll
     for (int u = 0; u < kRowBatch; ++u)
@@ -830,7 +866,7 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(MfmaParams p) {
   // tile waits, the items of a token tile clear that tile's counter row
   // (each its share) before they arrive; otherwise every block clears a
   // slice and the grid barrier orders the clear before the top-k phase.
-  const bool clear_tcnt = p.do_align && !p.logits_only;
+  const bool clear_tcnt = p.do_align && !p.logits_only && p.NT > 1;
   if (clear_tcnt && !p.tile_wait)
     for (int i = b * kThreads + threadIdx.x; i < p.NT * p.tcnt_row; i += (int)grid * kThreads)
       __hip_atomic_fetch_and(p.tcnt + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
