@@ -60,6 +60,17 @@ def test_selection_one_lane_holds_many(M):
     _run_and_check(d, 10, 1.0, exact=True)
 
 
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_selection_two_lanes_hold_the_lead(M):
+    """Sixteen experts far ahead of the rest sit in lanes 0 and 1 (all eight
+    keys of each), so the rounds' short lists run out in both lanes and the
+    selection is redone on the full lists."""
+    _say("two lanes lead", M)
+    lead = [64 * i for i in range(8)] + [64 * i + 1 for i in range(8)]
+    d = lane_heavy_inputs(M, 512, 4096, lead, seed=70 + M)
+    _run_and_check(d, 10, 1.0, exact=True)
+
+
 def test_exact_inputs_m8_bit_exact():
     wl = workloads.ROUTER_E512_M8_EXACT
     _say(wl)
