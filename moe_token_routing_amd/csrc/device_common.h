@@ -92,6 +92,18 @@ __device__ __forceinline__ uint32_t wave_max_all_u32(uint32_t v) {
   return max(b[0], b[1]);
 }
 
+// Max over each half of the wave (lanes 0..31 and 32..63), left in every
+// lane of that half: DPP within rows of 16, then the permlane16 swap pairs
+// rows 0 and 1, and rows 2 and 3.  Every lane must be active.
+__device__ __forceinline__ uint32_t half_max_all_u32(uint32_t v) {
+  v = max(v, dpp_u32<kQuadXor1>(v));
+  v = max(v, dpp_u32<kQuadXor2>(v));
+  v = max(v, dpp_u32<kRowHalfMirror>(v));
+  v = max(v, dpp_u32<kRowMirror>(v));
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return max(a[0], a[1]);
+}
+
 // Value held by lane (lane ^ J), for J = 1, 2, 4, 8 (DPP inside a row of 16;
 // J = 4 is the half-row mirror 7 - i = i ^ 7 followed by a quad reversal,
 // i ^ 3) and J = 16, 32 (gfx950's permlane16 / permlane32 swaps, which hand

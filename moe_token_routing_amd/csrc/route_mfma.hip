@@ -473,6 +473,97 @@ __device__ void shared_logits(const MfmaParams &p, int t0, int t1, float *sh) {
   }
 }
 
+// Phase T for E <= 128 and S <= 32: a token's logits fill half a wave (32
+// lanes of 4 experts), so a wave takes its two tokens side by side, lanes
+// 0..31 the first (ma) and 32..63 the second (mb): the partial-row loads
+// (every lane's 16 bytes are a real chunk), the key sort and every
+// selection round run once for both, with maxima and sums over 32 lanes.
+// The split order of the sums, the keys and the selection rule are those of
+// the full-wave path, and the softmax sum adds the same values in the same
+// order, so the outputs are the same.  Tokens as there: t0 + wave + 4 i,
+// two at a time.
+__device__ void topk_halves(const MfmaParams &p, int32_t *own, int t0, int t1, const float *sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int half = lane >> 5, hl = lane & 31;
+  const int M = p.M, E = p.E, k = p.k, S = p.S, SK = p.SK, Epad = p.Epad;
+  const int ch = min(hl, (Epad >> 2) - 1);  // this lane's 16-byte chunk of a partial row
+  const int ntw = (t1 - t0 > wave) ? (t1 - t0 - wave + 3) / 4 : 0;
+  constexpr int SB = 16;  // splits per batch of loads
+  for (int ti = 0; ti < ntw; ti += 2) {
+    const bool two = ti + 1 < ntw;
+    const int ma = t0 + wave + 4 * ti, mb = two ? ma + 4 : ma;
+    const int m = half ? mb : ma;
+    const bool mine_store = half == 0 || two;  // with one token the upper half only shadows it
+    float z[4] = {0.f, 0.f, 0.f, 0.f};
+    float2 shl = make_float2(0.f, 0.f);
+    for (int s0 = 0; s0 < SK; s0 += SB) {
+      u32x4_coh v[SB];
+#pragma unroll
+      for (int s = 0; s < SB; ++s) {
+        const int sp = min(s0 + s, SK - 1);
+        v[s] = reinterpret_cast<const u32x4_coh *>(p.part + ((size_t)sp * M + m) * Epad)[ch];
+      }
+      if (s0 == 0 && p.has_shared) shl = sh ? make_float2(sh[ma - t0], sh[mb - t0]) : shared_pair(p, ma, mb);
+#pragma unroll
+      for (int s = 0; s < SB; ++s)
+        if (s0 + s < SK) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) z[i] += __uint_as_float(v[s][i]);
+        }
+    }
+    const float sl = half ? shl.y : shl.x;
+    if (p.logits_only) {
+      if (mine_store) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (4 * hl + i < E) p.logits_out[(size_t)m * p.Ep + 4 * hl + i] = z[i];
+        if (p.has_shared && hl == 0) p.logits_out[(size_t)m * p.Ep + E] = sl;
+      }
+      continue;
+    }
+    uint32_t key[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) key[i] = 4 * hl + i < E ? make_key(z[i], (uint32_t)(4 * hl + i)) : 0u;
+    sort_desc_u32(key);
+    // k rounds of the half-wave maximum of the lanes' heads; the lane that
+    // held it drops its head (keys are unique)
+    uint32_t mine = 0u;
+    for (int j = 0; j < k; ++j) {
+      const uint32_t top = half_max_all_u32(key[0]);
+      mine = hl == j ? top : mine;
+      const uint32_t keep = key[0] != top ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+      for (int i = 0; i < 3; ++i) key[i] = min(key[i], key[i + 1] | keep);
+      key[3] &= keep;
+    }
+    // softmax over the chosen k (each half's own first logit and sum), the
+    // shared slot, the stores
+    const float r = key_value(mine);
+    const float r0a = readlane_f32(r, 0), r0b = readlane_f32(r, 32);
+    const float ex = hl < k ? expf(r - (half ? r0b : r0a)) : 0.0f;
+    float t = ex;
+    t += dpp_f32<kQuadXor1>(t);
+    t += dpp_f32<kQuadXor2>(t);
+    t += dpp_f32<kRowHalfMirror>(t);
+    t += dpp_f32<kRowMirror>(t);
+    const float da = readlane_f32(t, 0) + readlane_f32(t, 16), db = readlane_f32(t, 32) + readlane_f32(t, 48);
+    int32_t id = (int32_t)key_id(mine);
+    float w = ex / (half ? db : da);
+    if (p.has_shared && hl == k) {
+      id = E;
+      w = p.scale / (1.0f + expf(-sl));
+    }
+    if (hl < S && mine_store) {
+      st_agent(p.ids + (size_t)m * S + hl, id);
+      p.wts[(size_t)m * S + hl] = w;
+      own[(m - t0) * S + hl] = id;
+      if (p.do_align && p.NT > 1 && hl < k)  // (one token tile: the align counts the ids itself)
+        __hip_atomic_fetch_add(p.tcnt + (size_t)(m >> 7) * p.tcnt_row + id, 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 // sh: the shared logits of group g's tokens when the caller computed them
 // already (else null).
 template <int NKP>  // E <= 128 * NKP
@@ -483,6 +574,12 @@ __device__ void topk_group(const MfmaParams &p, int32_t *own, int g, const float
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int M = p.M, E = p.E, k = p.k, S = p.S, SK = p.SK, Epad = p.Epad;
   const int t0 = g * p.tpb, t1 = min(M, t0 + p.tpb);
+  if constexpr (NKP == 1) {
+    if (S <= 32) {
+      topk_halves(p, own, t0, t1, sh);
+      return;
+    }
+  }
   // compiled in only where E > 128 (E <= 128 takes all its splits in one
   // batch at H <= 2048, and the extra code slowed that instantiation)
   constexpr bool kCoop = NCH >= 2;
