@@ -154,8 +154,11 @@ __device__ void route_tail_rows1(const SmallParams &p, int32_t *lds_ids, uint32_
       w = p.scale / (1.0f + expf(-s));
     }
     if (lane < S) {
-      p.ids[(size_t)m * S + lane] = id;
-      p.wts[(size_t)m * S + lane] = w;
+      // every output of this launch is written through, like the keys: the
+      // end-of-launch L2 write-back then finds fewer dirty lines (measured
+      // -0.04 to -0.07 us per launch at M = 1..8)
+      st_agent(p.ids + (size_t)m * S + lane, id);
+      st_agent(p.wts + (size_t)m * S + lane, w);
       if (hand_off) {
         // for block 0's align
         st_agent(p.hids + (size_t)m * S + lane, arrived ? (uint32_t)id + 1u : kFailedHandOff);
@@ -241,7 +244,7 @@ __device__ void align_small(const SmallParams &p, const int32_t *lds_ids, const 
   const uint32_t incl = wave_incl_scan_u32(pc, lane);
   const uint32_t excl = incl - pc;  // touched experts in the words before lane's
   // npp = -1 marks a launch one of whose waits gave up
-  if (tid == 0) *p.npp = *failed ? -1 : (int32_t)(__builtin_amdgcn_readlane(incl, 63) << sh);
+  if (tid == 0) st_agent(p.npp, *failed ? -1 : (int32_t)(__builtin_amdgcn_readlane(incl, 63) << sh));
   for (int i0 = wave * kWave; i0 < n; i0 += kThreads) {  // wave-uniform trip count: every lane active
     const int i = i0 + lane;
     const int e = lds_ids[min(i, n - 1)];
@@ -253,8 +256,8 @@ __device__ void align_small(const SmallParams &p, const int32_t *lds_ids, const 
     const uint32_t blk = base + __builtin_popcount(touched[ew] & ((1u << (e & 31)) - 1u));
     const uint32_t rank = __builtin_popcount(rowbm[e] & ((1u << m) - 1u));
     const uint64_t pos = ((uint64_t)blk << sh) + rank;
-    if (pos < (uint64_t)p.sorted_cap) p.sorted[pos] = i;
-    if (rank == 0 && blk < (uint64_t)p.expert_cap) p.expert_ids[blk] = e;
+    if (pos < (uint64_t)p.sorted_cap) st_agent(p.sorted + pos, (int32_t)i);
+    if (rank == 0 && blk < (uint64_t)p.expert_cap) st_agent(p.expert_ids + blk, (int32_t)e);
   }
 }
 
