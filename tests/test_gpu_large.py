@@ -107,11 +107,23 @@ def test_exact_inputs_large_m(M):
     (130, 3, 96, True, 257, 2.0),      # two expert tiles, second nearly empty
     (512, 10, 8, True, 70, 1.0),       # H smaller than one MFMA step
     (256, 8, 1024, False, 1000, 1.0),
+    (128, 31, 256, True, 300, 1.0),    # E <= 128, S = 32: two tokens per wave side by side, shared slot in lane 31
+    (128, 32, 256, True, 300, 1.0),    # E <= 128 but S = 33: the full-wave selection
 ])
 def test_large_shapes(E, k, H, shared, M, scale):
     _say("shape", E, k, H, shared, M, scale)
     d = workloads.make_inputs(M, E, H, shared, "normal", seed=E * 7 + k)
     _run(d, k, scale)
+
+
+@pytest.mark.parametrize("M", [300, 1100])
+def test_selection_e128_lanes_full(M):
+    """E = 128: a token's keys fill 32 lanes of 4, and its eight chosen
+    experts (0..7) fill lanes 0 and 1 of its half-wave completely, so every
+    key of those lanes is taken before any other lane's."""
+    _say("e128 lanes full", M)
+    d = lane_heavy_inputs(M, 128, 512, list(range(8)), seed=80 + M)
+    _run(d, 8, exact=True)
 
 
 @pytest.mark.parametrize("M,pairs", [(64, False), (1100, True)])
