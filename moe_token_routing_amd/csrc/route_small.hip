@@ -405,7 +405,11 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
       const uint4 *xb = reinterpret_cast<const uint4 *>(p.x);
       constexpr int kChunks = 2 * RPB;             // chunks per thread per iteration (H = 4096: one iteration)
       constexpr int kStride = WPR * kWave;         // threads sharing the row
-      constexpr int kRowsPerGroup = 16 / kChunks;  // token rows whose chunks are loaded together
+      // token rows whose chunks are loaded together: 16 loads per group, but
+      // never more rows than acc holds (with one gate row per block, 16 loads
+      // would be 8 rows of 4 sums)
+      constexpr int kRowsPerGroup = 16 / kChunks < MAXM ? 16 / kChunks : MAXM;
+      static_assert(MAXM % kRowsPerGroup == 0, "whole groups of token rows");
       int c0 = sub * kWave + lane;
       for (; c0 + (kChunks - 1) * kStride < nch; c0 += kChunks * kStride) {
         uint4 wv[kChunks];

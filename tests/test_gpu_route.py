@@ -120,6 +120,9 @@ def test_router_sweep_small_m(M):
     (512, 10, 4096, True, 21, 1.0),  # 24-row loads
     (512, 10, 4096, True, 28, 1.0),  # 28-row loads
     (512, 10, 4096, True, 29, 1.0),  # 32-row loads
+    (128, 8, 4096, False, 3, 1.0),   # one gate row per block (E' <= 256) at M <= 4, H > 2048: two chunks a thread
+    (191, 23, 3808, False, 4, 1.0),  # the same with a ragged last pass and k > 16
+    (255, 6, 2056, True, 1, 1.0),    # E' = 256, one 16-byte chunk past the two-chunk passes
 ])
 def test_router_shapes(E, k, H, shared, M, scale):
     _say("shape", E, k, H, shared, M, scale)
