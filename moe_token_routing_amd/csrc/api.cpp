@@ -204,7 +204,8 @@ int route_impl(const char *fn, const void *x, const void *gate_w, const void *sh
   uint32_t *ctr = reinterpret_cast<uint32_t *>(wsb + L.counters);
   int log2A = 0;
   while ((1 << log2A) < A) ++log2A;
-  const uint32_t S_magic = (uint32_t)((((uint64_t)1 << 32) + (uint64_t)S - 1) / (uint64_t)S);
+  // ceil(2^32 / S); at S = 1 it would need 33 bits (the kernel does not divide then)
+  const uint32_t S_magic = S == 1 ? 0u : (uint32_t)((((uint64_t)1 << 32) + (uint64_t)S - 1) / (uint64_t)S);
   int64_t fill = 0;
   if (do_align) {
     fill = tight_capacity(n, Ep, A);

@@ -76,7 +76,8 @@ struct SmallParams {
   int stamp_blocks;   // blocks b < stamp_blocks record
   // align
   int do_align, A, log2A;
-  uint32_t S_magic;  // ceil(2^32 / S): i / S == umulhi(i, S_magic) for i < 2^32 / S
+  uint32_t S_magic;  // ceil(2^32 / S) for S >= 2: i / S == umulhi(i, S_magic) for i < 2^32 / S
+                     // (2^32 does not fit: S = 1 is not divided at all)
   int32_t *sorted;
   int64_t sorted_cap;
   int32_t *expert_ids;

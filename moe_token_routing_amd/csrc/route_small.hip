@@ -252,7 +252,7 @@ __device__ void align_small(const SmallParams &p, const int32_t *lds_ids, const 
     const int ew = valid ? e >> 5 : 0;
     const uint32_t base = (uint32_t)__builtin_amdgcn_ds_bpermute(ew << 2, (int)excl);
     if (!valid) continue;
-    const uint32_t m = __umulhi((uint32_t)i, p.S_magic);
+    const uint32_t m = p.S == 1 ? (uint32_t)i : __umulhi((uint32_t)i, p.S_magic);  // token row i / S
     const uint32_t blk = base + __builtin_popcount(touched[ew] & ((1u << (e & 31)) - 1u));
     const uint32_t rank = __builtin_popcount(rowbm[e] & ((1u << m) - 1u));
     const uint64_t pos = ((uint64_t)blk << sh) + rank;

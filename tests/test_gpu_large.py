@@ -109,6 +109,8 @@ def test_exact_inputs_large_m(M):
     (256, 8, 1024, False, 1000, 1.0),
     (128, 31, 256, True, 300, 1.0),    # E <= 128, S = 32: two tokens per wave side by side, shared slot in lane 31
     (128, 32, 256, True, 300, 1.0),    # E <= 128 but S = 33: the full-wave selection
+    (64, 1, 512, False, 300, 1.0),     # S = 1
+    (513, 1, 1024, False, 40, 1.0),    # S = 1, E > 512
 ])
 def test_large_shapes(E, k, H, shared, M, scale):
     _say("shape", E, k, H, shared, M, scale)

@@ -123,6 +123,8 @@ def test_router_sweep_small_m(M):
     (128, 8, 4096, False, 3, 1.0),   # one gate row per block (E' <= 256) at M <= 4, H > 2048: two chunks a thread
     (191, 23, 3808, False, 4, 1.0),  # the same with a ragged last pass and k > 16
     (255, 6, 2056, True, 1, 1.0),    # E' = 256, one 16-byte chunk past the two-chunk passes
+    (14, 1, 256, False, 15, 1.0),    # S = 1 (k = 1, no shared expert): a pair's token row is its index
+    (512, 1, 4096, False, 4, 1.0),   # S = 1 in block 0's own tail
 ])
 def test_router_shapes(E, k, H, shared, M, scale):
     _say("shape", E, k, H, shared, M, scale)
