@@ -1,6 +1,7 @@
 """Parity over seeded draws of the whole supported shape space (needs a gfx950
-GPU): route + align on exactly representable inputs, and the standalone
-align on random ids.
+GPU): route + align on exactly representable and on random-normal inputs,
+the standalone and the expert-parallel align on random ids, and the row-wise
+argmax.
 
 The hand-picked shapes elsewhere aim at known boundaries (tile edges, lane
 layouts, row-load variants); these draws are meant to land where nobody
@@ -45,7 +46,7 @@ def _route_draws(n, seed):
     return out
 
 
-ROUTE_DRAWS = _route_draws(48, 20261202)
+ROUTE_DRAWS = _route_draws(96, 20261202)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -114,3 +115,87 @@ def test_align_seeded_shape(i, M, S, Ep, A, kind):
     ws = mr.new_workspace(M, Ep, S, False)
     srt, eids, npp = mr.mr_align(t, Ep, A, workspace=ws)
     check_align(ids, Ep, A, srt.cpu().numpy(), eids.cpu().numpy(), int(npp.item()))
+
+
+NORMAL_DRAWS = _route_draws(32, 20261204)
+
+
+@pytest.mark.parametrize("i,E,k,H,M,shared,scale,A", NORMAL_DRAWS)
+def test_route_align_seeded_normal(i, E, k, H, M, shared, scale, A):
+    """Random-normal inputs: the ids and weights must be what the oracle's
+    rounding and selection give on the kernel's own fp32 logits, each logit
+    within the fp32 accumulation bound, and the align exact."""
+    if A is not None and 17 <= M <= 32 and A < M:
+        A = None  # the logits hook shows the small launch's sums at these M; keep route+align on it too
+    _say("normal draw", i, "E", E, "k", k, "H", H, "M", M, "shared", shared, "scale", scale, "A", A)
+    d = workloads.make_inputs(M, E, H, shared, "normal", seed=3000 + i)
+    ref = oracle.route(d["x"], d["w"], d["ws"], k, scale)
+    g = route_align_gpu(d, k, scale, A)
+    lg = logits_gpu(d)
+    check_backstop(d["x"], d["w"], d["ws"], lg, g["topk_ids"], g["topk_weights"], k, scale, ref)
+    check_align(g["topk_ids"], E + shared, g["A"], g["sorted_token_ids"], g["expert_ids"], g["npp"][0])
+
+
+def _local_draws(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.integers(1, 1025))
+        S = int(rng.integers(1, 34))
+        M = int(np.round(np.exp(rng.uniform(0.0, np.log(20000)))))
+        A = int(rng.choice([16, 32, 64, 128, 256]))
+        ranks = int(rng.choice([1, 2, 4, 8, 16]))
+        out.append((i, M, S, E, ranks, int(rng.integers(0, ranks)), A))
+    return out
+
+
+@pytest.mark.parametrize("i,M,S,E,ranks,r,A", _local_draws(24, 20261205))
+def test_align_local_seeded_shape(i, M, S, E, ranks, r, A):
+    """Expert-parallel align of rank r: experts dealt round-robin, ids two
+    past either end of [0, E) skipped."""
+    import torch
+    import moe_token_routing_amd as mr
+
+    _say("align_local draw", i, "M", M, "S", S, "E", E, "rank", r, "of", ranks, "A", A)
+    rng = np.random.default_rng(4000 + i)
+    ids = rng.integers(-2, E + 2, size=(M, S)).astype(np.int32)
+    emap = np.full(E, -1, np.int32)
+    mine = np.arange(r, E, ranks)
+    emap[mine] = np.arange(mine.size, dtype=np.int32)
+    nl = max(1, int(mine.size))
+    ws = mr.new_workspace(M, nl, S, False)
+    srt, eids, npp = mr.mr_align_local(torch.from_numpy(ids).cuda(), torch.from_numpy(emap).cuda(), nl, A,
+                                       workspace=ws)
+    n = int(npp.item())
+    want = oracle.align_local(ids, emap, nl, A)
+    assert n == want[2], (n, want[2])
+    assert np.array_equal(srt[:n].cpu().numpy(), want[0])
+    assert np.array_equal(eids[: n // A].cpu().numpy(), want[1])
+
+
+def _argmax_draws(n, seed):
+    rng = np.random.default_rng(seed)
+    return [(i, int(rng.integers(1, 65)), int(np.round(np.exp(rng.uniform(0.0, np.log(300000))))),
+             str(rng.choice(["normal", "ties", "nan"]))) for i in range(n)]
+
+
+@pytest.mark.parametrize("i,R,N,kind", _argmax_draws(24, 20261206))
+def test_argmax_seeded_shape(i, R, N, kind):
+    """Row-wise argmax of [R, N] rows padded to a multiple of 4 values with a
+    value larger than any in the rows, which must never be read."""
+    import torch
+    import moe_token_routing_amd as mr
+
+    _say("argmax draw", i, "R", R, "N", N, kind)
+    rng = np.random.default_rng(5000 + i)
+    x = rng.standard_normal((R, N)).astype(np.float32)
+    if kind == "ties":
+        x = np.round(x * 2).astype(np.float32)
+    elif kind == "nan":
+        x.reshape(-1)[rng.choice(R * N, max(1, R * N // 1000), replace=False)] = np.nan
+    ld = N + (-N) % 4
+    xp = np.full((R, ld), 7.0e30, np.float32)
+    xp[:, :N] = x
+    ws = mr.new_argmax_workspace(R, N)
+    got = mr.mr_argmax_rows_f32(torch.from_numpy(xp).cuda(), workspace=ws, n=N).cpu().numpy()
+    assert np.array_equal(got, oracle.argmax_rows(x))
