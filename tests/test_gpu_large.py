@@ -173,11 +173,26 @@ def test_exact_large_alignment_variants():
 
 
 def test_grid_larger_than_gpu():
-    """More token groups than blocks of the persistent launch: every block
-    handles several groups through the top-k and align phases."""
+    """More gate items than blocks of the persistent launch (157 token tiles x
+    4 expert tiles): every block computes several items."""
     _say("M=20000 E=512")
     d = workloads.make_inputs(20000, 512, 256, True, "normal", seed=21)
     _run(d, 10)
+
+
+@pytest.mark.parametrize("M,E,H,k,shared", [
+    (32768, 128, 64, 8, False),    # 256 token tiles: the most that tile waits take, one group per block
+    (33000, 128, 128, 8, True),    # 258 tiles: grid barrier instead of tile waits; two blocks own 2 groups
+    (40000, 512, 256, 10, True),   # 313 groups of 128 tokens on 256 blocks
+    (100000, 16, 64, 4, False),    # 782 groups: most blocks own 3 or 4
+])
+def test_more_token_groups_than_blocks(M, E, H, k, shared):
+    """Past 256 groups of 128 tokens a block owns several groups: it selects
+    them one after another, keeps only the last group's ids in LDS and
+    reloads each group's ids for the align.  Exact inputs: ids bit-exact."""
+    _say("groups", M, E, H, k, shared)
+    d = workloads.make_inputs(M, E, H, shared, "int", seed=M + E)
+    _run(d, k, exact=True)
 
 
 def test_large_consecutive_and_graph():
