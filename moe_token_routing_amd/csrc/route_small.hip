@@ -12,15 +12,21 @@
 //   over the chosen k); slot k = (E, scale * sigmoid(s));
 //   then moe_align_block_size over the M*S (token, slot) pairs.
 //
-// Launch shape (one kernel):
-//   grid = ceil(E' / RPB) blocks of 256 threads; block b owns gate rows
-//   [b*RPB, b*RPB + RPB) of the E' = E + shared rows (the shared row is
-//   row E).  At M <= 4, RPB = 2 (E' > 256) and each row is split over the
-//   block's waves: a thread streams 16-byte chunks of its row (coalesced
-//   128-bit non-temporal loads) and the same chunks of every token row.  At
-//   M >= 5, RPB = 2 and thread t streams the chunks t, t + 256, ... of both
-//   gate rows and of the M token rows (each token chunk loaded once per
-//   block), and its 16 or 32 sums are reduced by a halving DPP butterfly.
+// Launch shape (one kernel), blocks of 256 threads over the E' = E + shared
+//   gate rows (the shared row is row E):
+//   - M <= 4: ceil(E' / RPB) blocks, block b owns rows [b*RPB, b*RPB + RPB)
+//     (RPB = 2 at E' > 256, else 1), each row split over the block's waves:
+//     a thread streams 16-byte chunks of its row (coalesced 128-bit
+//     non-temporal loads) and the same chunks of every token row.
+//   - 5 <= M <= 8: the same grid with RPB = 2; thread t streams the chunks
+//     t, t + 256, ... of both gate rows and of the M token rows (each token
+//     chunk loaded once per block), and its 16 sums are reduced by a halving
+//     DPP butterfly.
+//   - M >= 9: token tiles: a block takes 4 gate rows against 4 (M <= 20) or
+//     8 token rows in the same way, so it streams 8 or 12 rows whatever M.
+//     With T token tiles, block b takes row group 8 * ((b / 8) / T) + b mod 8
+//     and token tile (b / 8) mod T: the T blocks of a row group run on one
+//     XCD (b mod 8) and share its L2.
 //   Either way all loads of a batch are issued before any arithmetic
 //   (v_dot2_f32_bf16), and partial sums meet across waves in LDS.
 //
@@ -312,14 +318,25 @@ __device__ __forceinline__ float wave_totals(float (&v)[V], int lane, int &idx) 
 
 // ML: token rows the shared-chunk gate loads and dots (the others keep zero
 // sums): fewer than MAXM when a launch is known to have M <= ML.
-template <int RPB, int MAXM, bool SHARED, int NK, int ML = MAXM>
+// GT > 0: token-tiled gate (shared-chunk layout): a block takes RPB gate
+// rows against GT token rows only, so it streams RPB + GT rows instead of
+// RPB + M.
+template <int RPB, int MAXM, bool SHARED, int NK, int ML = MAXM, int GT = 0>
 __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
-  constexpr int V = RPB * MAXM;
+  static_assert(GT == 0 || SHARED, "token tiles use the shared-chunk layout");
+  constexpr int GM = GT ? GT : MAXM;  // token rows in a block's gate sums
+  constexpr int GL = GT ? GT : ML;    // of which the gate loads
+  constexpr int V = RPB * GM;
   constexpr int WPR = (kThreads / kWave) / RPB;  // waves per gate row (split layout)
   static_assert(!SHARED || V == 16 || V == 32 || V == 64, "the butterfly reduces 16, 32 or 64 sums per thread");
   __shared__ float red[kThreads / kWave][SHARED ? V : MAXM];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int row0 = blockIdx.x * RPB;
+  // token tiles: the blocks of one gate-row group sit on one XCD (block b
+  // runs on XCD b mod 8), so each gate row is fetched into one L2 only
+  const int ntg = GT ? (p.M + GT - 1) / GT : 1;
+  const int q8 = (int)blockIdx.x >> 3;
+  const int row0 = (GT ? (q8 / ntg) * 8 + ((int)blockIdx.x & 7) : (int)blockIdx.x) * RPB;
+  const int m0 = GT ? (q8 % ntg) * GT : 0;  // first token row of the gate sums
   const int H = p.H, M = p.M;
   const int nch = H >> 3;  // 16-byte chunks per row
 
@@ -359,16 +376,16 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
       wr[r] = reinterpret_cast<const uint4 *>(e < p.E ? p.w + (size_t)e * H : p.ws_row);
     }
     const uint4 *xb = reinterpret_cast<const uint4 *>(p.x);
-    constexpr int UB = (RPB + MAXM <= 18) ? 2 : 1;  // chunk positions per batch
+    constexpr int UB = (RPB + GL <= 18) ? 2 : 1;  // chunk positions per batch
     for (int c0 = tid; c0 < nch; c0 += UB * kThreads) {
-      uint4 wv[UB][RPB], xv[UB][MAXM];
+      uint4 wv[UB][RPB], xv[UB][GL];
 #pragma unroll
       for (int u = 0; u < UB; ++u) {
         const int c = min(c0 + u * kThreads, nch - 1);
 #pragma unroll
         for (int r = 0; r < RPB; ++r) wv[u][r] = ld_stream_16(wr[r] + c);
 #pragma unroll
-        for (int m = 0; m < ML; ++m) xv[u][m] = xb[(size_t)min(m, M - 1) * nch + c];
+        for (int m = 0; m < GL; ++m) xv[u][m] = xb[(size_t)min(m0 + m, M - 1) * nch + c];
       }
       // branch-free (a selected sum for a chunk past the row), and fenced from
       // the loads, so that all the batch's loads are issued together
@@ -379,9 +396,9 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
 #pragma unroll
         for (int r = 0; r < RPB; ++r)
 #pragma unroll
-          for (int m = 0; m < ML; ++m) {
-            const float t = dot8_bf16(wv[u][r], xv[u][m], acc[r * MAXM + m]);
-            acc[r * MAXM + m] = in ? t : acc[r * MAXM + m];
+          for (int m = 0; m < GL; ++m) {
+            const float t = dot8_bf16(wv[u][r], xv[u][m], acc[r * GM + m]);
+            acc[r * GM + m] = in ? t : acc[r * GM + m];
           }
       }
     }
@@ -450,7 +467,7 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
     __syncthreads();
   }
   if (tid < V) {
-    const int r = tid / MAXM, m = tid % MAXM;
+    const int r = tid / GM, m = m0 + tid % GM;
     const int e = row0 + r;
     float z;
     if constexpr (SHARED) {
@@ -500,17 +517,19 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
   stamp(p, 6);
 }
 
-template <int RPB, int MAXM, bool SHARED, int ML = MAXM>
+template <int RPB, int MAXM, bool SHARED, int ML = MAXM, int GT = 0>
 hipError_t launch_nk(const SmallParams &p, hipStream_t stream) {
+  const int nrg = (p.Ep + RPB - 1) / RPB;  // gate-row groups
+  // token tiles: row groups rounded up to a multiple of 8 (one XCD per group)
+  int grid = GT ? (nrg + 7) / 8 * 8 * ((p.M + GT - 1) / GT) : nrg;
   // at M >= 5 the first ceil(M / 4) blocks also run the tail: there must be
   // that many (extra blocks own no gate rows: their sums are dropped)
-  int grid = (p.Ep + RPB - 1) / RPB;
   if (MAXM > kThreads / kWave && grid < (p.M + 3) / 4) grid = (p.M + 3) / 4;
   const int nk = (p.E + kWave - 1) / kWave;
-  if (nk <= 2) route_small_kernel<RPB, MAXM, SHARED, 2, ML><<<grid, kThreads, 0, stream>>>(p);
-  else if (nk <= 4) route_small_kernel<RPB, MAXM, SHARED, 4, ML><<<grid, kThreads, 0, stream>>>(p);
-  else if (nk <= 8) route_small_kernel<RPB, MAXM, SHARED, 8, ML><<<grid, kThreads, 0, stream>>>(p);
-  else route_small_kernel<RPB, MAXM, SHARED, 16, ML><<<grid, kThreads, 0, stream>>>(p);
+  if (nk <= 2) route_small_kernel<RPB, MAXM, SHARED, 2, ML, GT><<<grid, kThreads, 0, stream>>>(p);
+  else if (nk <= 4) route_small_kernel<RPB, MAXM, SHARED, 4, ML, GT><<<grid, kThreads, 0, stream>>>(p);
+  else if (nk <= 8) route_small_kernel<RPB, MAXM, SHARED, 8, ML, GT><<<grid, kThreads, 0, stream>>>(p);
+  else route_small_kernel<RPB, MAXM, SHARED, 16, ML, GT><<<grid, kThreads, 0, stream>>>(p);
   return hipGetLastError();
 }
 
@@ -528,19 +547,14 @@ hipError_t launch_route_small(const SmallParams &p, hipStream_t stream) {
   if (p.M <= 4) return small_rows_per_block(p.Ep, p.M) == 2 ? launch_nk<2, 4, false>(p, stream)
                                                             : launch_nk<1, 4, false>(p, stream);
   if (p.M <= 8) return launch_nk<2, 8, true>(p, stream);
-  // 9 <= M <= 14: the same 16-row layout loading only 10, 12 or 14 token
-  // rows (measured -0.9 to -1.4 us at M = 9..12, -0.3 at 13..14 against
-  // loading 16)
-  if (p.M <= 10) return launch_nk<2, 16, true, 10>(p, stream);
-  if (p.M <= 12) return launch_nk<2, 16, true, 12>(p, stream);
-  if (p.M <= 14) return launch_nk<2, 16, true, 14>(p, stream);
-  if (p.M <= 16) return launch_nk<2, 16, true>(p, stream);
-  // 17 <= M <= 32: the 32-row layout loading 20, 24, 28 or 32 token rows
-  // (against always 32: -2.3 us at M = 17, -2.1 at 20, -1.3 at 24)
-  if (p.M <= 20) return launch_nk<2, 32, true, 20>(p, stream);
-  if (p.M <= 24) return launch_nk<2, 32, true, 24>(p, stream);
-  if (p.M <= 28) return launch_nk<2, 32, true, 28>(p, stream);
-  return launch_nk<2, 32, true>(p, stream);
+  // M >= 9: token tiles.  A block dots 4 gate rows with 4 (M <= 20) or 8
+  // token rows, the blocks of one row group on one XCD.  Measured at E' =
+  // 513, H = 4096 against every block taking 2 gate rows and all M token
+  // rows: M = 9 -0.5 us, 16 -0.5, 17 -2.1, 24 -2.3, 32 -2.9 (4 x 8 tiles are
+  // the faster of the two from M = 24; at M = 5..8 and M <= 4 tiles were
+  // slower by 0.35 to 0.5 us)
+  if (p.M <= 20) return launch_nk<4, 32, true, 32, 4>(p, stream);
+  return launch_nk<4, 32, true, 32, 8>(p, stream);
 }
 
 }  // namespace mr
