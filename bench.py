@@ -29,7 +29,7 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 ROTATE_BYTES = 512 << 20        # inputs rotated per replay
 FLUSH_BYTES = 512 << 20         # the fill before each call in the memset method
-SWEEP_M = (1, 2, 3, 4, 5, 8, 9, 12, 16, 17, 24, 32, 40, 512, 2048)
+SWEEP_M = (1, 2, 3, 4, 5, 8, 9, 12, 16, 17, 24, 32, 40, 64, 128, 512, 2048)
 
 
 def parse():

@@ -212,9 +212,14 @@ int route_impl(const char *fn, const void *x, const void *gate_w, const void *sh
     if (fill > sorted_cap) fill = sorted_cap;
   }
 
-  // The small-M launch takes M <= kSmallMaxTokens, and with align also
-  // M <= 16 or M <= A (its align puts each expert's pairs in one block).
-  const bool small = M <= mr::kSmallMaxTokens && (M <= 16 || !do_align || A >= M);
+  // The small-M launch (a gate that streams gate rows against tiles of
+  // token rows on the VALU, then one wave per token row) up to 32 rows, and
+  // up to kSmallMaxTokens rows while its gate's multiply-adds stay under
+  // 160 M: measured against the prefill launch, M = 40 and 64 at E' = 513,
+  // H = 4096 (84 M and 134 M) 12.8 and 15.7 us against 18.6 and 18.7; M = 128
+  // at E = 128, H = 2048 (34 M) 12.0 against 15.2; M = 128 at E' = 513 (269 M)
+  // 24.0 against 21.0.
+  const bool small = M <= 32 || (M <= mr::kSmallMaxTokens && (int64_t)M * Ep * H <= (int64_t)160 << 20);
   if (!small) {
     const int cap = mr::mfma_capacity(E);
     if (cap < 1) {

@@ -11,7 +11,7 @@ namespace mr {
 constexpr int kMaxTopK = 32;            // routed k
 constexpr int kMaxRouteExperts = 1024;  // routed E for the route kernels
 constexpr int kMaxAlignExperts = 4096;  // E' for align
-constexpr int kSmallMaxTokens = 32;     // route_small handles M <= 32 (with align: M <= A as well)
+constexpr int kSmallMaxTokens = 128;    // the most token rows route_small takes
 
 // Counter words at the start of the workspace.  The first 256 bytes hold
 // single counters; then kTicketLanes first-level barrier counters follow,

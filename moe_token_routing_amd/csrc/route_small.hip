@@ -62,7 +62,7 @@ constexpr int kThreads = 256;
 // What a tail block hands block 0 in place of its ids when its own key wait
 // gave up (a real hand-off value is id + 1 <= 65536).
 constexpr uint32_t kFailedHandOff = 0xFFFFFFFFu;
-static_assert(kSmallMaxTokens <= 32, "one bit per token row in rowbm; the host sends M > A to the prefill launch, so each expert's pairs (one per row) fit one block of A slots");
+static_assert(kSmallMaxTokens <= 128, "up to 4 words of token-row bits per expert in rowbm");
 
 // Max of N keys held in registers (a balanced tree, depth log2 N).
 template <int N>
@@ -81,10 +81,11 @@ __device__ __forceinline__ uint32_t max_of(const uint32_t (&a)[N]) {
 // rowbm[e] marks that token row m chose expert e, bit e & 31 of
 // touched[e >> 5] that some row did.  The tail marks each pair as it stores
 // it; ids outside [0, E') are skipped.
+template <int BW>
 __device__ __forceinline__ void mark_pair(const SmallParams &p, int32_t id, int m, uint32_t *rowbm,
                                           uint32_t *touched) {
   if ((uint32_t)id < (uint32_t)p.Ep) {
-    atomicOr(&rowbm[id], 1u << m);
+    atomicOr(&rowbm[id * BW + (m >> 5)], 1u << (m & 31));
     atomicOr(&touched[id >> 5], 1u << (id & 31));
   }
 }
@@ -113,7 +114,7 @@ __device__ __forceinline__ void wait_failed(const SmallParams &p, uint32_t bit, 
 // into lds_ids and the align bitmaps (block 0) or, with hand_off, to block 0
 // through the hids row (id + 1, written through; kFailedHandOff if this
 // wave's key wait gave up).
-template <int NK>
+template <int NK, int BW>
 __device__ void route_tail_rows1(const SmallParams &p, int32_t *lds_ids, uint32_t *rowbm, uint32_t *touched,
                                  int m0, int m1, bool hand_off, uint32_t *failed) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -170,7 +171,7 @@ __device__ void route_tail_rows1(const SmallParams &p, int32_t *lds_ids, uint32_
         st_agent(p.hids + (size_t)m * S + lane, arrived ? (uint32_t)id + 1u : kFailedHandOff);
       } else {
         lds_ids[m * S + lane] = id;
-        if (p.do_align) mark_pair(p, id, m, rowbm, touched);
+        if (p.do_align) mark_pair<BW>(p, id, m, rowbm, touched);
       }
     }
     // Re-zero the row's slots for the next launch.  Branch-free: lanes past
@@ -189,11 +190,12 @@ __device__ void route_tail_rows1(const SmallParams &p, int32_t *lds_ids, uint32_
 // the key poll), then puts them in lds_ids, marks the align bitmaps and
 // re-zeroes the slots for the next launch.  A slot holding kFailedHandOff
 // (that block's key wait gave up) raises the block's failed flag.
-__device__ void gather_tail_ids(const SmallParams &p, int32_t *lds_ids, uint32_t *rowbm, uint32_t *touched,
+template <int MAXM, int BW>
+__device__ void gather_tail_rows(const SmallParams &p, int32_t *lds_ids, uint32_t *rowbm, uint32_t *touched,
                                 uint32_t *failed) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int S = p.S;
-  constexpr int kRows = kSmallMaxTokens / (kThreads / kWave) - 1;  // rows 4 + w + 4 r
+  constexpr int kRows = MAXM / (kThreads / kWave) - 1;  // rows 4 + w + 4 r
   uint32_t v[kRows];
 #pragma unroll
   for (int r = 0; r < kRows; ++r) v[r] = 0u;
@@ -221,8 +223,72 @@ __device__ void gather_tail_ids(const SmallParams &p, int32_t *lds_ids, uint32_t
       marker |= v[r] == kFailedHandOff;
       const int32_t id = (int32_t)v[r] - 1;  // kFailedHandOff and 0 give ids < 0: skipped
       lds_ids[m * S + lane] = id;
-      mark_pair(p, id, m, rowbm, touched);
+      mark_pair<BW>(p, id, m, rowbm, touched);
       st_agent(p.hids + (size_t)m * S + lane, 0u);
+    }
+  }
+  if (__builtin_amdgcn_ballot_w64(marker) != 0 && lane == 0) *failed = 1u;
+}
+
+// The same for up to 128 rows: blocks 1.. wrote the ids of
+// rows 4.. as id + 1 with write-through stores into hids, which is dense
+// [M, S] like topk_ids, so block 0 polls it as a flat array: thread t takes
+// the 16-byte chunks t, t + 256, ... from the one holding row 4's first slot,
+// one round of loads per poll (bounded, as the key poll), then puts the ids
+// in lds_ids, marks the align bitmaps and re-zeroes its chunks for the next
+// launch.  A slot holding kFailedHandOff (that block's key wait gave up)
+// raises the block's failed flag.
+template <int MAXM, int BW>
+__device__ void gather_tail_flat(const SmallParams &p, int32_t *lds_ids, uint32_t *rowbm, uint32_t *touched,
+                                uint32_t *failed) {
+  constexpr int kChunks = (MAXM * (kMaxTopK + 1) + 3) / 4;  // 16-byte chunks of the largest hids
+  constexpr int kPer0 = (kChunks + kThreads - 1) / kThreads;
+  constexpr int kPer = kPer0 <= 1 ? 1 : kPer0 <= 2 ? 2 : kPer0 <= 4 ? 4 : 8;  // chunks per thread
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int S = p.S, n = p.M * S, i0 = 4 * S;  // entries [i0, n): rows 4 ..
+  const int c0 = i0 >> 2, c1 = (n + 3) >> 2;
+  const u32x4_coh *hv = reinterpret_cast<const u32x4_coh *>(p.hids);
+  const u32x4_coh *a[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) a[u] = hv + min(c0 + tid + kThreads * u, c1 - 1);
+  u32x4_coh v[kPer];
+  auto want = [&](int u, int q) {  // entry q of this thread's chunk u is one of rows 4 ..
+    const int i = 4 * (c0 + tid + kThreads * u) + q;
+    return c0 + tid + kThreads * u < c1 && i >= i0 && i < n;
+  };
+  bool arrived = false;
+  for (int it = 0; it < p.wait_limit; ++it) {
+    ld_coherent_x4<kPer>(v, a);
+    bool missing = false;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) missing |= want(u, q) && v[u][q] == 0u;
+    if (__builtin_amdgcn_ballot_w64(missing) == 0) {
+      arrived = true;
+      break;
+    }
+  }
+  if (!arrived) wait_failed(p, kWaitIds, failed, lane);
+  bool marker = false;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int c = c0 + tid + kThreads * u;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (want(u, q)) {
+        const int i = 4 * c + q;
+        marker |= v[u][q] == kFailedHandOff;
+        const int32_t id = (int32_t)v[u][q] - 1;  // kFailedHandOff and 0 give ids < 0: skipped
+        lds_ids[i] = id;
+        const int m = S == 1 ? i : (int)__umulhi((uint32_t)i, p.S_magic);  // token row i / S
+        mark_pair<BW>(p, id, m, rowbm, touched);
+      }
+    }
+    if (c < c1) {
+      unsigned long long *z = reinterpret_cast<unsigned long long *>(p.hids) + 2 * c;
+      st_agent(z, 0ull);
+      st_agent(z + 1, 0ull);
     }
   }
   if (__builtin_amdgcn_ballot_w64(marker) != 0 && lane == 0) *failed = 1u;
@@ -264,6 +330,60 @@ __device__ void align_small(const SmallParams &p, const int32_t *lds_ids, const 
     const uint64_t pos = ((uint64_t)blk << sh) + rank;
     if (pos < (uint64_t)p.sorted_cap) st_agent(p.sorted + pos, (int32_t)i);
     if (rank == 0 && blk < (uint64_t)p.expert_cap) st_agent(p.expert_ids + blk, (int32_t)e);
+  }
+}
+
+// Tail, part 2 for up to 128 token rows and any A (BW words of token-row
+// bits per expert): an expert's pairs may fill several blocks of A slots.
+// Thread t counts the pairs of experts 5t .. 5t+4 (popcounts of their
+// bits), pads each to blocks of A, and one block scan gives every expert
+// its first block (boff, LDS); the thread writes those experts' expert_ids.
+// A pair's slot is its expert's first slot plus the number of earlier token
+// rows that chose the same expert (ascending flat index inside the expert).
+// Every thread of the block calls this after the barrier that follows the
+// tail's marks.
+template <int BW>
+__device__ void align_small_wide(const SmallParams &p, const int32_t *lds_ids, const uint32_t *rowbm,
+                                 uint32_t *boff, uint32_t *scan_tmp, const uint32_t *failed) {
+  constexpr int EPT = (kMaxRouteExperts + 1 + kThreads - 1) / kThreads;  // experts per thread
+  const int tid = threadIdx.x;
+  const int n = p.M * p.S, Ep = p.Ep, sh = p.log2A;
+  const uint32_t amask = (uint32_t)p.A - 1u;
+  const int e0 = tid * EPT;
+  uint32_t nb[EPT], run = 0;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    uint32_t c = 0;
+    if (e0 + j < Ep) {
+#pragma unroll
+      for (int w = 0; w < BW; ++w) c += __builtin_popcount(rowbm[(e0 + j) * BW + w]);
+    }
+    nb[j] = (c + amask) >> sh;
+    run += nb[j];
+  }
+  uint32_t total;
+  uint32_t o = block_excl_scan_u32<kThreads>(run, scan_tmp, &total);
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    if (e0 + j < Ep) {
+      boff[e0 + j] = o;
+      for (uint32_t b = 0; b < nb[j]; ++b)
+        if (o + b < (uint64_t)p.expert_cap) st_agent(p.expert_ids + o + b, (int32_t)(e0 + j));
+      o += nb[j];
+    }
+  }
+  // npp = -1 marks a launch one of whose waits gave up
+  if (tid == 0) st_agent(p.npp, *failed ? -1 : (int32_t)(total << sh));
+  __syncthreads();  // boff complete
+  for (int i = tid; i < n; i += kThreads) {
+    const int e = lds_ids[i];
+    if (e < 0 || e >= Ep) continue;
+    const uint32_t m = p.S == 1 ? (uint32_t)i : __umulhi((uint32_t)i, p.S_magic);  // token row i / S
+    const uint32_t *bits = rowbm + e * BW;
+    uint32_t rank = __builtin_popcount(bits[m >> 5] & ((1u << (m & 31)) - 1u));
+    for (uint32_t w = 0; w < (m >> 5); ++w) rank += __builtin_popcount(bits[w]);
+    const uint64_t pos = ((uint64_t)boff[e] << sh) + rank;
+    if (pos < (uint64_t)p.sorted_cap) st_agent(p.sorted + pos, (int32_t)i);
   }
 }
 
@@ -342,11 +462,12 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
 
   // align bitmaps of block 0's tail: zeroed now, off the tail's path (the
   // gate's block barrier orders these stores before the tail's marks)
-  __shared__ uint32_t rowbm[kWave * NK + 1];  // E' <= 64 NK + 1
+  constexpr int BW = (MAXM + 31) / 32;  // words of token-row bits per expert
+  __shared__ uint32_t rowbm[(kWave * NK + 1) * BW];  // E' <= 64 NK + 1
   __shared__ uint32_t touched[kMaxRouteExperts / 32 + 1];
   __shared__ uint32_t failed;  // a wait of this block gave up
   if (blockIdx.x == 0 && p.do_align && !p.logits_only) {
-    for (int e = tid; e < p.Ep; e += kThreads) rowbm[e] = 0u;
+    for (int e = tid; e < p.Ep * BW; e += kThreads) rowbm[e] = 0u;
     for (int w = tid; w < ((p.Ep + 31) >> 5); w += kThreads) touched[w] = 0u;
   }
   if (tid == 0) failed = 0u;
@@ -497,11 +618,21 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
     if ((int)blockIdx.x >= (M + 3) / 4) return;
     __shared__ int32_t lds_ids[MAXM * (kMaxTopK + 1)];
     const int m0 = 4 * blockIdx.x;
-    route_tail_rows1<NK>(p, lds_ids, rowbm, touched, m0, min(M, m0 + 4), blockIdx.x != 0 && p.do_align, &failed);
+    route_tail_rows1<NK, BW>(p, lds_ids, rowbm, touched, m0, min(M, m0 + 4), blockIdx.x != 0 && p.do_align, &failed);
     if (blockIdx.x != 0 || !p.do_align) return;
-    gather_tail_ids(p, lds_ids, rowbm, touched, &failed);
+    // up to 32 rows: one row per wave and poll; more: the flat poll (measured
+    // at E' = 513: M = 40 13.2 -> 12.8 us, 64 16.6 -> 15.7; M = 5..17 were
+    // 0.1 to 0.4 us faster with the rows)
+    if constexpr (MAXM <= 32) gather_tail_rows<MAXM, BW>(p, lds_ids, rowbm, touched, &failed);
+    else gather_tail_flat<MAXM, BW>(p, lds_ids, rowbm, touched, &failed);
     __syncthreads();  // every pair is marked and in lds_ids
-    align_small(p, lds_ids, rowbm, touched, &failed);
+    if constexpr (BW == 1) {
+      align_small(p, lds_ids, rowbm, touched, &failed);
+    } else {
+      __shared__ uint32_t boff[kMaxRouteExperts + 1];
+      __shared__ uint32_t scan_tmp[kThreads / kWave + 1];
+      align_small_wide<BW>(p, lds_ids, rowbm, boff, scan_tmp, &failed);
+    }
     stamp(p, 6);
     return;
   }
@@ -509,7 +640,7 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
 
   // ---- block 0: the tail ---------------------------------------------------
   __shared__ int32_t lds_ids[MAXM * (kMaxTopK + 1)];
-  route_tail_rows1<NK>(p, lds_ids, rowbm, touched, 0, p.M, false, &failed);
+  route_tail_rows1<NK, BW>(p, lds_ids, rowbm, touched, 0, p.M, false, &failed);
   if (p.do_align) {
     __syncthreads();  // every pair is marked and in lds_ids
     align_small(p, lds_ids, rowbm, touched, &failed);
@@ -553,6 +684,11 @@ hipError_t launch_route_small(const SmallParams &p, hipStream_t stream) {
   // rows: M = 9 -0.5 us, 16 -0.5, 17 -2.1, 24 -2.3, 32 -2.9 (4 x 8 tiles are
   // the faster of the two from M = 24; at M = 5..8 and M <= 4 tiles were
   // slower by 0.35 to 0.5 us)
+  // More than 32 rows, or an align whose blocks of A slots can hold more
+  // than one block's worth of an expert's pairs: 4 words of row bits per
+  // expert and the general align.
+  if (p.M > 64) return launch_nk<4, 128, true, 128, 8>(p, stream);
+  if (p.M > 32 || (p.do_align && p.A < p.M)) return launch_nk<4, 64, true, 64, 8>(p, stream);
   if (p.M <= 20) return launch_nk<4, 32, true, 32, 4>(p, stream);
   return launch_nk<4, 32, true, 32, 8>(p, stream);
 }

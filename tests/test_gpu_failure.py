@@ -54,7 +54,8 @@ def _status(ws):
 CASES = [
     (4, 512, 4096, 10, True, mr.MR_STATUS_KEY_WAIT),                              # block 0 alone runs the tail
     (12, 512, 4096, 10, True, mr.MR_STATUS_KEY_WAIT | mr.MR_STATUS_ID_WAIT),      # three tail blocks hand off ids
-    (128, 128, 2048, 8, False, mr.MR_STATUS_GRID_WAIT),                           # one token tile: two grid barriers
+    (128, 128, 2048, 8, False, mr.MR_STATUS_KEY_WAIT | mr.MR_STATUS_ID_WAIT),     # 32 tail blocks, the flat id poll
+    (120, 512, 4096, 10, True, mr.MR_STATUS_GRID_WAIT),                           # prefill, one token tile: two grid barriers
     (2048, 512, 4096, 10, True, mr.MR_STATUS_TILE_WAIT | mr.MR_STATUS_GRID_WAIT), # token-tile waits + the align barrier
 ]
 

@@ -200,8 +200,9 @@ def test_large_consecutive_and_graph():
     import moe_token_routing_amd as mr
 
     ws = mr.new_workspace(2048, 512, 10, True)
-    # M = 17 runs the small-M launch on the same workspace between prefill launches
-    for it, (M, seed) in enumerate([(512, 1), (2048, 2), (40, 3), (17, 4), (33, 5), (512, 1)]):
+    # M = 40 and 17 run the small-M launch on the same workspace between
+    # prefill launches (M = 100 and 120 are one-tile prefill launches)
+    for it, (M, seed) in enumerate([(512, 1), (2048, 2), (40, 3), (17, 4), (100, 5), (120, 6), (512, 1)]):
         _say("consecutive", it, M)
         d = workloads.make_inputs(M, 512, 4096, True, "int", seed=seed)
         ref = oracle.route(d["x"], d["w"], d["ws"], 10, 1.0)
