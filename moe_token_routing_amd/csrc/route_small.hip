@@ -86,7 +86,9 @@ __device__ __forceinline__ void mark_pair(const SmallParams &p, int32_t id, int 
                                           uint32_t *touched) {
   if ((uint32_t)id < (uint32_t)p.Ep) {
     atomicOr(&rowbm[id * BW + (m >> 5)], 1u << (m & 31));
-    atomicOr(&touched[id >> 5], 1u << (id & 31));
+    // the touched bitmap serves the one-word align only (at most E' / 32
+    // words, so every pair's atomic lands on a few addresses)
+    if constexpr (BW == 1) atomicOr(&touched[id >> 5], 1u << (id & 31));
   }
 }
 
@@ -270,26 +272,31 @@ __device__ void gather_tail_flat(const SmallParams &p, int32_t *lds_ids, uint32_
     }
   }
   if (!arrived) wait_failed(p, kWaitIds, failed, lane);
-  bool marker = false;
+  // the loaded entries go to lds_ids as they are (id + 1) and their slots are
+  // re-zeroed; then one compact pass over the entries of rows 4 .. turns
+  // them into ids and marks the bitmaps (the unrolled form of that pass,
+  // 4 * kPer entries per thread, ran for about a microsecond)
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
     const int c = c0 + tid + kThreads * u;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (want(u, q)) {
-        const int i = 4 * c + q;
-        marker |= v[u][q] == kFailedHandOff;
-        const int32_t id = (int32_t)v[u][q] - 1;  // kFailedHandOff and 0 give ids < 0: skipped
-        lds_ids[i] = id;
-        const int m = S == 1 ? i : (int)__umulhi((uint32_t)i, p.S_magic);  // token row i / S
-        mark_pair<BW>(p, id, m, rowbm, touched);
-      }
-    }
     if (c < c1) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)  // entries below i0 are block 0's own rows
+        if (4 * c + q >= i0 && 4 * c + q < n) lds_ids[4 * c + q] = (int32_t)v[u][q];
       unsigned long long *z = reinterpret_cast<unsigned long long *>(p.hids) + 2 * c;
       st_agent(z, 0ull);
       st_agent(z + 1, 0ull);
     }
+  }
+  __syncthreads();
+  bool marker = false;
+  for (int i = i0 + tid; i < n; i += kThreads) {
+    const uint32_t h = (uint32_t)lds_ids[i];
+    marker |= h == kFailedHandOff;
+    const int32_t id = (int32_t)h - 1;  // kFailedHandOff and 0 give ids < 0: skipped
+    lds_ids[i] = id;
+    const int m = S == 1 ? i : (int)__umulhi((uint32_t)i, p.S_magic);  // token row i / S
+    mark_pair<BW>(p, id, m, rowbm, touched);
   }
   if (__builtin_amdgcn_ballot_w64(marker) != 0 && lane == 0) *failed = 1u;
 }
@@ -368,7 +375,7 @@ __device__ void align_small_wide(const SmallParams &p, const int32_t *lds_ids, c
     if (e0 + j < Ep) {
       boff[e0 + j] = o;
       for (uint32_t b = 0; b < nb[j]; ++b)
-        if (o + b < (uint64_t)p.expert_cap) st_agent(p.expert_ids + o + b, (int32_t)(e0 + j));
+        if (o + b < (uint64_t)p.expert_cap) p.expert_ids[o + b] = (int32_t)(e0 + j);
       o += nb[j];
     }
   }
@@ -383,7 +390,10 @@ __device__ void align_small_wide(const SmallParams &p, const int32_t *lds_ids, c
     uint32_t rank = __builtin_popcount(bits[m >> 5] & ((1u << (m & 31)) - 1u));
     for (uint32_t w = 0; w < (m >> 5); ++w) rank += __builtin_popcount(bits[w]);
     const uint64_t pos = ((uint64_t)boff[e] << sh) + rank;
-    if (pos < (uint64_t)p.sorted_cap) st_agent(p.sorted + pos, (int32_t)i);
+    // plain stores: a write-through store per scattered slot costs a memory
+    // transaction each; the sentinel pre-fill of these slots (other blocks,
+    // written through) completed before those blocks published their keys
+    if (pos < (uint64_t)p.sorted_cap) p.sorted[pos] = (int32_t)i;
   }
 }
 
