@@ -172,7 +172,8 @@ int mr_debug_set_wait_limit(int32_t polls);
 
 /* Measurement hook, not part of the routing API: later route launches of
  * this process record, per block b, thread 0's 100 MHz clock (s_memrealtime)
- * at up to 8 points into stamps[b * 8 + i].  The prefill launch (M > 32):
+ * at up to 8 points into stamps[b * 8 + i].  The prefill launch (above the
+ * small-M range: M > 128, or M > 32 with M * E' * H over 160 * 2^20):
  * 0 kernel start, 1 the first gate item's MFMA loop done, 2 every gate item
  * done (partial tiles stored), 3 the first top-k group ready to start, 4
  * top-k done, 5 the align's grid barrier passed, 6 block end.  The small-M
@@ -260,8 +261,7 @@ int mr_route_align_noalloc(const void *x, const void *gate_w, const void *shared
 /* Test hook, not part of the routing API: writes the fp32 gate logits the
  * route kernels compute for these inputs -- logits [M, E + has_shared]
  * (the shared logit in the last column) -- using the same kernel code and
- * summation order as mr_route for the same M (and as mr_route_align, except
- * at 17 <= M <= 32 with an alignment A < M, which takes the prefill launch). */
+ * summation order as mr_route and mr_route_align for the same M. */
 int mr_debug_gate_logits(const void *x, const void *gate_w, const void *shared_w,
                          int32_t M, int32_t H, int32_t E, float *logits,
                          void *ws, size_t ws_bytes, void *stream);

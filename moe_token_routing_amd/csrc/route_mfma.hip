@@ -1,6 +1,6 @@
 // route_mfma.hip -- one-launch router + align for prefill token counts
-// (M > 32, or 17 <= M <= 32 aligned with A < M): the gate pass is a split-K
-// MFMA tile contraction.
+// (M > 128, or M > 32 with more gate work than the small-M launch takes):
+// the gate pass is a split-K MFMA tile contraction.
 //
 // Computes what "[AMD] One-launch small-M MoE router ... on gfx950"
 // (sglang), Modifications, and "W4A16 MoE prefill: M-aware moe_align block

@@ -1,6 +1,6 @@
 // route_small.hip -- one-launch router + align for small token counts
-// (M <= 32; with align, M <= 16 or M <= A): the gate pass is a
-// weight-streaming GEMV.
+// (M <= 32, and up to 128 while the gate's multiply-adds stay small; the
+// host decides): the gate pass is a weight-streaming GEMV.
 //
 // What it computes follows "[AMD] One-launch small-M MoE router ... on
 // gfx950" (sglang), Modifications, and "W4A16 MoE prefill: M-aware
@@ -697,10 +697,12 @@ hipError_t launch_route_small(const SmallParams &p, hipStream_t stream) {
   // More than 32 rows, or an align whose blocks of A slots can hold more
   // than one block's worth of an expert's pairs: 4 words of row bits per
   // expert and the general align.
+  // The token tile depends on M alone, so mr_route, mr_route_align and the
+  // logits hook sum every logit in the same order.
   if (p.M > 64) return launch_nk<4, 128, true, 128, 8>(p, stream);
-  if (p.M > 32 || (p.do_align && p.A < p.M)) return launch_nk<4, 64, true, 64, 8>(p, stream);
-  if (p.M <= 20) return launch_nk<4, 32, true, 32, 4>(p, stream);
-  return launch_nk<4, 32, true, 32, 8>(p, stream);
+  const bool wide = p.M > 32 || (p.do_align && p.A < p.M);
+  if (p.M <= 20) return wide ? launch_nk<4, 64, true, 64, 4>(p, stream) : launch_nk<4, 32, true, 32, 4>(p, stream);
+  return wide ? launch_nk<4, 64, true, 64, 8>(p, stream) : launch_nk<4, 32, true, 32, 8>(p, stream);
 }
 
 }  // namespace mr
