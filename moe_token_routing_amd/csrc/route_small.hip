@@ -349,6 +349,19 @@ __device__ void align_small(const SmallParams &p, const int32_t *lds_ids, const 
 // rows that chose the same expert (ascending flat index inside the expert).
 // Every thread of the block calls this after the barrier that follows the
 // tail's marks.
+// The BW row-bit words of one expert (16- or 8-byte aligned in rowbm).
+template <int BW>
+__device__ __forceinline__ void load_row_words(const uint32_t *bits, uint32_t (&w)[BW]) {
+  static_assert(BW == 2 || BW == 4, "2 or 4 words");
+  if constexpr (BW == 4) {
+    const uint4 v = *reinterpret_cast<const uint4 *>(bits);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  } else {
+    const uint2 v = *reinterpret_cast<const uint2 *>(bits);
+    w[0] = v.x; w[1] = v.y;
+  }
+}
+
 template <int BW>
 __device__ void align_small_wide(const SmallParams &p, const int32_t *lds_ids, const uint32_t *rowbm,
                                  uint32_t *boff, uint32_t *scan_tmp, const uint32_t *failed) {
@@ -358,14 +371,15 @@ __device__ void align_small_wide(const SmallParams &p, const int32_t *lds_ids, c
   const uint32_t amask = (uint32_t)p.A - 1u;
   const int e0 = tid * EPT;
   uint32_t nb[EPT], run = 0;
+  uint32_t wd[EPT][BW];
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) load_row_words<BW>(rowbm + min(e0 + j, Ep - 1) * BW, wd[j]);
 #pragma unroll
   for (int j = 0; j < EPT; ++j) {
     uint32_t c = 0;
-    if (e0 + j < Ep) {
 #pragma unroll
-      for (int w = 0; w < BW; ++w) c += __builtin_popcount(rowbm[(e0 + j) * BW + w]);
-    }
-    nb[j] = (c + amask) >> sh;
+    for (int w = 0; w < BW; ++w) c += __builtin_popcount(wd[j][w]);
+    nb[j] = e0 + j < Ep ? (c + amask) >> sh : 0u;
     run += nb[j];
   }
   uint32_t total;
@@ -382,18 +396,41 @@ __device__ void align_small_wide(const SmallParams &p, const int32_t *lds_ids, c
   // npp = -1 marks a launch one of whose waits gave up
   if (tid == 0) st_agent(p.npp, *failed ? -1 : (int32_t)(total << sh));
   __syncthreads();  // boff complete
-  for (int i = tid; i < n; i += kThreads) {
-    const int e = lds_ids[i];
-    if (e < 0 || e >= Ep) continue;
-    const uint32_t m = p.S == 1 ? (uint32_t)i : __umulhi((uint32_t)i, p.S_magic);  // token row i / S
-    const uint32_t *bits = rowbm + e * BW;
-    uint32_t rank = __builtin_popcount(bits[m >> 5] & ((1u << (m & 31)) - 1u));
-    for (uint32_t w = 0; w < (m >> 5); ++w) rank += __builtin_popcount(bits[w]);
-    const uint64_t pos = ((uint64_t)boff[e] << sh) + rank;
-    // plain stores: a write-through store per scattered slot costs a memory
-    // transaction each; the sentinel pre-fill of these slots (other blocks,
-    // written through) completed before those blocks published their keys
-    if (pos < (uint64_t)p.sorted_cap) p.sorted[pos] = (int32_t)i;
+  // A pair's slot: its expert's first slot plus the expert's row bits below
+  // its token row.  Four pairs per thread at a time, branch-free until the
+  // store, so their LDS reads overlap.
+  constexpr int kUnroll = 4;
+  for (int i0 = tid; i0 < n; i0 += kUnroll * kThreads) {
+    int eu[kUnroll];
+    bool ok[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int i = i0 + u * kThreads;
+      const int e = i < n ? lds_ids[i] : -1;
+      ok[u] = e >= 0 && e < Ep;
+      eu[u] = ok[u] ? e : 0;
+    }
+    uint32_t rw[kUnroll][BW], bo[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      load_row_words<BW>(rowbm + eu[u] * BW, rw[u]);
+      bo[u] = boff[eu[u]];
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int i = i0 + u * kThreads;
+      const uint32_t m = p.S == 1 ? (uint32_t)i : __umulhi((uint32_t)i, p.S_magic);  // token row i / S
+      const uint32_t mw = m >> 5, below = (1u << (m & 31)) - 1u;
+      uint32_t rank = 0;
+#pragma unroll
+      for (int w = 0; w < BW; ++w)
+        rank += __builtin_popcount(rw[u][w] & ((uint32_t)w < mw ? ~0u : (uint32_t)w == mw ? below : 0u));
+      const uint64_t pos = ((uint64_t)bo[u] << sh) + rank;
+      // plain stores: a write-through store per scattered slot costs a memory
+      // transaction each; the sentinel pre-fill of these slots (other blocks,
+      // written through) completed before those blocks published their keys
+      if (ok[u] && pos < (uint64_t)p.sorted_cap) p.sorted[pos] = (int32_t)i;
+    }
   }
 }
 
@@ -473,7 +510,7 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
   // align bitmaps of block 0's tail: zeroed now, off the tail's path (the
   // gate's block barrier orders these stores before the tail's marks)
   constexpr int BW = (MAXM + 31) / 32;  // words of token-row bits per expert
-  __shared__ uint32_t rowbm[(kWave * NK + 1) * BW];  // E' <= 64 NK + 1
+  __shared__ __attribute__((aligned(16))) uint32_t rowbm[(kWave * NK + 1) * BW];  // E' <= 64 NK + 1
   __shared__ uint32_t touched[kMaxRouteExperts / 32 + 1];
   __shared__ uint32_t failed;  // a wait of this block gave up
   if (blockIdx.x == 0 && p.do_align && !p.logits_only) {
