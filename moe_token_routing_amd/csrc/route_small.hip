@@ -240,12 +240,10 @@ __device__ void gather_tail_rows(const SmallParams &p, int32_t *lds_ids, uint32_
 // in lds_ids, marks the align bitmaps and re-zeroes its chunks for the next
 // launch.  A slot holding kFailedHandOff (that block's key wait gave up)
 // raises the block's failed flag.
-template <int MAXM, int BW>
-__device__ void gather_tail_flat(const SmallParams &p, int32_t *lds_ids, uint32_t *rowbm, uint32_t *touched,
-                                uint32_t *failed) {
-  constexpr int kChunks = (MAXM * (kMaxTopK + 1) + 3) / 4;  // 16-byte chunks of the largest hids
-  constexpr int kPer0 = (kChunks + kThreads - 1) / kThreads;
-  constexpr int kPer = kPer0 <= 1 ? 1 : kPer0 <= 2 ? 2 : kPer0 <= 4 ? 4 : 8;  // chunks per thread
+// kPer: 16-byte chunks per thread, as many as this launch's hand-off needs.
+template <int kPer, int BW>
+__device__ void gather_flat_kp(const SmallParams &p, int32_t *lds_ids, uint32_t *rowbm, uint32_t *touched,
+                               uint32_t *failed) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int S = p.S, n = p.M * S, i0 = 4 * S;  // entries [i0, n): rows 4 ..
   const int c0 = i0 >> 2, c1 = (n + 3) >> 2;
@@ -299,6 +297,19 @@ __device__ void gather_tail_flat(const SmallParams &p, int32_t *lds_ids, uint32_
     mark_pair<BW>(p, id, m, rowbm, touched);
   }
   if (__builtin_amdgcn_ballot_w64(marker) != 0 && lane == 0) *failed = 1u;
+}
+
+template <int MAXM, int BW>
+__device__ void gather_tail_flat(const SmallParams &p, int32_t *lds_ids, uint32_t *rowbm, uint32_t *touched,
+                                 uint32_t *failed) {
+  constexpr int kChunks = (MAXM * (kMaxTopK + 1) + 3) / 4;  // 16-byte chunks of the largest hids
+  // the poll loads only the chunks this launch's hand-off covers (a round of
+  // loads takes longer the more loads it holds)
+  const int nch = ((p.M * p.S + 3) >> 2) - p.S;
+  if (nch <= kThreads) gather_flat_kp<1, BW>(p, lds_ids, rowbm, touched, failed);
+  else if (nch <= 2 * kThreads) gather_flat_kp<2, BW>(p, lds_ids, rowbm, touched, failed);
+  else if (kChunks <= 4 * kThreads || nch <= 4 * kThreads) gather_flat_kp<4, BW>(p, lds_ids, rowbm, touched, failed);
+  else gather_flat_kp<8, BW>(p, lds_ids, rowbm, touched, failed);
 }
 
 // Tail, part 2: align of the n = M*S pairs in lds_ids.  Here M <= A,
