@@ -353,8 +353,8 @@ __device__ void align_small(const SmallParams &p, const int32_t *lds_ids, const 
 
 // Tail, part 2 for up to 128 token rows and any A (BW words of token-row
 // bits per expert): an expert's pairs may fill several blocks of A slots.
-// Thread t counts the pairs of experts 5t .. 5t+4 (popcounts of their
-// bits), pads each to blocks of A, and one block scan gives every expert
+// Thread t counts the pairs of ceil(E' / 256) consecutive experts
+// (popcounts of their bits), pads each to blocks of A, and one block scan gives every expert
 // its first block (boff, LDS); the thread writes those experts' expert_ids.
 // A pair's slot is its expert's first slot plus the number of earlier token
 // rows that chose the same expert (ascending flat index inside the expert).
@@ -376,11 +376,14 @@ __device__ __forceinline__ void load_row_words(const uint32_t *bits, uint32_t (&
 template <int BW>
 __device__ void align_small_wide(const SmallParams &p, const int32_t *lds_ids, const uint32_t *rowbm,
                                  uint32_t *boff, uint32_t *scan_tmp, const uint32_t *failed) {
-  constexpr int EPT = (kMaxRouteExperts + 1 + kThreads - 1) / kThreads;  // experts per thread
+  constexpr int EPT = (kMaxRouteExperts + 1 + kThreads - 1) / kThreads;  // most experts per thread
   const int tid = threadIdx.x;
   const int n = p.M * p.S, Ep = p.Ep, sh = p.log2A;
   const uint32_t amask = (uint32_t)p.A - 1u;
-  const int e0 = tid * EPT;
+  // thread t takes the ept consecutive experts from t * ept, as few as E'
+  // allows, so each thread's expert_ids stores stay few
+  const int ept = (Ep + kThreads - 1) / kThreads;
+  const int e0 = tid * ept;
   uint32_t nb[EPT], run = 0;
   uint32_t wd[EPT][BW];
 #pragma unroll
@@ -390,14 +393,14 @@ __device__ void align_small_wide(const SmallParams &p, const int32_t *lds_ids, c
     uint32_t c = 0;
 #pragma unroll
     for (int w = 0; w < BW; ++w) c += __builtin_popcount(wd[j][w]);
-    nb[j] = e0 + j < Ep ? (c + amask) >> sh : 0u;
+    nb[j] = (j < ept && e0 + j < Ep) ? (c + amask) >> sh : 0u;
     run += nb[j];
   }
   uint32_t total;
   uint32_t o = block_excl_scan_u32<kThreads>(run, scan_tmp, &total);
 #pragma unroll
   for (int j = 0; j < EPT; ++j) {
-    if (e0 + j < Ep) {
+    if (j < ept && e0 + j < Ep) {
       boff[e0 + j] = o;
       for (uint32_t b = 0; b < nb[j]; ++b)
         if (o + b < (uint64_t)p.expert_cap) p.expert_ids[o + b] = (int32_t)(e0 + j);
