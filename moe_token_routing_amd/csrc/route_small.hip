@@ -346,8 +346,8 @@ __device__ void align_small(const SmallParams &p, const int32_t *lds_ids, const 
     const uint32_t blk = base + __builtin_popcount(touched[ew] & ((1u << (e & 31)) - 1u));
     const uint32_t rank = __builtin_popcount(rowbm[e] & ((1u << m) - 1u));
     const uint64_t pos = ((uint64_t)blk << sh) + rank;
-    if (pos < (uint64_t)p.sorted_cap) st_agent(p.sorted + pos, (int32_t)i);
-    if (rank == 0 && blk < (uint64_t)p.expert_cap) st_agent(p.expert_ids + blk, (int32_t)e);
+    if (pos < (uint64_t)p.sorted_cap) p.sorted[pos] = (int32_t)i;
+    if (rank == 0 && blk < (uint64_t)p.expert_cap) p.expert_ids[blk] = (int32_t)e;
   }
 }
 
