@@ -160,6 +160,30 @@ def test_route_only_matches_route_align():
     assert np.array_equal(wts.cpu().numpy(), g["topk_weights"].cpu().numpy())
 
 
+@pytest.mark.parametrize("M,E,H,A", [(17, 512, 4096, 16), (20, 512, 4096, 16), (24, 512, 4096, 16),
+                                     (32, 512, 4096, 16), (40, 512, 4096, 16), (64, 512, 4096, 32),
+                                     (100, 512, 4096, 16), (128, 128, 2048, 16)])
+def test_route_only_and_logits_match_route_align_any_alignment(M, E, H, A):
+    """The launch and its token tiling depend on M, E and H only, never on A
+    or on whether the align runs: on random inputs (no exact sums), route-only
+    ids and weights equal route+align's bit for bit at a forced A below M, and
+    the logits hook's fp32 logits reproduce those ids through the oracle's
+    rounding and selection."""
+    import moe_token_routing_amd as mr
+
+    _say("route vs route_align vs logits", M, E, H, "A", A)
+    d = workloads.make_inputs(M, E, H, True, "normal", seed=M * 3 + A)
+    x, w, s = to_dev(d["x"]), to_dev(d["w"]), to_dev(d["ws"])
+    ws = mr.new_workspace(M, E, 10, True)
+    ids, wts = mr.mr_route(x, w, s, 10, 1.0, workspace=ws)
+    g = mr.mr_route_align(x, w, s, 10, 1.0, A, workspace=ws)
+    assert np.array_equal(ids.cpu().numpy(), g["topk_ids"].cpu().numpy())
+    assert np.array_equal(wts.cpu().numpy(), g["topk_weights"].cpu().numpy())
+    ref = oracle.route(d["x"], d["w"], d["ws"], 10, 1.0)
+    check_backstop(d["x"], d["w"], d["ws"], logits_gpu(d), g["topk_ids"].cpu().numpy(),
+                   g["topk_weights"].cpu().numpy(), 10, 1.0, ref)
+
+
 def test_consecutive_launches_reuse_workspace():
     """The ticket resets itself: back-to-back launches on one workspace, with
     different inputs and sizes, each match the oracle."""
