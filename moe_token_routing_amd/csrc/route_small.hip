@@ -22,8 +22,9 @@
 //     t, t + 256, ... of both gate rows and of the M token rows (each token
 //     chunk loaded once per block), and its 16 sums are reduced by a halving
 //     DPP butterfly.
-//   - M >= 9: token tiles: a block takes 4 gate rows against 4 (M <= 20) or
-//     8 token rows in the same way, so it streams 8 or 12 rows whatever M.
+//   - M >= 9: token tiles: a block takes 4 gate rows against 4 (M <= 20), 8
+//     (M <= 64) or 16 token rows in the same way, so it streams 8, 12 or 20
+//     rows whatever M.
 //     With T token tiles, block b takes row group 8 * ((b / 8) / T) + b mod 8
 //     and token tile (b / 8) mod T: the T blocks of a row group run on one
 //     XCD (b mod 8) and share its L2.
@@ -33,24 +34,26 @@
 // Hand-off (no ticket): every block writes, with write-through agent-scope
 //   stores, the 32-bit selection key of each routed logit -- the bf16 order
 //   code in the high half and 0xFFFF - e in the low half, never 0 -- and the
-//   shared logit as (1 << 32 | fp32 bits).  Block 0, after its own gate rows,
-//   polls the key buffer with coherent loads until its rows are complete (a
-//   zero marks a slot not yet written); the poll IS the load of the tail's
-//   input.  It then re-zeroes the buffer for the next launch.  Only block 0
-//   ever waits, on blocks that never wait, and the wait is bounded.  The
-//   sentinel pre-fill of sorted_token_ids is issued first in every block and
-//   completed before that block's keys are written, so block 0 never races it.
+//   shared logit as (1 << 32 | fp32 bits).  Each tail wave polls its token
+//   row of the key buffer with coherent loads until it is complete (a zero
+//   marks a slot not yet written); the poll IS the load of the tail's input.
+//   It then re-zeroes the row for the next launch.  Only tail blocks wait,
+//   on gate work that never waits, and every wait is bounded.  The sentinel
+//   pre-fill of sorted_token_ids is issued first in every block and completed
+//   before that block's keys are written, so the align never races it.
 //
 // Tail: the first ceil(M/4) blocks each take four token rows, one per wave
 //   (at M <= 4 that is block 0 alone); blocks 1.. hand their ids to block 0
 //   (id + 1, written through, polled), which aligns.  A wave selects the
 //   top-k as k rounds of a wave-wide maximum over the packed keys (DPP within
 //   rows of 16, then gfx950's permlane16/32 swaps), then the softmax, shared
-//   slot and stores, marking each pair in two LDS bitmaps; then the align:
-//   with M <= A every touched expert takes exactly one block, so the
-//   bitmap of touched experts (block index = rank among them, one wave scan)
-//   and the one of token rows per expert (slot in the block) place every
-//   pair, one pair per thread.
+//   slot and stores, marking each pair in LDS bitmaps (token rows per expert,
+//   one to four words; touched experts); then the align: up to 32 rows with
+//   M <= A every touched expert takes exactly one block, so the bitmap of
+//   touched experts (block index = rank among them, one wave scan) and the
+//   one of token rows per expert (slot in the block) place every pair, one
+//   pair per thread; otherwise the experts' row counts, padded to whole
+//   blocks of A, go through one block scan first (align_small_wide).
 #include "device_common.h"
 #include "kernels.h"
 
