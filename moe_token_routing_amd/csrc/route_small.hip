@@ -549,8 +549,11 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
     // Thread t takes the 16-byte chunks t, t + 256, ... of every row, so each
     // token chunk is loaded once per block and serves all RPB gate rows.  A
     // batch issues all its loads (gate chunks non-temporal: read once) before
-    // any arithmetic.  Rows past E' reload row E'-1 and tokens past M reload
-    // token M-1; those sums are dropped.
+    // any arithmetic.  Tokens past M reload token M-1 and rows past E' row
+    // E'-1 (those sums are dropped), but a block with no row below E' (the
+    // row groups that round the grid up to whole XCDs) skips the loop: their
+    // clamped loads of row E'-1, non-temporal and from many blocks at once,
+    // delayed that row's own blocks by up to 4 us (M = 16).
     float acc[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] = 0.0f;
@@ -562,13 +565,20 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
     }
     const uint4 *xb = reinterpret_cast<const uint4 *>(p.x);
     constexpr int UB = (RPB + GL <= 18) ? 2 : 1;  // chunk positions per batch
-    for (int c0 = tid; c0 < nch; c0 += UB * kThreads) {
+    const int c_end = row0 < p.Ep ? nch : 0;  // block-uniform
+    for (int c0 = tid; c0 < c_end; c0 += UB * kThreads) {
       uint4 wv[UB][RPB], xv[UB][GL];
 #pragma unroll
       for (int u = 0; u < UB; ++u) {
         const int c = min(c0 + u * kThreads, nch - 1);
 #pragma unroll
-        for (int r = 0; r < RPB; ++r) wv[u][r] = ld_stream_16(wr[r] + c);
+        for (int r = 0; r < RPB; ++r) {
+          // rows past E' load nothing (block-uniform), in the untiled layout:
+          // with token tiles the per-row branch measured slower than the
+          // clamped loads of the one partly used row group (C3 +0.7 us)
+          if (GT > 0 || row0 + r < p.Ep) wv[u][r] = ld_stream_16(wr[r] + c);
+          else wv[u][r] = make_uint4(0u, 0u, 0u, 0u);
+        }
 #pragma unroll
         for (int m = 0; m < GL; ++m) xv[u][m] = xb[(size_t)min(m0 + m, M - 1) * nch + c];
       }
