@@ -84,6 +84,7 @@ struct SmallParams {
   int64_t expert_cap;
   int32_t *npp;
   int64_t fill_count;  // sentinel pre-fill length
+  int fill_blocks;     // blocks 0 .. fill_blocks - 1 take the pre-fill slices (set by the launch)
 };
 
 // Standalone align.

@@ -39,8 +39,10 @@
 //   marks a slot not yet written); the poll IS the load of the tail's input.
 //   It then re-zeroes the row for the next launch.  Only tail blocks wait,
 //   on gate work that never waits, and every wait is bounded.  The sentinel
-//   pre-fill of sorted_token_ids is issued first in every block and completed
-//   before that block's keys are written, so the align never races it.
+//   pre-fill of sorted_token_ids is issued first, only by blocks that block
+//   0 waits for (blocks with a live gate row and tail blocks), and completed
+//   before such a block publishes its keys or hands over its ids, so the
+//   align never races it.
 //
 // Tail: the first ceil(M/4) blocks each take four token rows, one per wave
 //   (at M <= 4 that is block 0 alone); blocks 1.. hand their ids to block 0
@@ -537,10 +539,20 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(SmallParams p) {
   if (tid == 0) failed = 0u;
   stamp(p, 0);
 
-  // ---- sentinel pre-fill of this block's slice of sorted_token_ids ------
-  if (p.do_align) {
+  // ---- sentinel pre-fill of sorted_token_ids ---------------------------
+  // Only blocks that block 0 waits for take a slice: a block with a live
+  // gate row publishes keys (or the shared logit) after its slice is
+  // complete, and a tail wave polls every key of its row before it hands its
+  // ids to block 0; a tail block hands its ids over itself.  Untiled, every
+  // block is one or the other.  With token tiles the grid rounds the row
+  // groups up to whole XCDs, and a block of a padding row group that is no
+  // tail block publishes nothing and is waited for by no one: a slice of its
+  // could still be in flight when block 0 writes the same slots.  There the
+  // first p.fill_blocks blocks, chosen by the launch, take the slices.
+  if (p.do_align && (GT == 0 || (int)blockIdx.x < p.fill_blocks)) {
     const int32_t sentinel = M * p.S;
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + tid; i < p.fill_count; i += (int64_t)gridDim.x * kThreads)
+    const int64_t nf = GT ? (int64_t)p.fill_blocks : (int64_t)gridDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + tid; i < p.fill_count; i += nf * kThreads)
       st_agent(p.sorted + i, sentinel);
   }
 
@@ -730,11 +742,21 @@ hipError_t launch_nk(const SmallParams &p, hipStream_t stream) {
   // at M >= 5 the first ceil(M / 4) blocks also run the tail: there must be
   // that many (extra blocks own no gate rows: their sums are dropped)
   if (MAXM > kThreads / kWave && grid < (p.M + 3) / 4) grid = (p.M + 3) / 4;
+  // Token tiles: the pre-fill slices go to blocks that block 0 waits for.
+  // Block b holds row group 8 * (b / 8 / T) + b % 8 of T token tiles, so
+  // the first 8 * T * floor(nrg / 8) blocks own live rows, and the first
+  // ceil(M / 4) are tail blocks.
+  SmallParams q = p;
+  q.fill_blocks = grid;
+  if (GT) {
+    const int live = nrg / 8 * 8 * ((p.M + GT - 1) / GT), tail = (p.M + 3) / 4;
+    q.fill_blocks = live > tail ? live : tail;
+  }
   const int nk = (p.E + kWave - 1) / kWave;
-  if (nk <= 2) route_small_kernel<RPB, MAXM, SHARED, 2, ML, GT><<<grid, kThreads, 0, stream>>>(p);
-  else if (nk <= 4) route_small_kernel<RPB, MAXM, SHARED, 4, ML, GT><<<grid, kThreads, 0, stream>>>(p);
-  else if (nk <= 8) route_small_kernel<RPB, MAXM, SHARED, 8, ML, GT><<<grid, kThreads, 0, stream>>>(p);
-  else route_small_kernel<RPB, MAXM, SHARED, 16, ML, GT><<<grid, kThreads, 0, stream>>>(p);
+  if (nk <= 2) route_small_kernel<RPB, MAXM, SHARED, 2, ML, GT><<<grid, kThreads, 0, stream>>>(q);
+  else if (nk <= 4) route_small_kernel<RPB, MAXM, SHARED, 4, ML, GT><<<grid, kThreads, 0, stream>>>(q);
+  else if (nk <= 8) route_small_kernel<RPB, MAXM, SHARED, 8, ML, GT><<<grid, kThreads, 0, stream>>>(q);
+  else route_small_kernel<RPB, MAXM, SHARED, 16, ML, GT><<<grid, kThreads, 0, stream>>>(q);
   return hipGetLastError();
 }
 

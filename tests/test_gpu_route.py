@@ -147,6 +147,26 @@ def test_router_forced_alignment_17_to_32(M, A):
     _run_and_check(d, 10, 1.0, A=A, exact=True)
 
 
+@pytest.mark.parametrize("M,E,k,A", [(15, 14, 10, 128), (9, 15, 4, 128), (12, 20, 8, 64)])
+def test_fill_slices_only_from_live_row_groups(M, E, k, A):
+    """Small E' at 9 <= M <= 20: the grid rounds the gate's row groups up to
+    whole XCDs, so some of the first blocks hold no live gate row and are not
+    tail blocks either.  Such a block publishes nothing and no block waits
+    for it, so it must not take a slice of the sorted_token_ids pre-fill (its
+    sentinels could land after block 0's placements).  20 launches on one
+    workspace, each checked against the oracle's align."""
+    import moe_token_routing_amd as mr
+
+    _say("fill slices", M, E, k, "A", A)
+    ws = mr.new_workspace(M, E, k, False)
+    for it in range(20):
+        d = workloads.make_inputs(M, E, 64, False, "int", seed=100 * M + it)
+        ref = oracle.route(d["x"], d["w"], d["ws"], k, 1.0)
+        g = route_align_gpu(d, k, 1.0, A, ws=ws)
+        assert np.array_equal(g["topk_ids"], ref["ids"]), it
+        check_align(g["topk_ids"], E, A, g["sorted_token_ids"], g["expert_ids"], g["npp"][0])
+
+
 def test_route_only_matches_route_align():
     import moe_token_routing_amd as mr
 
