@@ -1,7 +1,7 @@
 """Parity over seeded draws of the whole supported shape space (needs a gfx950
 GPU): route + align on exactly representable and on random-normal inputs,
-the standalone and the expert-parallel align on random ids, and the row-wise
-argmax.
+one workspace reused over a sequence of token counts, the standalone and the
+expert-parallel align on random ids, and the row-wise argmax.
 
 The hand-picked shapes elsewhere aim at known boundaries (tile edges, lane
 layouts, row-load variants); these draws are meant to land where nobody
@@ -169,6 +169,51 @@ def test_align_local_seeded_shape(i, M, S, E, ranks, r, A):
     assert n == want[2], (n, want[2])
     assert np.array_equal(srt[:n].cpu().numpy(), want[0])
     assert np.array_equal(eids[: n // A].cpu().numpy(), want[1])
+
+
+def _reuse_draws(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        band = i % 4  # tiny, small, middling and many experts in turn
+        E = int(rng.integers(2, 17)) if band == 0 else int(rng.integers(17, 64)) if band == 1 \
+            else int(rng.integers(64, 300)) if band == 2 else int(rng.integers(300, 1025))
+        k = int(rng.integers(1, min(32, E) + 1))
+        H = 8 * int(rng.integers(1, 129))
+        top = int(rng.integers(9, 161))
+        Ms = sorted({top} | {int(rng.integers(1, top + 1)) for _ in range(3)} | {int(rng.integers(1, 9))},
+                    reverse=bool(rng.random() < 0.5))
+        shared = bool(rng.random() < 0.5)
+        A = None if rng.random() < 0.5 else int(rng.choice([16, 32, 64, 128, 256]))
+        out.append((i, E, k, H, Ms, shared, A))
+    return out
+
+
+@pytest.mark.parametrize("i,E,k,H,Ms,shared,A", _reuse_draws(32, 20261207))
+def test_workspace_reuse_seeded(i, E, k, H, Ms, shared, A):
+    """One workspace over a seeded sequence of token counts (the small-M
+    launch with and without token tiles, and the prefill launch past its
+    range), route + align and route-only in turn, twice over: every call's
+    ids equal the oracle's, every align equals the oracle's align of those
+    ids, and the status word stays 0.  Exact inputs."""
+    import moe_token_routing_amd as mr
+
+    _say("reuse draw", i, "E", E, "k", k, "H", H, "Ms", Ms, "shared", shared, "A", A)
+    ws = mr.new_workspace(max(Ms), E, k, shared)
+    for j, M in enumerate(Ms + Ms):
+        d = workloads.make_inputs(M, E, H, shared, "int", seed=7000 + 10 * i + j)
+        ref = oracle.route(d["x"], d["w"], d["ws"], k, 1.0)
+        Am = A if A is not None else oracle.select_alignment(M, k, E)
+        if j % 2 == 0:
+            g = route_align_gpu(d, k, 1.0, Am, ws=ws)
+            assert np.array_equal(g["topk_ids"], ref["ids"]), ("ids", j, M)
+            check_align(g["topk_ids"], E + shared, Am, g["sorted_token_ids"], g["expert_ids"], g["npp"][0])
+        else:
+            from gpu_util import to_dev
+
+            ids, _ = mr.mr_route(to_dev(d["x"]), to_dev(d["w"]), to_dev(d["ws"]), k, 1.0, workspace=ws)
+            assert np.array_equal(ids.cpu().numpy(), ref["ids"]), ("route ids", j, M)
+    assert int(mr.mr_workspace_status(ws).item()) == 0
 
 
 def _argmax_draws(n, seed):
